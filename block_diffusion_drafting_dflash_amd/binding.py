@@ -1,0 +1,270 @@
+"""ctypes binding for libdflash.so (argument marshalling only).
+
+Every computation of the drafting step runs in the HIP library; this module
+turns torch tensors into device pointers, keeps the weight tensors alive for
+the context's lifetime and raises on non-OK statuses.  If the library has
+not been built, loading fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdflash.so")
+HARNESS_PATH = os.path.join(_HERE, "libdflash_harness.so")
+
+DFLASH_OK = 0
+STATUS = {0: "DFLASH_OK", -1: "DFLASH_E_INVALID", -2: "DFLASH_E_SHAPE",
+          -3: "DFLASH_E_CAPACITY", -4: "DFLASH_E_DEVICE",
+          -5: "DFLASH_E_UNSUPPORTED"}
+DTYPE = {"f32": 0, "bf16": 1}
+
+# C-ABI symbols declared in include/dflash.h and include/dflash_harness.h
+LIB_SYMBOLS = ["dflash_create", "dflash_destroy", "dflash_kv_cache_bytes",
+               "dflash_last_error", "dflash_check_device_errors",
+               "dflash_inject_kv", "dflash_draft_block",
+               "dflash_verify_greedy"]
+HARNESS_SYMBOLS = ["dflash_harness_synth_target"]
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_layers", "hidden", "num_q_heads", "num_kv_heads", "head_dim",
+        "intermediate", "vocab", "num_target_layers", "target_hidden",
+        "block_size", "mask_token_id", "dtype", "max_batch", "max_ctx",
+        "max_inject_rows")] + [("rope_theta", ctypes.c_float),
+                               ("rms_eps", ctypes.c_float)]
+
+
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("fc", ctypes.c_void_p),
+                ("hidden_norm", ctypes.c_void_p)] + [
+        (n, _PP) for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm",
+                           "w_gate", "w_up", "w_down")] + [
+        ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p)]
+
+
+_lib = None
+_harness = None
+
+
+def load_library():
+    """Load libdflash.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} not found: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.dflash_create.argtypes = [ctypes.POINTER(Config),
+                                  ctypes.POINTER(Weights),
+                                  ctypes.POINTER(vp)]
+    lib.dflash_create.restype = ctypes.c_int
+    lib.dflash_destroy.argtypes = [vp]
+    lib.dflash_destroy.restype = None
+    lib.dflash_kv_cache_bytes.argtypes = [ctypes.POINTER(Config)]
+    lib.dflash_kv_cache_bytes.restype = ctypes.c_size_t
+    lib.dflash_last_error.argtypes = []
+    lib.dflash_last_error.restype = ctypes.c_char_p
+    lib.dflash_check_device_errors.argtypes = [vp, vp,
+                                               ctypes.POINTER(i32)]
+    lib.dflash_check_device_errors.restype = ctypes.c_int
+    lib.dflash_inject_kv.argtypes = [vp, vp, _PP, i64, i32, vp, vp, vp]
+    lib.dflash_inject_kv.restype = ctypes.c_int
+    lib.dflash_draft_block.argtypes = [vp, vp, i32, vp, vp, vp, i32, vp, i32,
+                                       i32, vp, vp, vp, vp]
+    lib.dflash_draft_block.restype = ctypes.c_int
+    lib.dflash_verify_greedy.argtypes = [vp, i32, i32, vp, vp, vp, vp]
+    lib.dflash_verify_greedy.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def load_harness():
+    global _harness
+    if _harness is not None:
+        return _harness
+    if not os.path.exists(HARNESS_PATH):
+        raise RuntimeError(f"{HARNESS_PATH} not found: build it first")
+    h = ctypes.CDLL(HARNESS_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    h.dflash_harness_synth_target.argtypes = [vp, i32, i32, i32, vp, vp, vp,
+                                              vp, vp, vp]
+    h.dflash_harness_synth_target.restype = ctypes.c_int
+    _harness = h
+    return h
+
+
+def _check(status: int):
+    if status != DFLASH_OK:
+        msg = load_library().dflash_last_error().decode(errors="replace")
+        raise DFlashError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_config(wl, max_batch=None, max_ctx=None,
+                max_inject_rows=None) -> Config:
+    """dflash_config for a workloads.Workload."""
+    return Config(
+        num_layers=wl.num_layers, hidden=wl.hidden,
+        num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+        head_dim=wl.head_dim, intermediate=wl.intermediate, vocab=wl.vocab,
+        num_target_layers=wl.num_target_layers,
+        target_hidden=wl.target_hidden, block_size=wl.block_size,
+        mask_token_id=wl.mask_id, dtype=DTYPE[wl.dtype],
+        max_batch=max_batch or wl.batch, max_ctx=max_ctx or wl.ctx_max,
+        max_inject_rows=max_inject_rows or max(wl.batch * wl.new_rows, 2048),
+        rope_theta=wl.rope_theta, rms_eps=wl.rms_eps)
+
+
+def kv_cache_bytes(cfg: Config) -> int:
+    return int(load_library().dflash_kv_cache_bytes(ctypes.byref(cfg)))
+
+
+class DFlash:
+    """A drafting context on the current device (one per drafter)."""
+
+    def __init__(self, wl, weights: Dict[str, object], max_batch=None,
+                 max_ctx=None, max_inject_rows=None):
+        self.lib = load_library()
+        self.wl = wl
+        self.cfg = make_config(wl, max_batch, max_ctx, max_inject_rows)
+        self.weights = weights  # keep tensors alive
+        self._arrays = []
+        n = wl.num_layers
+
+        def plist(key):
+            arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in weights[key]])
+            self._arrays.append(arr)
+            return ctypes.cast(arr, _PP)
+
+        w = Weights(embed=weights["embed"].data_ptr(),
+                    fc=weights["fc"].data_ptr(),
+                    hidden_norm=weights["hidden_norm"].data_ptr(),
+                    final_norm=weights["final_norm"].data_ptr(),
+                    lm_head=weights["lm_head"].data_ptr())
+        for key in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate",
+                    "w_up", "w_down"):
+            setattr(w, key, plist(key))
+        self._w = w
+        ctx = ctypes.c_void_p()
+        _check(self.lib.dflash_create(ctypes.byref(self.cfg), ctypes.byref(w),
+                                      ctypes.byref(ctx)))
+        self.ctx = ctx
+
+    def close(self):
+        if getattr(self, "ctx", None) is not None and self.ctx.value:
+            self.lib.dflash_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- tensors ------------------------------------------------------------
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.wl.dtype == "f32" else torch.bfloat16
+
+    def kv_cache_bytes(self) -> int:
+        return kv_cache_bytes(self.cfg)
+
+    def new_kv_cache(self, device="cuda") -> torch.Tensor:
+        """[N_l, 2, max_batch, Hkv, max_ctx + K, d] in the drafter dtype."""
+        c = self.cfg
+        return torch.zeros(c.num_layers, 2, c.max_batch, c.num_kv_heads,
+                           c.max_ctx + c.block_size, c.head_dim,
+                           dtype=self.torch_dtype, device=device)
+
+    # -- entry points -------------------------------------------------------
+    def inject_kv(self, hiddens: Sequence[torch.Tensor], row_seq: torch.Tensor,
+                  row_pos: torch.Tensor, kv: torch.Tensor, stream=None):
+        T = hiddens[0].shape[0]
+        ld = hiddens[0].stride(0)
+        arr = (ctypes.c_void_p * len(hiddens))(*[h.data_ptr() for h in hiddens])
+        _check(self.lib.dflash_inject_kv(
+            self.ctx, _stream(stream), ctypes.cast(arr, _PP), ld, T,
+            _ptr(row_seq), _ptr(row_pos), _ptr(kv)))
+
+    def draft_block(self, ctx_len: torch.Tensor, kv: torch.Tensor,
+                    max_ctx_len: int, anchor: Optional[torch.Tensor] = None,
+                    block_tokens: Optional[torch.Tensor] = None,
+                    num_passes: int = 1, commit_per_pass: int = 0,
+                    draft: Optional[torch.Tensor] = None,
+                    conf: Optional[torch.Tensor] = None,
+                    margin: Optional[torch.Tensor] = None,
+                    logits: Optional[torch.Tensor] = None, stream=None):
+        B = ctx_len.shape[0]
+        K = self.cfg.block_size
+        dev = ctx_len.device
+        if draft is None:
+            draft = torch.empty(B, K - 1, dtype=torch.int32, device=dev)
+        _check(self.lib.dflash_draft_block(
+            self.ctx, _stream(stream), B, _ptr(anchor), _ptr(block_tokens),
+            _ptr(ctx_len), int(max_ctx_len), _ptr(kv), num_passes,
+            commit_per_pass, _ptr(draft), _ptr(conf), _ptr(margin),
+            _ptr(logits)))
+        return draft
+
+    def check_device_errors(self, stream=None) -> int:
+        bits = ctypes.c_int32(0)
+        st = self.lib.dflash_check_device_errors(self.ctx, _stream(stream),
+                                                 ctypes.byref(bits))
+        if st not in (DFLASH_OK, -4):
+            _check(st)
+        return bits.value
+
+
+def verify_greedy(draft: torch.Tensor, target: torch.Tensor,
+                  accept: Optional[torch.Tensor] = None,
+                  next_anchor: Optional[torch.Tensor] = None, stream=None):
+    lib = load_library()
+    B, K = target.shape
+    if accept is None:
+        accept = torch.empty(B, dtype=torch.int32, device=target.device)
+    if next_anchor is None:
+        next_anchor = torch.empty(B, dtype=torch.int32, device=target.device)
+    _check(lib.dflash_verify_greedy(_stream(stream), B, K, _ptr(draft),
+                                    _ptr(target), _ptr(accept),
+                                    _ptr(next_anchor)))
+    return accept, next_anchor
+
+
+def synth_target(draft, u, r, tail, p, vocab, target=None, stream=None):
+    h = load_harness()
+    B, k1 = draft.shape
+    if target is None:
+        target = torch.empty(B, k1 + 1, dtype=torch.int32, device=draft.device)
+    st = h.dflash_harness_synth_target(_stream(stream), B, k1 + 1, vocab,
+                                       _ptr(draft), _ptr(u), _ptr(r),
+                                       _ptr(tail), _ptr(p), _ptr(target))
+    if st != 0:
+        raise RuntimeError(f"dflash_harness_synth_target failed ({st})")
+    return target

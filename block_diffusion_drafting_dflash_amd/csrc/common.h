@@ -1,0 +1,169 @@
+// Shared device helpers for the DFlash gfx950 kernels: storage types, 16-byte
+// fragment loads, the MFMA step, and wave-level shuffles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Storage tag for bf16 tensors (bits held in a uint16).
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T> struct Storage;
+
+// One lane fragment is 16 bytes.  E = elements per fragment; KC = elements of
+// the contraction covered by one fragment across the four 16-lane groups of a
+// wave (the step of the K loop).
+template <> struct Storage<bf16_t> {
+  static constexpr int E = 8;
+  static constexpr int KC = 32;
+};
+template <> struct Storage<float> {
+  static constexpr int E = 4;
+  static constexpr int KC = 16;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// Round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float load_elem(const bf16_t* p, int64_t i) {
+  return bf16_to_f32(p[i].bits);
+}
+__device__ __forceinline__ float load_elem(const float* p, int64_t i) {
+  return p[i];
+}
+__device__ __forceinline__ void store_elem(bf16_t* p, int64_t i, float v) {
+  p[i].bits = (uint16_t)f32_to_bf16(v);
+}
+__device__ __forceinline__ void store_elem(float* p, int64_t i, float v) {
+  p[i] = v;
+}
+// Value after rounding to the storage type (what a store then load returns).
+__device__ __forceinline__ float round_to(bf16_t, float v) {
+  return bf16_to_f32(f32_to_bf16(v));
+}
+__device__ __forceinline__ float round_to(float, float v) { return v; }
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// acc += A_frag . B_frag over one fragment step.  Lane l supplies row (A) or
+// column (B) l % 16 and contraction slots of lane group l / 16; the two
+// operands must place the same contraction index in the same (lane group,
+// element) slot.  Output: lane l, register j holds row 4*(l/16)+j, column
+// l % 16.
+__device__ __forceinline__ void mma16(f32x4& acc, u32x4 a, u32x4 b, bf16_t) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0, 0,
+      0);
+}
+__device__ __forceinline__ void mma16(f32x4& acc, u32x4 a, u32x4 b, float) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x),
+                                             __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y),
+                                             __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z),
+                                             __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w),
+                                             __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum for blockDim.x == 64 * nwaves (nwaves <= 16), fixed order.
+template <int NWAVES>
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+  v = warp_sum(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) t += scratch[i];
+  __syncthreads();
+  return t;
+}
+
+// Running (max, argmax, second max, sum of exp(z - max)) over a set of
+// logits.  Merging is associative and commutative in exact arithmetic for
+// everything but the floating-point sum, which callers merge in a fixed
+// order.  Ties in the maximum go to the lower index.
+struct Top2 {
+  float m1;
+  int i1;
+  float m2;
+  float s;
+};
+
+__device__ __forceinline__ Top2 top2_empty() {
+  Top2 t;
+  t.m1 = -INFINITY;
+  t.i1 = 0x7fffffff;
+  t.m2 = -INFINITY;
+  t.s = 0.f;
+  return t;
+}
+
+__device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
+  const bool b_wins = (b.m1 > a.m1) || (b.m1 == a.m1 && b.i1 < a.i1);
+  Top2 w = b_wins ? b : a;
+  Top2 l = b_wins ? a : b;
+  Top2 r;
+  r.m1 = w.m1;
+  r.i1 = w.i1;
+  r.m2 = fmaxf(w.m2, l.m1);
+  const float sl = (l.m1 == -INFINITY) ? 0.f : l.s * __expf(l.m1 - w.m1);
+  r.s = w.s + sl;
+  return r;
+}
+
+__device__ __forceinline__ Top2 top2_shfl_xor(Top2 t, int o) {
+  Top2 r;
+  r.m1 = __shfl_xor(t.m1, o, 64);
+  r.i1 = __shfl_xor(t.i1, o, 64);
+  r.m2 = __shfl_xor(t.m2, o, 64);
+  r.s = __shfl_xor(t.s, o, 64);
+  return r;
+}
+
+// Butterfly merge across the 64 lanes; every lane ends with the result.
+// The butterfly pairs differ per lane, so the float sum is only guaranteed
+// identical on a lane-by-lane basis run to run: callers read lane 0.
+__device__ __forceinline__ Top2 top2_wave(Top2 t) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) t = top2_merge(t, top2_shfl_xor(t, o));
+  return t;
+}
+
+__device__ __forceinline__ void set_error(int* err, int bit) {
+  atomicOr(err, bit);
+}
+
+}  // namespace dflash

@@ -1,0 +1,252 @@
+/*
+ * dflash.h -- C ABI of the DFlash drafting hot path on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * One drafting step of DFlash block-diffusion speculative decoding:
+ *   dflash_inject_kv     target hidden states from several target layers are
+ *                        fused (concat -> fc -> RMSNorm) and projected through
+ *                        every draft layer's K/V weights (RoPE on K) into the
+ *                        draft KV cache;
+ *   dflash_draft_block   a block of K = 16 positions (the anchor, then K-1
+ *                        mask tokens) runs once through every draft layer and
+ *                        the LM head; each masked position takes its argmax
+ *                        (optionally over S confidence-ordered refinement
+ *                        passes);
+ *   dflash_verify_greedy the accepted length is the longest prefix of the
+ *                        draft that matches the target's greedy tokens, plus
+ *                        one token from the target.
+ *
+ * Sources: "DFlash Guide: Block Diffusion for Speculative Decoding"
+ * (aifetchly blog), "DFlash: Block Diffusion for Flash Speculative Decoding"
+ * (sciencestack abstract page, arXiv 2602.06036) and "DFlash: Diffusion Drafts
+ * the Block" (stable-lab tutorial).  Each entry point cites its passage.
+ *
+ * Conventions for every call:
+ *   - All tensor arguments are DEVICE pointers unless marked "host".  The
+ *     caller owns every weight, input, output and the KV cache; the library
+ *     never frees them.  Weights are read-only.  Tensor pointers must be
+ *     16-byte aligned.
+ *   - Element type of weights, hidden states, activations and the KV cache is
+ *     the config's dtype (DFLASH_BF16 or DFLASH_F32); ids are int32; logits,
+ *     confidences and margins are fp32.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  They allocate nothing, synchronise nothing and read nothing
+ *     back to the host, so a step can be enqueued without host stalls.
+ *     Lengths live in device arrays; the host passes only upper bounds that
+ *     size the launch grids.
+ *   - Host-side validation runs before anything is launched.  A failing call
+ *     launches nothing and returns a negative dflash_status;
+ *     dflash_last_error() then returns a message (per thread).
+ *   - Values that only the device sees (an out-of-range token id, context
+ *     length, slot or position) are clamped so that every access stays in
+ *     bounds, and set a sticky device error word that
+ *     dflash_check_device_errors() reports.
+ *   - Results are bitwise reproducible from run to run: no reduction depends
+ *     on scheduling order.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_E_INVALID = -1,     /* null pointer, misaligned pointer, bad scalar */
+  DFLASH_E_SHAPE = -2,       /* sizes inconsistent with each other */
+  DFLASH_E_CAPACITY = -3,    /* beyond max_batch / max_ctx / max_inject_rows */
+  DFLASH_E_DEVICE = -4,      /* HIP runtime failure or device error word set */
+  DFLASH_E_UNSUPPORTED = -5  /* a shape the kernels do not implement */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Device error word bits (dflash_check_device_errors). */
+#define DFLASH_DEVERR_TOKEN    0x1  /* token id outside [0, vocab) */
+#define DFLASH_DEVERR_CTX_LEN  0x2  /* context length outside [0, max ctx] */
+#define DFLASH_DEVERR_SLOT     0x4  /* inject row's sequence slot out of range */
+#define DFLASH_DEVERR_POS      0x8  /* inject row's position out of range */
+
+/* Drafter shape and capacities.  Supported: block_size == 16; head_dim 64 or
+ * 128; num_q_heads a multiple of num_kv_heads with group size <= 8; hidden,
+ * intermediate, target_hidden and num_q_heads*head_dim multiples of 64;
+ * vocab a multiple of 16.  Anything else returns DFLASH_E_UNSUPPORTED. */
+typedef struct {
+  int32_t num_layers;        /* N_l draft layers */
+  int32_t hidden;            /* D */
+  int32_t num_q_heads;       /* Hq */
+  int32_t num_kv_heads;      /* Hkv */
+  int32_t head_dim;          /* d */
+  int32_t intermediate;      /* I (SwiGLU) */
+  int32_t vocab;             /* V */
+  int32_t num_target_layers; /* n_t target layers fused per context row */
+  int32_t target_hidden;     /* D_t */
+  int32_t block_size;        /* K */
+  int32_t mask_token_id;     /* id of the [MASK] token */
+  int32_t dtype;             /* dflash_dtype */
+  int32_t max_batch;         /* sequences (= KV-cache slots) */
+  int32_t max_ctx;           /* max context length L per sequence */
+  int32_t max_inject_rows;   /* max rows T per dflash_inject_kv call */
+  float rope_theta;          /* RoPE base */
+  float rms_eps;             /* RMSNorm epsilon */
+} dflash_config;
+
+/* Drafter weights, PyTorch Linear layout [out, in], row-major, dtype of the
+ * config.  Per-layer entries are HOST arrays of num_layers DEVICE pointers;
+ * the library copies those arrays at dflash_create, the weights themselves
+ * must stay alive and unchanged until dflash_destroy. */
+typedef struct {
+  const void* embed;        /* [V, D] */
+  const void* fc;           /* [D, n_t * D_t]: fuses the concatenated layers */
+  const void* hidden_norm;  /* [D] RMSNorm gain applied after fc */
+  const void* const* attn_norm;  /* [D]        per layer */
+  const void* const* wq;         /* [Hq*d, D]  per layer */
+  const void* const* wk;         /* [Hkv*d, D] per layer */
+  const void* const* wv;         /* [Hkv*d, D] per layer */
+  const void* const* wo;         /* [D, Hq*d]  per layer */
+  const void* const* mlp_norm;   /* [D]        per layer */
+  const void* const* w_gate;     /* [I, D]     per layer */
+  const void* const* w_up;       /* [I, D]     per layer */
+  const void* const* w_down;     /* [D, I]     per layer */
+  const void* final_norm;   /* [D] */
+  const void* lm_head;      /* [V, D] */
+} dflash_weights;
+
+typedef struct dflash_ctx dflash_ctx;
+
+/* Create a drafting context on the current HIP device: validates the config
+ * and weights, allocates the context's own workspace (activations, split-K
+ * partials, RoPE table, device error word).  *out is set on success. */
+dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
+                            dflash_ctx** out);
+
+/* Free the context's workspace.  Waits for the device first.  NULL is a
+ * no-op. */
+void dflash_destroy(dflash_ctx* ctx);
+
+/* Bytes of the KV cache for this config:
+ *   num_layers * 2 * max_batch * num_kv_heads * (max_ctx + block_size)
+ *   * head_dim * sizeof(dtype).
+ * Layout kv[layer][0 = K | 1 = V][slot][kv_head][pos][head_dim].  Positions
+ * [L, L + block_size) of a slot are scratch for the block being drafted. */
+size_t dflash_kv_cache_bytes(const dflash_config* cfg);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* dflash_last_error(void);
+
+/* Test/debug only (synchronises `stream`): returns DFLASH_E_DEVICE and writes
+ * the DFLASH_DEVERR_* bits to *bits if any were set since the last check,
+ * then clears them.  bits may be NULL. */
+dflash_status dflash_check_device_errors(dflash_ctx* ctx, void* stream,
+                                         int32_t* bits);
+
+/* KV injection of T context rows.
+ *
+ * Passage: "DFlash Guide", sections "2. Target Hidden-State Conditioning"
+ * (H_cond = W_proj H_T) and "3. Cross-Layer KV Injection" (K^(l) = W_K^(l)
+ * H_cond, V^(l) = W_V^(l) H_cond); sciencestack page, Figure 2 (features from
+ * several target layers are fused and injected into every draft layer's KV
+ * cache); stable-lab "KV Injection" (through the draft model's own K/V
+ * projections, at every draft layer).
+ *
+ * For each row r < T:  c = RMSNorm(fc . concat_k target_hidden[k][r]) * g,
+ * stored in the config dtype; then for every layer l and kv head h:
+ *   kv[l][K][row_seq[r]][h][row_pos[r]][:] = RoPE(wk[l] . c, row_pos[r])
+ *   kv[l][V][row_seq[r]][h][row_pos[r]][:] = wv[l] . c
+ *
+ * target_hidden: HOST array of num_target_layers DEVICE pointers, each to a
+ *                [T, D_t] matrix with row stride `ld` elements (ld >= D_t).
+ * row_seq, row_pos: [T] int32 slot in [0, max_batch) and position in
+ *                [0, max_ctx).  Rows of one call must not repeat a
+ *                (slot, pos) pair.
+ * kv_cache:      dflash_kv_cache_bytes(cfg) bytes, written in place.
+ * T:             1 <= T <= max_inject_rows.
+ */
+dflash_status dflash_inject_kv(dflash_ctx* ctx, void* stream,
+                               const void* const* target_hidden, int64_t ld,
+                               int32_t T, const int32_t* row_seq,
+                               const int32_t* row_pos, void* kv_cache);
+
+/* Draft one block per sequence in a single forward pass (or S passes).
+ *
+ * Passage: "DFlash Guide", section "1. Single-Pass Block-Diffusion Drafting"
+ * (argmax over the drafter's output for a masked block given the context and
+ * target features, one forward pass) and "Architectural Comparison" (the
+ * block positions attend to each other bidirectionally); stable-lab "The
+ * Model at a Glance" (S = 1-2 refinement passes committing positions in
+ * confidence order; injected context is reused).
+ *
+ * Sequence b (slot b) has ctx_len[b] = L_b injected context positions.  The
+ * block occupies positions L_b .. L_b+K-1; index 0 is the anchor (the last
+ * verified token), indices 1..K-1 start as mask_token_id.  Each pass embeds
+ * the block, runs every layer once over all K rows (attention over the L_b
+ * context keys plus all K block keys, no mask), then the final norm and LM
+ * head for still-masked rows only.  Per row: argmax (ties -> lowest id),
+ * confidence = top-1 softmax probability, margin = top-1 minus top-2 logit.
+ * Pass s < S commits the commit_per_pass most confident masked positions
+ * (ties -> lower index); pass S commits the rest.
+ *
+ * batch:          1 <= batch <= max_batch.
+ * anchor:         [batch] int32 anchor ids; ignored when block_tokens given.
+ * block_tokens:   NULL, or [batch, K] int32 starting block: index 0 is the
+ *                 anchor, mask_token_id marks masked positions, other ids
+ *                 are already committed.
+ * ctx_len:        [batch] int32 L_b in [0, max_ctx_len] (values outside
+ *                 are clamped and set DFLASH_DEVERR_CTX_LEN).
+ * max_ctx_len:    host upper bound on every ctx_len[b] (sizes the attention
+ *                 grid), 0 <= max_ctx_len <= max_ctx.
+ * kv_cache:       as for dflash_inject_kv; positions [L_b, L_b+K) of each
+ *                 slot are overwritten with the block's own K/V.
+ * num_passes:     S >= 1; commit_per_pass c >= 1 when S > 1, with
+ *                 c * (S-1) < K-1.
+ * draft_tokens:   [batch, K-1] int32 out: the drafted id at block index i+1
+ *                 (a position already committed in block_tokens is returned
+ *                 as given).
+ * confidence:     NULL or [batch, K-1] fp32 out (from the committing pass;
+ *                 not written for positions committed in block_tokens).
+ * top2_margin:    NULL or [batch, K-1] fp32 out (as confidence).
+ * logits_debug:   NULL or [S, batch, K-1, V] fp32 out: logits of every row
+ *                 computed in pass s (rows not computed are not written).
+ *                 For parity tests only; costs a full logits write.
+ */
+dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
+                                 const int32_t* anchor,
+                                 const int32_t* block_tokens,
+                                 const int32_t* ctx_len, int32_t max_ctx_len,
+                                 void* kv_cache, int32_t num_passes,
+                                 int32_t commit_per_pass,
+                                 int32_t* draft_tokens, float* confidence,
+                                 float* top2_margin, float* logits_debug);
+
+/* Greedy verification.
+ *
+ * Passage: "DFlash Guide", section "The Cost Breakdown of Speculative Rounds"
+ * (the target checks all drafts in one pass and keeps the longest valid
+ * prefix; latency is amortised over tau + 1 tokens); stable-lab "Common
+ * misconception" (nothing drafted survives unless the target agrees, so the
+ * output is exactly the target's).  With greedy decoding the acceptance rule
+ * is an exact match.
+ *
+ * draft_tokens:  [batch, K-1] int32, draft for block index j+1.
+ * target_argmax: [batch, K] int32, the target's greedy id for block index
+ *                j+1 (entry K-1 is the id after the last drafted position).
+ * accept_len:    [batch] int32 out, tau + 1 where tau is the number of
+ *                leading j with draft[j] == target[j] (1 <= accept_len <= K).
+ * next_anchor:   [batch] int32 out, target_argmax[b][tau].
+ * Needs no context; 1 <= block_size <= 64.
+ */
+dflash_status dflash_verify_greedy(void* stream, int32_t batch,
+                                   int32_t block_size,
+                                   const int32_t* draft_tokens,
+                                   const int32_t* target_argmax,
+                                   int32_t* accept_len, int32_t* next_anchor);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

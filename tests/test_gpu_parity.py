@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Inputs come from the seeded ``workloads`` generators and are handed to both
+sides unchanged; nothing the GPU computes is fed to the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import (OracleModel, draft_batch, inject_rows, synthetic_target,
+                    verify_greedy as oracle_verify)
+from tests.gpu_common import (DEV, LOGCONF_TOL, LOGIT_TOL, MARGIN_MIN,
+                              cache_rows, check_bf16_close, compare_draft,
+                              f64, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+dfl = pytest.importorskip("block_diffusion_drafting_dflash_amd")
+
+
+def small_s2():
+    return W.small_bf16(num_passes=2, commit_per_pass=8, name="small-bf16-S2")
+
+
+WLS = {
+    "tiny-f32": W.WORKLOADS["tiny-f32"],
+    "small-bf16": W.small_bf16(),
+}
+
+
+def _setup(wl, random_gains=False, max_ctx=None):
+    w_cpu = W.gen_weights(wl, random_gains=random_gains)
+    w_dev = to_dev(w_cpu)
+    ctx = dfl.DFlash(wl, w_dev, max_ctx=max_ctx)
+    return w_cpu, w_dev, ctx
+
+
+# ------------------------------------------------------------- verify -----
+
+def test_verify_all_patterns_bit_exact():
+    K1 = 15
+    B = 1 << K1
+    rng = np.random.default_rng(0)
+    draft = rng.integers(0, 151936, (B, K1)).astype(np.int32)
+    pat = np.arange(B)[:, None] >> np.arange(K1)[None, :] & 1
+    target = np.concatenate([np.where(pat == 1, draft, draft + 1),
+                             rng.integers(0, 151936, (B, 1))], 1).astype(np.int32)
+    acc, nxt = dfl.verify_greedy(torch.from_numpy(draft).to(DEV),
+                                 torch.from_numpy(target).to(DEV))
+    acc, nxt = acc.cpu().numpy(), nxt.cpu().numpy()
+    for b in range(0, B, 7):
+        a, n = oracle_verify(draft[b], target[b])
+        assert acc[b] == a and nxt[b] == n
+    lead = np.argmin(np.concatenate([pat, np.zeros((B, 1), int)], 1), 1)
+    np.testing.assert_array_equal(acc, lead + 1)
+
+
+def test_synthetic_target_harness_matches_oracle():
+    wl = W.WORKLOADS["qwen3-8b-3L-b4-ctx32k"].replace(batch=512)
+    d = W.gen_verify_draws(wl)
+    rng = np.random.default_rng(1)
+    draft = rng.integers(0, wl.vocab, (wl.batch, 15)).astype(np.int32)
+    T = dfl.synth_target(*(torch.from_numpy(a).to(DEV) for a in (
+        draft, d["u"], d["r"], d["tail"], d["p"])), wl.vocab)
+    ref = synthetic_target(draft, d["u"], d["r"], d["tail"], d["p"], wl.vocab)
+    np.testing.assert_array_equal(T.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------ inject ------
+
+@pytest.mark.parametrize("name", list(WLS))
+@pytest.mark.parametrize("gains", [False, True])
+def test_inject_kv_parity(name, gains):
+    wl = WLS[name]
+    say(f"[inject] {name} random_gains={gains}")
+    w_cpu, w_dev, ctx = _setup(wl, random_gains=gains)
+    model = OracleModel(wl, w_cpu)
+    lens = W.gen_ctx_lens(wl)
+    kv = ctx.new_kv_cache()
+    # two calls with ragged row counts, rows of several sequences interleaved
+    seqs, poss = [], []
+    for b, L in enumerate(lens):
+        seqs += [b] * int(L)
+        poss += list(range(int(L)))
+    seqs, poss = np.array(seqs), np.array(poss)
+    perm = np.random.default_rng(2).permutation(len(seqs))
+    seqs, poss = seqs[perm], poss[perm]
+    H = W.gen_hiddens(wl, len(seqs))
+    cut = len(seqs) // 3 + 1
+    for lo, hi in ((0, cut), (cut, len(seqs))):
+        ctx.inject_kv([h[lo:hi].to(DEV) for h in H],
+                      torch.from_numpy(seqs[lo:hi].astype(np.int32)).to(DEV),
+                      torch.from_numpy(poss[lo:hi].astype(np.int32)).to(DEV),
+                      kv)
+    torch.cuda.synchronize()
+    assert ctx.check_device_errors() == 0
+    ref = inject_rows(model, H, poss)
+    for l in range(wl.num_layers):
+        for b, L in enumerate(lens):
+            sel = np.nonzero(seqs == b)[0]
+            order = np.argsort(poss[sel])
+            rk = ref[l][0][sel][order]
+            rv = ref[l][1][sel][order]
+            gk, gv = cache_rows(kv, l, b, int(L))
+            if wl.dtype == "bf16":
+                check_bf16_close(gk, rk, f"K l{l} b{b}")
+                check_bf16_close(gv, rv, f"V l{l} b{b}")
+            else:
+                np.testing.assert_allclose(gk, rk, rtol=1e-4, atol=2e-5)
+                np.testing.assert_allclose(gv, rv, rtol=1e-4, atol=2e-5)
+
+
+def test_inject_device_errors_are_reported():
+    wl = WLS["small-bf16"]
+    _, _, ctx = _setup(wl)
+    kv = ctx.new_kv_cache()
+    H = [h.to(DEV) for h in W.gen_hiddens(wl, 3)]
+    seq = torch.tensor([0, 99, 1], dtype=torch.int32, device=DEV)
+    pos = torch.tensor([0, 1, 5], dtype=torch.int32, device=DEV)
+    ctx.inject_kv(H, seq, pos, kv)
+    bits = ctx.check_device_errors()
+    assert bits & 0x4
+    pos = torch.tensor([0, 1, 10 ** 6], dtype=torch.int32, device=DEV)
+    seq = torch.tensor([0, 1, 1], dtype=torch.int32, device=DEV)
+    ctx.inject_kv(H, seq, pos, kv)
+    assert ctx.check_device_errors() & 0x8
+    assert ctx.check_device_errors() == 0
+
+
+# ------------------------------------------------------------- draft ------
+
+def _seeded_cache(wl, ctx, lens):
+    """Context KV written directly from the seeded generator (shared data)."""
+    kv = ctx.new_kv_cache()
+    per_seq = []
+    for b, L in enumerate(lens):
+        d = {}
+        for l in range(wl.num_layers):
+            k = W.gen_kv_prefix(wl, l, "k", b, int(L), device=DEV)
+            v = W.gen_kv_prefix(wl, l, "v", b, int(L), device=DEV)
+            kv[l, 0, b, :, :L] = k
+            kv[l, 1, b, :, :L] = v
+            d[l] = (f64(k).transpose(1, 0, 2), f64(v).transpose(1, 0, 2))
+        per_seq.append(d)
+    return kv, per_seq
+
+
+def _gpu_draft(ctx, wl, lens, kv, anchors=None, block=None, S=1, c=0):
+    B = len(lens)
+    K1 = wl.block_size - 1
+    draft = torch.full((B, K1), -7, dtype=torch.int32, device=DEV)
+    conf = torch.full((B, K1), float("nan"), device=DEV)
+    margin = torch.full((B, K1), float("nan"), device=DEV)
+    logits = torch.full((S, B, K1, wl.vocab), float("nan"), device=DEV)
+    ctx.draft_block(
+        torch.from_numpy(np.asarray(lens, np.int32)).to(DEV), kv,
+        int(max(lens)),
+        anchor=None if anchors is None else torch.from_numpy(
+            np.asarray(anchors, np.int32)).to(DEV),
+        block_tokens=None if block is None else torch.from_numpy(
+            np.asarray(block, np.int32)).to(DEV),
+        num_passes=S, commit_per_pass=c, draft=draft, conf=conf,
+        margin=margin, logits=logits)
+    torch.cuda.synchronize()
+    assert ctx.check_device_errors() == 0
+    return {"draft": draft.cpu().numpy(), "conf": conf.cpu().numpy(),
+            "margin": margin.cpu().numpy(), "logits_all": logits.cpu().numpy()}
+
+
+@pytest.mark.parametrize("name", list(WLS))
+def test_draft_single_pass_parity(name):
+    wl = WLS[name]
+    say(f"[draft S=1] {name}")
+    w_cpu, w_dev, ctx = _setup(wl, random_gains=True)
+    model = OracleModel(wl, w_cpu)
+    lens = W.gen_ctx_lens(wl)
+    kv, per_seq = _seeded_cache(wl, ctx, lens)
+    anchors = W.gen_anchors(wl)
+    g = _gpu_draft(ctx, wl, lens, kv, anchors=anchors)
+    ref = draft_batch(model, per_seq, lens, anchors=anchors, keep_logits=True)
+    g["logits"] = g["logits_all"][0]
+    comp, excl, dl = compare_draft(wl, g, ref)
+    say(f"  tokens compared {comp}, excluded {excl}, max |dlogit| {dl:.2e}")
+    assert comp > 0
+    lc = np.abs(np.log(g["conf"]) - np.log(np.stack([o["conf"][1:] for o in ref])))
+    assert lc.max() <= LOGCONF_TOL[wl.dtype]
+    mg = np.stack([o["margin"][1:] for o in ref])
+    assert np.abs(g["margin"] - mg).max() <= 2 * LOGIT_TOL[wl.dtype]
+
+
+def test_draft_two_pass_parity_and_teacher_forcing():
+    wl = small_s2()
+    say("[draft S=2] small-bf16")
+    w_cpu, w_dev, ctx = _setup(wl)
+    model = OracleModel(wl, w_cpu)
+    lens = W.gen_ctx_lens(wl)
+    kv, per_seq = _seeded_cache(wl, ctx, lens)
+    anchors = W.gen_anchors(wl)
+    g = _gpu_draft(ctx, wl, lens, kv, anchors=anchors, S=2, c=8)
+    ref = draft_batch(model, per_seq, lens, anchors=anchors, num_passes=2,
+                      commit_per_pass=8, keep_logits=True)
+    tol = LOGIT_TOL[wl.dtype]
+    # pass 1: every row computed
+    for b, o in enumerate(ref):
+        z1 = g["logits_all"][0][b]
+        assert np.abs(z1 - o["logits"][0]).max() <= tol
+    # commit sets compared where the oracle's cut is clear
+    teacher = []
+    for b, o in enumerate(ref):
+        c1 = o["pass_conf"][0][1:]
+        order = sorted(range(15), key=lambda i: (-c1[i], i))
+        gap = np.log(c1[order[7]]) - np.log(c1[order[8]])
+        oracle_set = set(np.nonzero(o["pass"] == 0)[0].tolist())
+        gpu_rows_p2 = set(np.nonzero(~np.isnan(g["logits_all"][1][b][:, 0]))[0]
+                          + 1)
+        gpu_set = set(range(1, 16)) - gpu_rows_p2
+        if gap > MARGIN_MIN:
+            assert gpu_set == oracle_set, f"seq {b}: commit sets differ"
+            rows2 = o["masked_rows"][1]
+            z2 = g["logits_all"][1][b][rows2 - 1]
+            assert np.abs(z2 - o["logits"][1]).max() <= tol
+        blk = np.full(16, wl.mask_id)
+        blk[0] = anchors[b]
+        for i in oracle_set:
+            blk[i] = o["tokens"][i]
+        teacher.append(blk)
+    # teacher-forced second pass from the oracle's own pass-1 commits
+    tf = _gpu_draft(ctx, wl, lens, kv, block=np.stack(teacher), S=1)
+    for b, o in enumerate(ref):
+        rows2 = o["masked_rows"][1]
+        z2 = tf["logits_all"][0][b][rows2 - 1]
+        assert np.abs(z2 - o["logits"][1]).max() <= tol
+        for i in rows2:
+            if o["pass_margin"][1][int(i)] > MARGIN_MIN:
+                assert tf["draft"][b, i - 1] == o["pass_token"][1][int(i)]
+        # caller-committed positions come back as given
+        for i in range(1, 16):
+            if i not in rows2:
+                assert tf["draft"][b, i - 1] == teacher[b][i]
+    # bidirectional: changing a later committed token moves an earlier row
+    blk2 = np.stack(teacher).copy()
+    b0 = 0
+    later = max(i for i in range(1, 16) if blk2[b0][i] != wl.mask_id)
+    early = min(o for o in ref[b0]["masked_rows"][1])
+    if early < later:
+        blk2[b0][later] = (blk2[b0][later] + 1) % (wl.vocab - 1)
+        tf2 = _gpu_draft(ctx, wl, lens, kv, block=blk2, S=1)
+        d = np.abs(tf2["logits_all"][0][b0][early - 1] -
+                   tf["logits_all"][0][b0][early - 1]).max()
+        assert d > 1e-3
+
+
+def test_draft_is_deterministic():
+    wl = WLS["small-bf16"]
+    w_cpu, w_dev, ctx = _setup(wl)
+    lens = W.gen_ctx_lens(wl)
+    kv, _ = _seeded_cache(wl, ctx, lens)
+    anchors = W.gen_anchors(wl)
+    a = _gpu_draft(ctx, wl, lens, kv, anchors=anchors)
+    b = _gpu_draft(ctx, wl, lens, kv, anchors=anchors)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+# -------------------------------------------------------- whole step ------
+
+@pytest.mark.parametrize("name", list(WLS))
+def test_full_step_inject_draft_verify(name):
+    """Inject the whole context, draft, synthetic target, verify."""
+    wl = WLS[name]
+    say(f"[step] {name}")
+    w_cpu, w_dev, ctx = _setup(wl)
+    model = OracleModel(wl, w_cpu)
+    lens = W.gen_ctx_lens(wl)
+    kv = ctx.new_kv_cache()
+    per_seq = []
+    for b, L in enumerate(lens):
+        H = W.gen_hiddens(wl, int(L), index=b)
+        pos = np.arange(int(L), dtype=np.int32)
+        ctx.inject_kv([h.to(DEV) for h in H],
+                      torch.full((int(L),), b, dtype=torch.int32, device=DEV),
+                      torch.from_numpy(pos).to(DEV), kv)
+        per_seq.append(inject_rows(model, H, pos))
+    anchors = W.gen_anchors(wl)
+    g = _gpu_draft(ctx, wl, lens, kv, anchors=anchors)
+    ref = draft_batch(model, per_seq, lens, anchors=anchors, keep_logits=True)
+    g["logits"] = g["logits_all"][0]
+    comp, excl, dl = compare_draft(wl, g, ref)
+    say(f"  tokens compared {comp}, excluded {excl}, max |dlogit| {dl:.2e}")
+    d = W.gen_verify_draws(wl)
+    dd = {k: torch.from_numpy(v).to(DEV) for k, v in d.items()}
+    gdraft = torch.from_numpy(g["draft"]).to(DEV)
+    T = dfl.synth_target(gdraft, dd["u"], dd["r"], dd["tail"], dd["p"],
+                         wl.vocab)
+    acc, nxt = dfl.verify_greedy(gdraft, T)
+    acc, nxt = acc.cpu().numpy(), nxt.cpu().numpy()
+    odraft = np.stack([o["draft"] for o in ref])
+    oT = synthetic_target(odraft, d["u"], d["r"], d["tail"], d["p"], wl.vocab)
+    for b, o in enumerate(ref):
+        a_ref, n_ref = oracle_verify(odraft[b], oT[b])
+        # tau is decided by drafted positions 1 .. min(a_ref, K-1)
+        decisive = range(1, min(a_ref, 15) + 1)
+        if all(o["margin"][i] > MARGIN_MIN for i in decisive):
+            assert acc[b] == a_ref and nxt[b] == n_ref
