@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Drafted tokens/s of one DFlash drafting step on one MI355X.
+
+A step is the whole drafting path for one batch: KV injection of 16 new
+context rows per sequence, the block draft (all layers, LM head, argmax /
+confidence commit over S passes), the synthetic target's greedy tokens (a
+stand-in for the target model, which is out of scope) and greedy
+verification.  Inputs (weights, hidden states, ids, random draws) are resident
+in HBM before the timed region; the prefix context is injected untimed.
+
+Prints one JSON line.  `value` = drafted tokens per second = batch * (K - 1)
+* steps / elapsed.  `roofline` rates the dominant kernel against its bound
+(HBM bytes or MFMA flops) with its duration taken from HIP events around
+each of its launches inside the timed region.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+import workloads as W
+
+METRIC = "drafted tokens/s (K=16 block, incl. KV injection) + % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK = {"bf16": 2500.0, "f32": 157.3}   # dense TFLOP/s (f32: vector)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=W.HEADLINE,
+                    choices=list(W.WORKLOADS))
+    ap.add_argument("--timed-kernel", default="auto",
+                    choices=["auto", "lmhead", "attention", "gemm"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter scale)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic cost of a step (bytes that must cross HBM, flops of the math)
+# ---------------------------------------------------------------------------
+
+def step_cost(wl, lens):
+    esz = 4 if wl.dtype == "f32" else 2
+    D, I, V, d = wl.hidden, wl.intermediate, wl.vocab, wl.head_dim
+    qd, kvd = wl.num_q_heads * d, wl.num_kv_heads * d
+    B, K, Nl = wl.batch, wl.block_size, wl.num_layers
+    T = B * wl.new_rows
+    ntd = wl.num_target_layers * wl.target_hidden
+    by = fl = 0.0
+    # injection
+    by += T * ntd * esz + D * ntd * esz + Nl * 2 * kvd * D * esz
+    by += T * Nl * 2 * kvd * esz + D * esz
+    fl += 2.0 * T * D * ntd + 2.0 * T * Nl * 2 * kvd * D
+    lm = []
+    R = B * K
+    for s in range(wl.num_passes):
+        masked = B * (K - 1 - s * wl.commit_per_pass)
+        by += R * D * esz
+        layer_w = ((qd + 2 * kvd) * D + qd * D + 3 * I * D + 2 * D) * esz
+        kv_read = sum((int(L) + K) * 2 * kvd * esz for L in lens)
+        by += Nl * (layer_w + kv_read + R * 2 * kvd * esz)
+        fl += Nl * 2.0 * R * ((qd + 2 * kvd) * D + qd * D + 3 * I * D)
+        fl += Nl * sum(4.0 * wl.num_q_heads * K * (int(L) + K) * d for L in lens)
+        lm_bytes = V * D * esz + masked * D * esz + D * esz
+        lm_flops = 2.0 * masked * V * D
+        by += lm_bytes
+        fl += lm_flops
+        lm.append((lm_bytes, lm_flops))
+    by += B * (2 * K - 1) * 4 * 2
+    return by, fl, lm
+
+
+def kernel_cost(wl, lens, kind):
+    """Algorithmic (bytes, flops) per launch of the timed kernel class,
+    averaged over its launches in one step."""
+    esz = 4 if wl.dtype == "f32" else 2
+    D, I, d = wl.hidden, wl.intermediate, wl.head_dim
+    qd, kvd = wl.num_q_heads * d, wl.num_kv_heads * d
+    B, K = wl.batch, wl.block_size
+    if kind == "lmhead":
+        _, _, lm = step_cost(wl, lens)
+        return (sum(b for b, _ in lm) / len(lm), sum(f for _, f in lm) / len(lm))
+    if kind == "attention":
+        kv = sum((int(L) + K) * 2 * kvd * esz for L in lens)
+        q_o = 2 * B * K * qd * esz
+        fl = sum(4.0 * wl.num_q_heads * K * (int(L) + K) * d for L in lens)
+        return kv + q_o, fl
+    # every projection GEMM launch of a step: inject fc + kv, then per layer
+    # qkv, o, gate/up, down
+    T = B * wl.new_rows
+    ntd = wl.num_target_layers * wl.target_hidden
+    R = B * K
+    shapes = [(T, D, ntd), (T, wl.num_layers * 2 * kvd, D)]
+    for _ in range(wl.num_passes):
+        for _ in range(wl.num_layers):
+            shapes += [(R, qd + 2 * kvd, D), (R, D, qd), (R, 2 * I, D), (R, D, I)]
+    by = sum((n * k + m * k) * esz for m, n, k in shapes)
+    fl = sum(2.0 * m * n * k for m, n, k in shapes)
+    return by / len(shapes), fl / len(shapes)
+
+
+# ---------------------------------------------------------------------------
+
+def setup(wl, torch, dfl, dev):
+    weights = W.gen_weights(wl, device=dev)
+    lens = W.gen_ctx_lens(wl)
+    B, K = wl.batch, wl.block_size
+    chunk = 2048
+    ctx = dfl.DFlash(wl, weights, max_inject_rows=max(chunk, B * wl.new_rows))
+    kv = ctx.new_kv_cache(dev)
+    # untimed prefix: positions [0, L_b - 16) of every sequence
+    for b, L in enumerate(lens):
+        n_pre = int(L) - wl.new_rows
+        for c0 in range(0, n_pre, chunk):
+            n = min(chunk, n_pre - c0)
+            H = W.gen_hiddens(wl, n, device=dev, index=b * 100000 + c0 // chunk,
+                              tag="prefix")
+            ctx.inject_kv(H, torch.full((n,), b, dtype=torch.int32, device=dev),
+                          torch.arange(c0, c0 + n, dtype=torch.int32,
+                                       device=dev), kv)
+    torch.cuda.synchronize()
+    T = B * wl.new_rows
+    inp = {
+        "H": W.gen_hiddens(wl, T, device=dev, index=0, tag="step"),
+        "row_seq": torch.arange(B, dtype=torch.int32,
+                                device=dev).repeat_interleave(wl.new_rows),
+        "row_pos": torch.from_numpy(np.concatenate(
+            [np.arange(int(L) - wl.new_rows, int(L)) for L in lens]).astype(
+                np.int32)).to(dev),
+        "ctx_len": torch.from_numpy(lens.astype(np.int32)).to(dev),
+        "anchor": torch.from_numpy(W.gen_anchors(wl)).to(dev),
+    }
+    draws = W.gen_verify_draws(wl)
+    for k, v in draws.items():
+        inp[k] = torch.from_numpy(v).to(dev)
+    inp["draft"] = torch.zeros(B, K - 1, dtype=torch.int32, device=dev)
+    inp["target"] = torch.zeros(B, K, dtype=torch.int32, device=dev)
+    inp["accept"] = torch.zeros(B, dtype=torch.int32, device=dev)
+    inp["next"] = torch.zeros(B, dtype=torch.int32, device=dev)
+    return ctx, kv, lens, inp, weights
+
+
+def make_step(ctx, kv, lens, inp, wl, torch, dfl):
+    """Pre-marshalled C-ABI calls of one step on torch's current stream."""
+    lib, har = dfl.load_library(), dfl.load_harness()
+    vp = ctypes.c_void_p
+    P = lambda t: vp(t.data_ptr())
+    s = vp(torch.cuda.current_stream().cuda_stream)
+    H = inp["H"]
+    harr = (vp * len(H))(*[h.data_ptr() for h in H])
+    hpp = ctypes.cast(harr, ctypes.POINTER(vp))
+    T, ld = H[0].shape[0], H[0].stride(0)
+    B, K = wl.batch, wl.block_size
+    maxL = int(max(lens))
+    a = dict(seq=P(inp["row_seq"]), pos=P(inp["row_pos"]), kv=P(kv),
+             cl=P(inp["ctx_len"]), an=P(inp["anchor"]), dr=P(inp["draft"]),
+             u=P(inp["u"]), r=P(inp["r"]), tail=P(inp["tail"]), p=P(inp["p"]),
+             tg=P(inp["target"]), acc=P(inp["accept"]), nx=P(inp["next"]))
+    S, c = wl.num_passes, wl.commit_per_pass
+    ctxp = ctx.ctx
+
+    def step():
+        st = lib.dflash_inject_kv(ctxp, s, hpp, ld, T, a["seq"], a["pos"],
+                                  a["kv"])
+        st |= lib.dflash_draft_block(ctxp, s, B, a["an"], None, a["cl"], maxL,
+                                     a["kv"], S, c, a["dr"], None, None, None)
+        st |= har.dflash_harness_synth_target(s, B, K, wl.vocab, a["dr"],
+                                              a["u"], a["r"], a["tail"],
+                                              a["p"], a["tg"])
+        st |= lib.dflash_verify_greedy(s, B, K, a["dr"], a["tg"], a["acc"],
+                                       a["nx"])
+        if st != 0:
+            raise RuntimeError("a drafting call failed: " +
+                               lib.dflash_last_error().decode())
+    return step
+
+
+def cpu_baseline(wl, weights, lens, budget_s):
+    """The oracle as it stands, one step at a time on a sample of the
+    workload's sequences: inject the 16 new rows, draft, verify."""
+    import torch
+    from oracle import (OracleModel, draft_batch, inject_rows,
+                        synthetic_target, verify_greedy)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or
+                      [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    model = OracleModel(wl, weights)
+    draws = W.gen_verify_draws(wl)
+    anchors = W.gen_anchors(wl)
+    H_step = W.gen_hiddens(wl, wl.batch * wl.new_rows, device="cuda", index=0,
+                           tag="step")
+    H_step = [h.cpu() for h in H_step]
+    n_new = wl.new_rows
+    done_seqs, elapsed, steps = 0, 0.0, 0
+    b = 0
+    while elapsed < budget_s and steps < 64:
+        L = int(lens[b])
+        # context prefix: seeded stand-in with the injected prefix's shape
+        prefix = {}
+        for l in range(wl.num_layers):
+            k = W.gen_kv_prefix(wl, l, "k", b, L - n_new).float().numpy()
+            v = W.gen_kv_prefix(wl, l, "v", b, L - n_new).float().numpy()
+            prefix[l] = (k.astype(np.float64).transpose(1, 0, 2),
+                         v.astype(np.float64).transpose(1, 0, 2))
+        rows = slice(b * n_new, (b + 1) * n_new)
+        t0 = time.perf_counter()
+        new = inject_rows(model, [h[rows] for h in H_step],
+                          np.arange(L - n_new, L))
+        ctx_kv = {l: (np.concatenate([prefix[l][0], new[l][0]]),
+                      np.concatenate([prefix[l][1], new[l][1]]))
+                  for l in model.layers}
+        res = draft_batch(model, [ctx_kv], [L], anchors=[anchors[b]],
+                          num_passes=wl.num_passes,
+                          commit_per_pass=wl.commit_per_pass)[0]
+        Tg = synthetic_target(res["draft"][None], draws["u"][b:b + 1],
+                              draws["r"][b:b + 1], draws["tail"][b:b + 1],
+                              draws["p"], wl.vocab)
+        verify_greedy(res["draft"], Tg[0])
+        elapsed += time.perf_counter() - t0
+        steps += 1
+        done_seqs += 1
+        b = (b + 1) % wl.batch
+    return {"value": done_seqs * (wl.block_size - 1) / elapsed,
+            "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{steps} single-sequence step(s) of {wl.name} "
+                       f"(inject 16 rows + {wl.num_passes}-pass draft + "
+                       f"verify; context prefix from the seeded generator), "
+                       f"{elapsed:.1f} s of float64 numpy on the host")}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the drafting path is not sharded in this "
+              "build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_diffusion_drafting_dflash_amd as dfl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = W.WORKLOADS[args.workload]
+    kind = args.timed_kernel
+    if kind == "auto":
+        kind = {"qwen3-8b-3L-b4-ctx32k": "attention",
+                "qwen3-8b-3L-b64-ctx256-2k-S2": "gemm",
+                "qwen3-8b-5L-b16-ctx1k-4k": "gemm"}.get(wl.name, "lmhead")
+
+    ctx, kv, lens, inp, weights = setup(wl, torch, dfl, dev)
+    step = make_step(ctx, kv, lens, inp, wl, torch, dfl)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if ctx.check_device_errors() != 0:
+        raise RuntimeError("device error during warmup")
+
+    ctx.set_kernel_timing(kind)
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(
+        enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    n_launch, k_ms = ctx.kernel_timing()
+    ctx.set_kernel_timing("off")
+    ms_step = ms_total / args.steps
+    drafted = wl.batch * (wl.block_size - 1)
+    value = drafted * args.steps / (ms_total / 1e3)
+
+    by, fl, _ = step_cost(wl, lens)
+    kb, kf = kernel_cost(wl, lens, kind)
+    k_avg_s = (k_ms / max(n_launch, 1)) / 1e3
+    bound = "hbm" if (kf / max(kb, 1)) < (MFMA_PEAK[wl.dtype] * 1e12 /
+                                          (HBM_PEAK_GBS * 1e9)) else "mfma"
+    if bound == "hbm":
+        ach, peak, unit = kb / k_avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        ach, peak, unit = kf / k_avg_s / 1e12, MFMA_PEAK[wl.dtype], "TFLOP/s"
+    acc = inp["accept"].cpu().numpy()
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch,
+                   "ctx_len": [int(lens.min()), int(lens.max())],
+                   "block": wl.block_size, "draft_layers": wl.num_layers,
+                   "passes": wl.num_passes,
+                   "commit_per_pass": wl.commit_per_pass,
+                   "new_rows_per_seq": wl.new_rows},
+        "roofline": {"kernel": kind, "bound": bound, "achieved": round(ach, 1),
+                     "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+                     "traffic": None, "launches": n_launch,
+                     "avg_us": round(k_avg_s * 1e6, 2),
+                     "alg_bytes_per_launch": int(kb),
+                     "alg_flops_per_launch": kf},
+        "step": {"alg_bytes": int(by), "alg_flops": fl,
+                 "hbm_frac": round(by / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "mfma_frac": round(fl / (ms_step / 1e3) / 1e12 /
+                                    MFMA_PEAK[wl.dtype], 4),
+                 "mean_accept_len": float(acc.mean())},
+    }
+    if args.copy_calibration:
+        n = 1 << 28
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n * 4
+    if not args.no_cpu_baseline:
+        del ctx, kv
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(wl, weights, lens, args.cpu_budget)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 3)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

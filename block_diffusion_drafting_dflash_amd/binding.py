@@ -27,7 +27,9 @@ DTYPE = {"f32": 0, "bf16": 1}
 LIB_SYMBOLS = ["dflash_create", "dflash_destroy", "dflash_kv_cache_bytes",
                "dflash_last_error", "dflash_check_device_errors",
                "dflash_inject_kv", "dflash_draft_block",
-               "dflash_verify_greedy"]
+               "dflash_verify_greedy", "dflash_set_kernel_timing",
+               "dflash_get_kernel_timing"]
+TIME_KIND = {"off": 0, "lmhead": 1, "attention": 2, "gemm": 3}
 HARNESS_SYMBOLS = ["dflash_harness_synth_target"]
 
 
@@ -92,6 +94,11 @@ def load_library():
     lib.dflash_draft_block.restype = ctypes.c_int
     lib.dflash_verify_greedy.argtypes = [vp, i32, i32, vp, vp, vp, vp]
     lib.dflash_verify_greedy.restype = ctypes.c_int
+    lib.dflash_set_kernel_timing.argtypes = [vp, i32]
+    lib.dflash_set_kernel_timing.restype = ctypes.c_int
+    lib.dflash_get_kernel_timing.argtypes = [vp, ctypes.POINTER(i32),
+                                             ctypes.POINTER(ctypes.c_double)]
+    lib.dflash_get_kernel_timing.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -232,6 +239,17 @@ class DFlash:
             commit_per_pass, _ptr(draft), _ptr(conf), _ptr(margin),
             _ptr(logits)))
         return draft
+
+    def set_kernel_timing(self, kind: str):
+        _check(self.lib.dflash_set_kernel_timing(self.ctx, TIME_KIND[kind]))
+
+    def kernel_timing(self):
+        """(launches recorded, summed milliseconds) since the last call."""
+        n = ctypes.c_int32(0)
+        ms = ctypes.c_double(0.0)
+        _check(self.lib.dflash_get_kernel_timing(self.ctx, ctypes.byref(n),
+                                                 ctypes.byref(ms)))
+        return n.value, ms.value
 
     def check_device_errors(self, stream=None) -> int:
         bits = ctypes.c_int32(0)

@@ -164,28 +164,44 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
   }
 }
 
-// o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the sequence's chunks.
-template <typename T>
-__global__ void attn_merge_kernel(AttnArgs p, int D) {
-  const int bh = blockIdx.x, b = bh / p.Hq, hq = bh % p.Hq;
+// o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the sequence's
+// chunks (M = the largest m_c), in chunk order, written packed for the output
+// projection.  One workgroup per (sequence, query head, 4 block queries);
+// 32 lanes per query, each owning D/32 consecutive channels.
+template <typename T, int D>
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs p) {
+  constexpr int DPT = D / 32;
+  const int groups = p.K / 4;
+  const int bh = blockIdx.x / groups, qg = blockIdx.x % groups;
+  const int b = bh / p.Hq, hq = bh % p.Hq;
+  const int i = qg * 4 + (threadIdx.x >> 5);
+  const int d0 = (threadIdx.x & 31) * DPT;
   int L = p.ctx_len[b];
   L = min(max(L, 0), p.max_len);
   const int nc = (L + p.K + p.chunk - 1) / p.chunk;
-  const int dd = threadIdx.x;
-  T* out = static_cast<T*>(p.o);
-  for (int i = 0; i < p.K; ++i) {
-    const int64_t base = ((int64_t)b * p.Hq + hq) * p.nch * p.K + i;
-    float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, p.part_ml[(base + (int64_t)c * p.K) * 2]);
-    float acc = 0.f, ls = 0.f;
-    for (int c = 0; c < nc; ++c) {
-      const int64_t e = base + (int64_t)c * p.K;
-      const float w = exp2f(p.part_ml[e * 2] - M);
-      acc += w * p.part_o[e * D + dd];
-      ls += w * p.part_ml[e * 2 + 1];
-    }
-    store_elem(out, (int64_t)(b * p.K + i) * p.Hq * D + hq * D + dd, acc / ls);
+  const int64_t base = ((int64_t)b * p.Hq + hq) * p.nch * p.K + i;
+  const float* ml = p.part_ml + base * 2;
+  const int64_t cstride = (int64_t)p.K;  // entries between chunks
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[c * cstride * 2]);
+  float ls = 0.f, acc[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < nc; ++c) {
+    const float w = exp2f(ml[c * cstride * 2] - M);
+    ls += w * ml[c * cstride * 2 + 1];
+    const float* oc = p.part_o + (base + c * cstride) * D + d0;
+#pragma unroll
+    for (int k = 0; k < DPT; ++k) acc[k] += w * oc[k];
   }
+  const float inv = 1.f / ls;
+  const int row = b * p.K + i, Kd = p.Hq * D;
+  T* dst = reinterpret_cast<T*>(static_cast<char*>(p.o) +
+                                packed_offset<T>(row, hq * D + d0, Kd));
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) store_elem(dst, k, acc[k] * inv);
 }
 
 template <typename T, int D>
@@ -195,7 +211,8 @@ hipError_t attn_t(int B, const AttnArgs& a, hipStream_t s) {
                      dim3(64 * G), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge_kernel<T>, dim3(B * a.Hq), dim3(D), 0, s, a, D);
+  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(B * a.Hq * (a.K / 4)),
+                     dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

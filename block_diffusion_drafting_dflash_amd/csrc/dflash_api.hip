@@ -1,6 +1,7 @@
-// Host side of libdflash: argument validation, workspace planning, and the
-// launch sequence of each C-ABI entry point.  Nothing here computes a value
-// of the method except the RoPE cos/sin table built once at create time.
+// Host side of libdflash: argument validation, workspace planning, the
+// one-time weight repack, and the launch sequence of each C-ABI entry point.
+// Nothing here computes a value of the method except the RoPE cos/sin table
+// built once at create time.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -41,6 +42,8 @@ bool aligned16(const void* p) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+constexpr size_t kTimingSlots = 8192;
+
 }  // namespace
 
 struct dflash_ctx {
@@ -50,36 +53,76 @@ struct dflash_ctx {
   int num_cu = 256;
   int P = 0;  // positions per cache slot (max_ctx + block_size)
 
+  // read in place after create: the embedding table and the norm gains
   const void* embed = nullptr;
-  const void* fc = nullptr;
   const void* hidden_norm = nullptr;
   const void* final_norm = nullptr;
-  const void* lm_head = nullptr;
-  std::vector<const void*> attn_norm, wq, wk, wv, wo, mlp_norm, w_gate, w_up,
-      w_down;
+  std::vector<const void*> attn_norm, mlp_norm;
 
+  // packed copies of every projection matrix (fragment-major, see kernels.h)
+  void* wpack = nullptr;
+  void* pk_fc = nullptr;   // [D][n_t * D_t]
+  void* pk_kv = nullptr;   // [N_l * 2 * Hkv * d][D], K/V heads, RoPE pairs
+  void* pk_lm = nullptr;   // [V][D]
+  std::vector<void*> pk_qkv, pk_o, pk_gu, pk_down;
+
+  // workspace
   void* ws = nullptr;
-  size_t partial_floats = 0, attn_floats = 0, lm_part_count = 0;
+  size_t attn_floats = 0, lm_part_count = 0;
   float2* rope = nullptr;
-  float* partial = nullptr;
-  float* x = nullptr;
-  void* h = nullptr;
-  void* qb = nullptr;
-  void* ob = nullptr;
-  void* act = nullptr;
-  void* hf = nullptr;
-  void* hcond = nullptr;
+  float* u = nullptr;        // fused target features before RMSNorm [TI][D]
+  void* cond = nullptr;      // H_cond, packed [TI16][D]
+  float* x = nullptr;        // residual rows [R][D]
+  void* h = nullptr;         // RMSNorm(x) * g, packed [R][D]
+  void* hf = nullptr;        // final-norm rows of still-masked positions, packed
+  void* qb = nullptr;        // q after RoPE [R][Hq*d]
+  void* ob = nullptr;        // attention output, packed [R][Hq*d]
+  void* act = nullptr;       // SwiGLU output, packed [R][I]
   int32_t* tokens = nullptr;
   int32_t* committed = nullptr;
   int32_t* rowmap = nullptr;
-  Top2* lm_part = nullptr;
-  RowResult* rowres = nullptr;
+  Top2* lm_part = nullptr;   // [rows][V/16]
+  Top2* lm_part2 = nullptr;  // [rows][kMergeChunks]
   float* attn_o = nullptr;
   float* attn_ml = nullptr;
   int* err = nullptr;
+
+  // benchmark timing of one kernel class (dflash_set_kernel_timing)
+  int time_kind = 0;
+  std::vector<hipEvent_t> ev_start, ev_stop;
+  size_t ev_next = 0, ev_count = 0;
 };
 
 namespace {
+
+void free_events(dflash_ctx* c) {
+  for (auto e : c->ev_start) hipEventDestroy(e);
+  for (auto e : c->ev_stop) hipEventDestroy(e);
+  c->ev_start.clear();
+  c->ev_stop.clear();
+  c->ev_next = c->ev_count = 0;
+}
+
+// Brackets one launch of the timed kernel class with an event pair.
+struct TimedLaunch {
+  dflash_ctx* c;
+  hipStream_t s;
+  size_t slot = 0;
+  bool on = false;
+  TimedLaunch(dflash_ctx* ctx, int kind, hipStream_t st) : c(ctx), s(st) {
+    if (c->time_kind == kind && !c->ev_start.empty()) {
+      on = true;
+      slot = c->ev_next;
+      hipEventRecord(c->ev_start[slot], s);
+    }
+  }
+  ~TimedLaunch() {
+    if (!on) return;
+    hipEventRecord(c->ev_stop[slot], s);
+    c->ev_next = (c->ev_next + 1) % c->ev_start.size();
+    if (c->ev_count < c->ev_start.size()) c->ev_count++;
+  }
+};
 
 dflash_status check_config(const dflash_config* c) {
   if (!c) return fail(DFLASH_E_INVALID, "config is NULL");
@@ -119,20 +162,10 @@ dflash_status check_config(const dflash_config* c) {
   if (c->num_target_layers > kMaxASeg)
     return fail(DFLASH_E_UNSUPPORTED, "num_target_layers %d > %d",
                 c->num_target_layers, kMaxASeg);
-  if (c->hidden > 16384)
-    return fail(DFLASH_E_UNSUPPORTED, "hidden %d > 16384", c->hidden);
+  const int max_hidden = c->dtype == DFLASH_F32 ? 4096 : 8192;
+  if (c->hidden > max_hidden)
+    return fail(DFLASH_E_UNSUPPORTED, "hidden %d > %d", c->hidden, max_hidden);
   return DFLASH_OK;
-}
-
-// Largest split-K partial buffer any call can need, over all row counts.
-size_t max_partial(int max_rows, int N, int Kd, bool bf16, int num_cu) {
-  size_t best = 0;
-  for (int m = 16; m < max_rows + 16; m += 16) {
-    const int mm = m > max_rows ? max_rows : m;
-    GemmPlan pl = plan_gemm(mm, N, Kd, bf16, num_cu);
-    if (pl.partial_floats > best) best = pl.partial_floats;
-  }
-  return best;
 }
 
 // Keys per attention workgroup: about 2 workgroups per CU over the batch,
@@ -146,34 +179,43 @@ int attn_chunk(int B, int Hkv, int max_keys, int num_cu) {
   return ch;
 }
 
-dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, GemmPlan& pl,
-                       hipStream_t s) {
-  pl = plan_gemm(a.M, a.N, a.Kd, c->bf16, c->num_cu);
-  if (pl.partial_floats > c->partial_floats)
-    return fail(DFLASH_E_CAPACITY, "split-K workspace too small (%zu > %zu)",
-                pl.partial_floats, c->partial_floats);
-  a.k_split = pl.k_split;
-  a.out = c->partial;
+dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
+                       int kind = DFLASH_TIME_GEMM) {
+  const GemmPlan pl = plan_gemm(a.M, a.N);
+  a.err = c->err;
+  TimedLaunch tl(c, kind, s);
   DF_HIP(launch_gemm(c->bf16, pl, a, s));
   return DFLASH_OK;
 }
 
-GemmArgs make_args(const void* A, int64_t lda, int M, int Kd) {
+// GEMM on a packed activation operand (rows M, contraction Kd).
+GemmArgs packed_args(const void* A, const void* W, int M, int N, int Kd) {
   GemmArgs a{};
   a.a_ptr[0] = A;
-  a.lda = lda;
+  a.a_packed = 1;
   a.a_seg_k = Kd;
+  a.w = W;
   a.M = M;
+  a.N = N;
   a.Kd = Kd;
+  a.cmap = MAP_LINEAR;
   return a;
 }
 
-void add_b(GemmArgs& a, const void* w, int n) {
-  if (a.b_nseg == 0) a.b_n0[0] = 0;
-  a.b_ptr[a.b_nseg] = w;
-  a.b_n0[a.b_nseg + 1] = a.b_n0[a.b_nseg] + n;
-  a.b_nseg++;
-  a.N = a.b_n0[a.b_nseg];
+void set_pairs(GemmArgs& a, int group, int off) {
+  a.cmap = MAP_PAIRS;
+  a.pair_group = group;
+  a.pair_off = off;
+}
+
+void set_cache_geometry(GemmArgs& a, const dflash_ctx* c) {
+  a.Hq = c->cfg.num_q_heads;
+  a.Hkv = c->cfg.num_kv_heads;
+  a.d = c->cfg.head_dim;
+  a.max_batch = c->cfg.max_batch;
+  a.P = c->P;
+  a.max_ctx = c->cfg.max_ctx;
+  a.rope = c->rope;
 }
 
 }  // namespace
@@ -187,6 +229,15 @@ size_t dflash_kv_cache_bytes(const dflash_config* c) {
   const size_t esz = c->dtype == DFLASH_F32 ? 4 : 2;
   return (size_t)c->num_layers * 2 * c->max_batch * c->num_kv_heads *
          (size_t)(c->max_ctx + c->block_size) * c->head_dim * esz;
+}
+
+void dflash_destroy(dflash_ctx* ctx) {
+  if (!ctx) return;
+  hipDeviceSynchronize();
+  free_events(ctx);
+  if (ctx->ws) hipFree(ctx->ws);
+  if (ctx->wpack) hipFree(ctx->wpack);
+  delete ctx;
 }
 
 dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
@@ -234,51 +285,113 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
     return fail(DFLASH_E_DEVICE, "no HIP device available");
   }
   x->embed = w->embed;
-  x->fc = w->fc;
   x->hidden_norm = w->hidden_norm;
   x->final_norm = w->final_norm;
-  x->lm_head = w->lm_head;
-  std::vector<const void*>* dst[] = {&x->attn_norm, &x->wq, &x->wk, &x->wv,
-                                     &x->wo, &x->mlp_norm, &x->w_gate,
-                                     &x->w_up, &x->w_down};
-  for (int i = 0; i < 9; ++i) dst[i]->assign(lists[i], lists[i] + c.num_layers);
+  x->attn_norm.assign(w->attn_norm, w->attn_norm + c.num_layers);
+  x->mlp_norm.assign(w->mlp_norm, w->mlp_norm + c.num_layers);
 
-  // ---- workspace plan ----
-  const int D = c.hidden, K = c.block_size, d = c.head_dim;
+  const int D = c.hidden, K = c.block_size, d = c.head_dim, I = c.intermediate;
   const int qd = c.num_q_heads * d, kvd = c.num_kv_heads * d;
+  const int ntd = c.num_target_layers * c.target_hidden;
+  const int Nl = c.num_layers;
+  const size_t esz = x->esz;
+
+  // ---- packed weights: one allocation, repacked by pack kernels ----
+  struct PItem { void** p; size_t elems; };
+  std::vector<PItem> pit;
+  x->pk_qkv.resize(Nl);
+  x->pk_o.resize(Nl);
+  x->pk_gu.resize(Nl);
+  x->pk_down.resize(Nl);
+  pit.push_back({&x->pk_fc, (size_t)D * ntd});
+  pit.push_back({&x->pk_kv, (size_t)Nl * 2 * kvd * D});
+  pit.push_back({&x->pk_lm, (size_t)c.vocab * D});
+  for (int l = 0; l < Nl; ++l) {
+    pit.push_back({&x->pk_qkv[l], (size_t)(qd + 2 * kvd) * D});
+    pit.push_back({&x->pk_o[l], (size_t)D * qd});
+    pit.push_back({&x->pk_gu[l], (size_t)2 * I * D});
+    pit.push_back({&x->pk_down[l], (size_t)D * I});
+  }
+  size_t ptotal = 0;
+  for (auto& it : pit) ptotal += align_up(it.elems * esz, 256);
+  if (hipMalloc(&x->wpack, ptotal) != hipSuccess) {
+    delete x;
+    return fail(DFLASH_E_DEVICE, "packed-weight allocation of %zu bytes failed",
+                ptotal);
+  }
+  {
+    char* p = static_cast<char*>(x->wpack);
+    for (auto& it : pit) {
+      *it.p = p;
+      p += align_up(it.elems * esz, 256);
+    }
+  }
+  auto pack = [&](std::vector<std::pair<const void*, int>> segs, int Kd,
+                  void* dst, int cmap, int group, int off) -> bool {
+    PackArgs a{};
+    int n = 0;
+    a.n0[0] = 0;
+    for (auto& sg : segs) {
+      a.src[a.nseg] = sg.first;
+      n += sg.second;
+      a.n0[++a.nseg] = n;
+    }
+    a.N = n;
+    a.K = Kd;
+    a.cmap = cmap;
+    a.pair_group = group;
+    a.pair_off = off;
+    a.dst = dst;
+    return launch_pack(x->bf16, a, nullptr) == hipSuccess;
+  };
+  bool ok = pack({{w->fc, D}}, ntd, x->pk_fc, MAP_LINEAR, 0, 0) &&
+            pack({{w->lm_head, c.vocab}}, D, x->pk_lm, MAP_LINEAR, 0, 0);
+  {
+    std::vector<std::pair<const void*, int>> kvsegs;
+    for (int l = 0; l < Nl; ++l) {
+      kvsegs.push_back({w->wk[l], kvd});
+      kvsegs.push_back({w->wv[l], kvd});
+    }
+    ok = ok && pack(kvsegs, D, x->pk_kv, MAP_PAIRS, d, d / 2);
+  }
+  for (int l = 0; l < Nl && ok; ++l) {
+    ok = pack({{w->wq[l], qd}, {w->wk[l], kvd}, {w->wv[l], kvd}}, D,
+              x->pk_qkv[l], MAP_PAIRS, d, d / 2) &&
+         pack({{w->wo[l], D}}, qd, x->pk_o[l], MAP_LINEAR, 0, 0) &&
+         pack({{w->w_gate[l], I}, {w->w_up[l], I}}, D, x->pk_gu[l], MAP_PAIRS,
+              2 * I, I) &&
+         pack({{w->w_down[l], D}}, I, x->pk_down[l], MAP_LINEAR, 0, 0);
+  }
+  if (!ok || hipDeviceSynchronize() != hipSuccess) {
+    dflash_destroy(x);
+    return fail(DFLASH_E_DEVICE, "weight repack failed");
+  }
+
+  // ---- workspace ----
   const int R = c.max_batch * K;
   const int TI = c.max_inject_rows;
-  const bool bf = x->bf16;
-  size_t pf = 0;
-  auto upd = [&](size_t v) { if (v > pf) pf = v; };
-  upd(max_partial(TI, D, c.num_target_layers * c.target_hidden, bf, x->num_cu));
-  upd(max_partial(TI, c.num_layers * 2 * kvd, D, bf, x->num_cu));
-  upd(max_partial(R, qd + 2 * kvd, D, bf, x->num_cu));
-  upd(max_partial(R, D, qd, bf, x->num_cu));
-  upd(max_partial(R, 2 * c.intermediate, D, bf, x->num_cu));
-  upd(max_partial(R, D, c.intermediate, bf, x->num_cu));
-  x->partial_floats = pf;
+  const int TI16 = (TI + 15) / 16 * 16;
   const int G = c.num_q_heads / c.num_kv_heads;
   x->attn_floats = (size_t)G * (2 * x->num_cu + c.max_batch * c.num_kv_heads) * K;
   const int lm_rows = c.max_batch * (K - 1);
-  x->lm_part_count = (size_t)lm_rows * ((c.vocab + 63) / 64);
+  x->lm_part_count = (size_t)lm_rows * (c.vocab / 16);
 
   struct Item { void** p; size_t bytes; };
   std::vector<Item> items = {
       {(void**)&x->rope, (size_t)x->P * (d / 2) * sizeof(float2)},
-      {(void**)&x->partial, pf * sizeof(float)},
+      {(void**)&x->u, (size_t)TI * D * sizeof(float)},
+      {&x->cond, (size_t)TI16 * D * esz},
       {(void**)&x->x, (size_t)R * D * sizeof(float)},
-      {&x->h, (size_t)R * D * x->esz},
-      {&x->qb, (size_t)R * qd * x->esz},
-      {&x->ob, (size_t)R * qd * x->esz},
-      {&x->act, (size_t)R * c.intermediate * x->esz},
-      {&x->hf, (size_t)R * D * x->esz},
-      {&x->hcond, (size_t)TI * D * x->esz},
+      {&x->h, (size_t)R * D * esz},
+      {&x->hf, (size_t)R * D * esz},
+      {&x->qb, (size_t)R * qd * esz},
+      {&x->ob, (size_t)R * qd * esz},
+      {&x->act, (size_t)R * I * esz},
       {(void**)&x->tokens, (size_t)R * sizeof(int32_t)},
       {(void**)&x->committed, (size_t)R * sizeof(int32_t)},
       {(void**)&x->rowmap, (size_t)R * sizeof(int32_t)},
       {(void**)&x->lm_part, x->lm_part_count * sizeof(Top2)},
-      {(void**)&x->rowres, (size_t)lm_rows * sizeof(RowResult)},
+      {(void**)&x->lm_part2, (size_t)lm_rows * kMergeChunks * sizeof(Top2)},
       {(void**)&x->attn_o, x->attn_floats * d * sizeof(float)},
       {(void**)&x->attn_ml, x->attn_floats * 2 * sizeof(float)},
       {(void**)&x->err, 256},
@@ -286,13 +399,15 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
   size_t total = 0;
   for (auto& it : items) total += align_up(it.bytes, 256);
   if (hipMalloc(&x->ws, total) != hipSuccess) {
-    delete x;
+    dflash_destroy(x);
     return fail(DFLASH_E_DEVICE, "workspace allocation of %zu bytes failed", total);
   }
-  char* p = static_cast<char*>(x->ws);
-  for (auto& it : items) {
-    *it.p = p;
-    p += align_up(it.bytes, 256);
+  {
+    char* p = static_cast<char*>(x->ws);
+    for (auto& it : items) {
+      *it.p = p;
+      p += align_up(it.bytes, 256);
+    }
   }
   // RoPE table: angle pos * theta^(-2i/d) evaluated in double precision.
   std::vector<float2> tab((size_t)x->P * (d / 2));
@@ -307,19 +422,55 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
                 hipMemcpyHostToDevice) != hipSuccess ||
       hipMemset(x->err, 0, 256) != hipSuccess ||
       hipMemset(x->committed, 0, (size_t)R * sizeof(int32_t)) != hipSuccess) {
-    hipFree(x->ws);
-    delete x;
+    dflash_destroy(x);
     return fail(DFLASH_E_DEVICE, "workspace initialisation failed");
   }
   *out = x;
   return DFLASH_OK;
 }
 
-void dflash_destroy(dflash_ctx* ctx) {
-  if (!ctx) return;
-  hipDeviceSynchronize();
-  if (ctx->ws) hipFree(ctx->ws);
-  delete ctx;
+dflash_status dflash_set_kernel_timing(dflash_ctx* ctx, int32_t kind) {
+  g_last_error.clear();
+  if (!ctx) return fail(DFLASH_E_INVALID, "ctx is NULL");
+  if (kind < 0 || kind > DFLASH_TIME_GEMM)
+    return fail(DFLASH_E_INVALID, "unknown timing kind %d", kind);
+  DF_HIP(hipDeviceSynchronize());
+  free_events(ctx);
+  ctx->time_kind = kind;
+  if (kind == 0) return DFLASH_OK;
+  ctx->ev_start.resize(kTimingSlots);
+  ctx->ev_stop.resize(kTimingSlots);
+  for (size_t i = 0; i < kTimingSlots; ++i) {
+    if (hipEventCreate(&ctx->ev_start[i]) != hipSuccess ||
+        hipEventCreate(&ctx->ev_stop[i]) != hipSuccess) {
+      ctx->ev_start.resize(i);
+      ctx->ev_stop.resize(i);
+      free_events(ctx);
+      ctx->time_kind = 0;
+      return fail(DFLASH_E_DEVICE, "hipEventCreate failed");
+    }
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_get_kernel_timing(dflash_ctx* ctx, int32_t* launches,
+                                       double* total_ms) {
+  g_last_error.clear();
+  if (!ctx || !launches || !total_ms)
+    return fail(DFLASH_E_INVALID, "NULL argument");
+  double tot = 0.0;
+  const size_t n = ctx->ev_count, cap = ctx->ev_start.size();
+  for (size_t k = 0; k < n; ++k) {
+    const size_t i = (ctx->ev_next + cap - n + k) % cap;
+    DF_HIP(hipEventSynchronize(ctx->ev_stop[i]));
+    float ms = 0.f;
+    DF_HIP(hipEventElapsedTime(&ms, ctx->ev_start[i], ctx->ev_stop[i]));
+    tot += ms;
+  }
+  *launches = (int32_t)n;
+  *total_ms = tot;
+  ctx->ev_count = 0;
+  return DFLASH_OK;
 }
 
 dflash_status dflash_check_device_errors(dflash_ctx* ctx, void* stream,
@@ -366,34 +517,38 @@ dflash_status dflash_inject_kv(dflash_ctx* ctx, void* stream,
     return fail(DFLASH_E_INVALID, "kv_cache not 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int D = c.hidden, d = c.head_dim, kvd = c.num_kv_heads * d;
+  const int ntd = c.num_target_layers * c.target_hidden;
 
-  // fused features: fc over the concatenated target layers, then RMSNorm
+  // fused features: u = fc . concat(target layers), A read row-major from
+  // the caller's hidden states
   GemmArgs a{};
   for (int k = 0; k < c.num_target_layers; ++k) a.a_ptr[k] = target_hidden[k];
   a.lda = ld;
   a.a_seg_k = c.target_hidden;
+  a.a_packed = 0;
+  a.w = ctx->pk_fc;
   a.M = T;
-  a.Kd = c.num_target_layers * c.target_hidden;
-  add_b(a, ctx->fc, D);
-  GemmPlan pl;
-  dflash_status st = run_gemm(ctx, a, pl, s);
+  a.N = D;
+  a.Kd = ntd;
+  a.cmap = MAP_LINEAR;
+  a.ep = EP_STORE;
+  a.out_f32 = ctx->u;
+  a.ldo = D;
+  dflash_status st = run_gemm(ctx, a, s);
   if (st != DFLASH_OK) return st;
-  DF_HIP(launch_rows_rmsnorm(ctx->bf16, T, D, pl.gz, ctx->partial,
-                             ctx->hidden_norm, c.rms_eps, ctx->hcond, s));
-
-  // every layer's K and V projection in one pass over H_cond
-  GemmArgs b = make_args(ctx->hcond, D, T, D);
-  for (int l = 0; l < c.num_layers; ++l) {
-    add_b(b, ctx->wk[l], kvd);
-    add_b(b, ctx->wv[l], kvd);
-  }
-  st = run_gemm(ctx, b, pl, s);
-  if (st != DFLASH_OK) return st;
-  DF_HIP(launch_kv_inject_epilogue(ctx->bf16, T, c.num_layers,
-                                   c.num_kv_heads, d, pl.gz, ctx->partial,
-                                   row_seq, row_pos, ctx->rope, c.max_batch,
-                                   c.max_ctx, ctx->P, kv_cache, ctx->err, s));
-  return DFLASH_OK;
+  // H_cond = RMSNorm(u) * g
+  DF_HIP(launch_rmsnorm(ctx->bf16, T, D, ctx->u, nullptr, ctx->hidden_norm,
+                        c.rms_eps, ctx->cond, s));
+  // every layer's K and V projection of H_cond in one pass; RoPE on K;
+  // scatter into the cache
+  GemmArgs b = packed_args(ctx->cond, ctx->pk_kv, T, c.num_layers * 2 * kvd, D);
+  set_pairs(b, d, d / 2);
+  set_cache_geometry(b, ctx);
+  b.ep = EP_KV;
+  b.kv = kv_cache;
+  b.row_seq = row_seq;
+  b.row_pos = row_pos;
+  return run_gemm(ctx, b, s);
 }
 
 dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
@@ -460,61 +615,75 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
     const int n_cap = (K - 1) - pass * commit_per_pass;
     const bool last = pass == num_passes - 1;
     DF_HIP(launch_embed(bf, batch, K, D, V, c.mask_token_id, pass, n_cap,
-                        anchor, block_tokens, bs, ctx->embed, ctx->attn_norm[0],
-                        c.rms_eps, ctx->x, ctx->h, ctx->hf, draft_tokens, s));
+                        anchor, block_tokens, bs, ctx->embed, ctx->x,
+                        draft_tokens, s));
     for (int l = 0; l < c.num_layers; ++l) {
       char* kvl = static_cast<char*>(kv_cache) + l * layer_elems * ctx->esz;
-      GemmPlan pl;
-      // q, k, v projection + RoPE; block k, v go to cache positions L_b + i
-      GemmArgs a = make_args(ctx->h, D, R, D);
-      add_b(a, ctx->wq[l], qd);
-      add_b(a, ctx->wk[l], kvd);
-      add_b(a, ctx->wv[l], kvd);
-      dflash_status st = run_gemm(ctx, a, pl, s);
+      // q, k, v of RMSNorm(x); RoPE; q -> q buffer, block k, v -> cache
+      // positions L_b + i
+      DF_HIP(launch_rmsnorm(bf, R, D, ctx->x, nullptr, ctx->attn_norm[l],
+                            c.rms_eps, ctx->h, s));
+      GemmArgs a = packed_args(ctx->h, ctx->pk_qkv[l], R, qd + 2 * kvd, D);
+      set_pairs(a, d, d / 2);
+      set_cache_geometry(a, ctx);
+      a.ep = EP_QKV;
+      a.out_t = ctx->qb;
+      a.kv = kvl;
+      a.ctx_len = ctx_len;
+      a.max_len = max_ctx_len;
+      a.K = K;
+      dflash_status st = run_gemm(ctx, a, s);
       if (st != DFLASH_OK) return st;
-      DF_HIP(launch_qkv_epilogue(bf, batch, K, Hq, Hkv, d, pl.gz, ctx->partial,
-                                 ctx_len, max_ctx_len, ctx->rope, ctx->P,
-                                 c.max_batch, ctx->qb, kvl, ctx->err, s));
       at.kc = kvl;
       at.vc = kvl + (size_t)c.max_batch * Hkv * ctx->P * d * ctx->esz;
-      DF_HIP(launch_attention(bf, d, batch, at, s));
-      // output projection, residual, norm for the MLP
-      GemmArgs o = make_args(ctx->ob, qd, R, qd);
-      add_b(o, ctx->wo[l], D);
-      st = run_gemm(ctx, o, pl, s);
+      {
+        TimedLaunch tl(ctx, DFLASH_TIME_ATTENTION, s);
+        DF_HIP(launch_attention(bf, d, batch, at, s));
+      }
+      // x += o . Wo^T
+      GemmArgs o = packed_args(ctx->ob, ctx->pk_o[l], R, D, qd);
+      o.ep = EP_RESID;
+      o.out_f32 = ctx->x;
+      o.ldo = D;
+      st = run_gemm(ctx, o, s);
       if (st != DFLASH_OK) return st;
-      DF_HIP(launch_resid_norm(bf, R, K, D, pl.gz, ctx->partial, ctx->x,
-                               ctx->mlp_norm[l], c.rms_eps, ctx->h, false, 0,
-                               bs, s));
-      // SwiGLU MLP
-      GemmArgs gu = make_args(ctx->h, D, R, D);
-      add_b(gu, ctx->w_gate[l], I);
-      add_b(gu, ctx->w_up[l], I);
-      st = run_gemm(ctx, gu, pl, s);
+      // act = silu(h Wg^T) * (h Wu^T), h = RMSNorm(x)
+      DF_HIP(launch_rmsnorm(bf, R, D, ctx->x, nullptr, ctx->mlp_norm[l],
+                            c.rms_eps, ctx->h, s));
+      GemmArgs gu = packed_args(ctx->h, ctx->pk_gu[l], R, 2 * I, D);
+      set_pairs(gu, 2 * I, I);
+      gu.ep = EP_SWIGLU;
+      gu.out_t = ctx->act;
+      st = run_gemm(ctx, gu, s);
       if (st != DFLASH_OK) return st;
-      DF_HIP(launch_swiglu(bf, R, I, pl.gz, ctx->partial, ctx->act, s));
-      GemmArgs dn = make_args(ctx->act, I, R, I);
-      add_b(dn, ctx->w_down[l], D);
-      st = run_gemm(ctx, dn, pl, s);
+      // x += act . Wd^T
+      GemmArgs dn = packed_args(ctx->act, ctx->pk_down[l], R, D, I);
+      dn.ep = EP_RESID;
+      dn.out_f32 = ctx->x;
+      dn.ldo = D;
+      st = run_gemm(ctx, dn, s);
       if (st != DFLASH_OK) return st;
-      const bool fin = l == c.num_layers - 1;
-      DF_HIP(launch_resid_norm(bf, R, K, D, pl.gz, ctx->partial, ctx->x,
-                               fin ? ctx->final_norm : ctx->attn_norm[l + 1],
-                               c.rms_eps, fin ? ctx->hf : ctx->h, fin, n_cap,
-                               bs, s));
     }
-    // LM head over the still-masked rows, fused argmax / top-2 / LSE
+    // final norm of the still-masked rows (compacted), then the LM head with
+    // the fused argmax / top-2 / log-sum-exp per 16-column vocabulary tile
     const int Mh = batch * n_cap;
-    GemmArgs hd = make_args(ctx->hf, D, Mh, D);
-    add_b(hd, ctx->lm_head, V);
-    GemmPlan hp = plan_lmhead(Mh, V, D, bf);
-    float* dbg = logits_debug
-                     ? logits_debug + (size_t)pass * batch * (K - 1) * V
-                     : nullptr;
-    DF_HIP(launch_lmhead(bf, hp, hd, ctx->lm_part, dbg, ctx->rowmap, V, s));
-    DF_HIP(launch_lm_merge(Mh, hp.gx, ctx->lm_part, ctx->rowres, s));
-    DF_HIP(launch_commit(batch, K, n_cap, commit_per_pass, last, ctx->rowres,
-                         bs, draft_tokens, confidence, top2_margin, s));
+    DF_HIP(launch_rmsnorm(bf, Mh, D, ctx->x, ctx->rowmap, ctx->final_norm,
+                          c.rms_eps, ctx->hf, s));
+    GemmArgs hd = packed_args(ctx->hf, ctx->pk_lm, Mh, V, D);
+    hd.ep = EP_TOP2;
+    hd.top2 = ctx->lm_part;
+    hd.rowmap = ctx->rowmap;
+    hd.K = K;
+    hd.logits = logits_debug
+                    ? logits_debug + (size_t)pass * batch * (K - 1) * V
+                    : nullptr;
+    hd.logits_ld = V;
+    dflash_status st = run_gemm(ctx, hd, s, DFLASH_TIME_LMHEAD);
+    if (st != DFLASH_OK) return st;
+    DF_HIP(launch_lm_merge(Mh, V / 16, ctx->lm_part, ctx->lm_part2, s));
+    DF_HIP(launch_commit(batch, K, n_cap, commit_per_pass, last,
+                         ctx->lm_part2, bs, draft_tokens, confidence,
+                         top2_margin, s));
   }
   return DFLASH_OK;
 }

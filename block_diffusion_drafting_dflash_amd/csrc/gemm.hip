@@ -1,244 +1,305 @@
-// Skinny MFMA GEMMs for the drafter's projections and its LM head.
+// MFMA GEMMs of the drafter (projections and LM head) on packed operands.
 //
-// The drafter multiplies 16 * batch block rows (or the injected context rows)
-// by weight matrices stored [out, in].  At batch 1 the job is streaming each
-// weight byte from HBM exactly once, so a workgroup owns 64 output columns
-// (four 16-column MFMA tiles) and its four waves split the contraction,
-// interleaved by 32-element steps so that together they read each weight
-// row contiguously.  The waves' partial tiles are summed through LDS in a
-// fixed order; a grid-z split of the contraction adds workgroups when the
-// output is narrow, and the epilogue kernels sum those slices in order.
-//
-// Fragment layout (both operands K-contiguous in memory): lane l loads 16
-// bytes of row / column l % 16 at contraction offset (l / 16) * E within the
-// current step, which is the same slot on both operands, so any intra-
-// instruction contraction order of the MFMA gives the same sum.
+// At batch 1 the job is streaming each weight byte from HBM exactly once.
+// Weights are packed once into fragment-major order (see kernels.h), so each
+// wave-wide weight load is one contiguous 1 KiB burst; the activation rows are
+// written packed by the kernels that produce them, so their loads are
+// contiguous too.  A workgroup owns one 16-column output tile over the whole
+// contraction: its waves take interleaved fragment steps, keep several steps
+// of loads in flight, and sum their tiles through LDS in wave order.  The
+// finished tile is handled by the same workgroup (residual add, RoPE and the
+// KV-cache scatter, SwiGLU, the LM-head top-2 reduction), so no workgroup
+// ever waits on another.
+#include "../../include/dflash.h"
 #include "kernels.h"
 
 namespace dflash {
 
 namespace {
 
-template <typename T, int MT, int NT>
-__device__ __forceinline__ void gemm_core(const GemmArgs& p, int n_base,
-                                          int m_base, int k_lo, int k_hi,
-                                          f32x4 (&acc)[MT][NT]) {
-  constexpr int E = Storage<T>::E, KC = Storage<T>::KC;
-  constexpr int STEP = 4 * KC;  // the four waves interleave by KC
+__device__ __forceinline__ void rope_pair(float a, float b, float2 cs,
+                                          float& ra, float& rb) {
+  ra = a * cs.x - b * cs.y;
+  rb = b * cs.x + a * cs.y;
+}
+
+template <int MT>
+constexpr int waves_for() {
+  return MT == 1 ? 8 : (MT == 2 ? 4 : 2);
+}
+
+// acc[m] over this wave's share of the contraction.
+template <typename T, int MT, int AP>
+__device__ __forceinline__ void gemm_core(const GemmArgs& p, int tile,
+                                          int m_base, f32x4 (&acc)[MT]) {
+  constexpr int E = Storage<T>::E, KC = Storage<T>::KC, SZ = sizeof(T);
+  constexpr int W = waves_for<MT>();
+  constexpr int U = 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-
-  const char* bptr[NT];
+  const int nsteps = p.Kd / KC;
+  const char* wbase =
+      static_cast<const char*>(p.w) + ((int64_t)tile * nsteps * 64 + lane) * 16;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int n = min(n_base + 16 * t + r, p.N - 1);
-    int s = 0;
-    while (s + 1 < p.b_nseg && n >= p.b_n0[s + 1]) ++s;
-    bptr[t] = static_cast<const char*>(p.b_ptr[s]) +
-              ((int64_t)(n - p.b_n0[s]) * p.Kd + g * E) * (int64_t)sizeof(T);
-  }
+  for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // A operand addressing: packed fragments, or row-major segments
+  const int sps = AP ? nsteps : p.a_seg_k / KC;  // steps per segment
+  const int nseg = AP ? 1 : (nsteps + sps - 1) / sps;
   int64_t aoff[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int row = min(m_base + 16 * m + r, p.M - 1);
-    aoff[m] = ((int64_t)row * p.lda + g * E) * (int64_t)sizeof(T);
-  }
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int seg = k_lo / p.a_seg_k; seg * p.a_seg_k < k_hi; ++seg) {
-    const int s0 = seg * p.a_seg_k;
-    const int ks = max(k_lo, s0), ke = min(k_hi, s0 + p.a_seg_k);
-    const char* abase = static_cast<const char*>(p.a_ptr[seg]) -
-                        (int64_t)s0 * (int64_t)sizeof(T);
-    int kc = ks + wave * KC;
-    constexpr int U = 4;
-    for (; kc + (U - 1) * STEP < ke; kc += U * STEP) {
-      u32x4 bf[U][NT], af[U][MT];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          bf[u][t] = load16(bptr[t] + (int64_t)(kc + u * STEP) * sizeof(T));
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-          af[u][m] = load16(abase + aoff[m] +
-                            (int64_t)(kc + u * STEP) * sizeof(T));
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int t = 0; t < NT; ++t) mma16(acc[m][t], af[u][m], bf[u][t], T());
+    if (AP) {
+      const int mt = min(m_base / 16 + m, (p.M + 15) / 16 - 1);
+      aoff[m] = ((int64_t)mt * nsteps * 64 + lane) * 16;
+    } else {
+      const int row = min(m_base + 16 * m + r, p.M - 1);
+      aoff[m] = ((int64_t)row * p.lda + g * E) * SZ;
     }
-    for (; kc < ke; kc += STEP) {
-      u32x4 bf[NT], af[MT];
+  }
+  for (int seg = 0; seg < nseg; ++seg) {
+    const int s0 = seg * sps, s1 = min(nsteps, s0 + sps);
+    const char* abase = static_cast<const char*>(p.a_ptr[seg]);
+    // A fragment of step s within this segment
+    auto a_at = [&](int m, int s) -> const char* {
+      return AP ? abase + aoff[m] + (int64_t)s * 1024
+                : abase + aoff[m] + (int64_t)(s - s0) * KC * SZ;
+    };
+    int s = s0 + ((wave - s0) % W + W) % W;
+    for (; s + (U - 1) * W < s1; s += U * W) {
+      u32x4 bf[U], af[U][MT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        bf[t] = load16(bptr[t] + (int64_t)kc * sizeof(T));
+      for (int u = 0; u < U; ++u)
+        bf[u] = load16(wbase + (int64_t)(s + u * W) * 1024);
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        af[m] = load16(abase + aoff[m] + (int64_t)kc * sizeof(T));
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; ++m) af[u][m] = load16(a_at(m, s + u * W));
 #pragma unroll
-        for (int t = 0; t < NT; ++t) mma16(acc[m][t], af[m], bf[t], T());
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) mma16(acc[m], af[u][m], bf[u], T());
+    }
+    for (; s < s1; s += W) {
+      const u32x4 bf = load16(wbase + (int64_t)s * 1024);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) mma16(acc[m], load16(a_at(m, s)), bf, T());
     }
   }
 }
 
-// Each wave parks its tile in LDS: red[wave][(m*NT + t)*4 + j][lane].
-template <int MT, int NT>
-__device__ __forceinline__ void park(const f32x4 (&acc)[MT][NT], float* red) {
+// Sums the waves' tiles in wave order; red[(m*4 + j)*64 + lane] then holds
+// row 16m + 4(lane/16) + j, tile column lane % 16.
+template <int MT, int W>
+__device__ __forceinline__ void reduce_waves(const f32x4 (&acc)[MT],
+                                             float* red) {
+  constexpr int S = MT * 256;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int j = 0; j < 4; ++j)
+      red[(wave * MT + m) * 256 + j * 64 + lane] = acc[m][j];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < S; idx += W * 64) {
+    float v = red[idx];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        red[((wave * MT * NT + m * NT + t) * 4 + j) * 64 + lane] = acc[m][t][j];
+    for (int w = 1; w < W; ++w) v += red[w * S + idx];
+    red[idx] = v;
+  }
   __syncthreads();
 }
 
-template <typename T, int MT, int NT>
-__global__ __launch_bounds__(256) void gemm_partial_kernel(GemmArgs p) {
-  __shared__ float red[4 * MT * NT * 4 * 64];
-  const int n_base = blockIdx.x * 16 * NT, m_base = blockIdx.y * 16 * MT;
-  const int k_lo = blockIdx.z * p.k_split;
-  const int k_hi = min(p.Kd, k_lo + p.k_split);
-  f32x4 acc[MT][NT];
-  gemm_core<T, MT, NT>(p, n_base, m_base, k_lo, k_hi, acc);
-  park<MT, NT>(acc, red);
-  constexpr int S = MT * NT * 4 * 64;
-  float* out = p.out + (int64_t)blockIdx.z * p.M * p.N;
-  for (int idx = threadIdx.x; idx < S; idx += 256) {
-    const float v = red[idx] + red[S + idx] + red[2 * S + idx] + red[3 * S + idx];
-    const int e = idx >> 6, ln = idx & 63;
-    const int j = e & 3, mt = (e >> 2) / NT, t = (e >> 2) % NT;
-    const int row = m_base + 16 * mt + 4 * (ln >> 4) + j;
-    const int col = n_base + 16 * t + (ln & 15);
-    if (row < p.M && col < p.N) out[(int64_t)row * p.N + col] = v;
-  }
-}
-
-// LM head: z = A . W^T for a 64-column vocabulary tile, reduced per row to
-// (max, argmax, 2nd max, sum exp(z - max)) without writing logits (unless a
-// debug buffer is given).
-template <typename T, int MT>
-__global__ __launch_bounds__(256) void lmhead_kernel(GemmArgs p, Top2* part,
-                                                     float* logits,
-                                                     const int* rowmap,
-                                                     int64_t logits_ld) {
-  constexpr int NT = 4;
-  __shared__ float red[4 * MT * NT * 4 * 64];
-  const int n_base = blockIdx.x * 64, m_base = blockIdx.y * 16 * MT;
-  f32x4 acc[MT][NT];
-  gemm_core<T, MT, NT>(p, n_base, m_base, 0, p.Kd, acc);
-  park<MT, NT>(acc, red);
-  constexpr int S = MT * NT * 4 * 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = n_base + lane;
-  const int t = lane >> 4;
-  for (int rr = wave; rr < 16 * MT; rr += 4) {
-    const int row = m_base + rr;
-    if (row >= p.M) break;
-    const int mt = rr >> 4, j = rr & 3;
-    const int ln = ((rr & 15) >> 2) * 16 + (lane & 15);
-    const int idx = ((mt * NT + t) * 4 + j) * 64 + ln;
-    const float z = red[idx] + red[S + idx] + red[2 * S + idx] + red[3 * S + idx];
-    Top2 v = top2_empty();
-    if (col < p.N) {
-      v.m1 = z;
-      v.i1 = col;
-      v.s = 1.f;
-      if (logits != nullptr) {
-        const int dst = rowmap[row];
-        if (dst >= 0) logits[(int64_t)dst * logits_ld + col] = z;
-      }
+template <typename T, int MT, int W>
+__device__ void apply_epilogue(const GemmArgs& p, int tile, int m_base,
+                               const float* red) {
+  constexpr int S = MT * 256;
+  const int tid = threadIdx.x;
+  auto row_of = [&](int idx) {
+    return m_base + 16 * (idx >> 8) + 4 * ((idx & 63) >> 4) + ((idx >> 6) & 3);
+  };
+  if (p.ep == EP_STORE || p.ep == EP_RESID) {
+    for (int idx = tid; idx < S; idx += W * 64) {
+      const int row = row_of(idx);
+      if (row >= p.M) continue;
+      const int col = map_col(p.cmap, p.pair_group, p.pair_off, tile, idx & 15);
+      float* o = p.out_f32 + (int64_t)row * p.ldo + col;
+      *o = p.ep == EP_RESID ? *o + red[idx] : red[idx];
     }
-    v = top2_wave(v);
-    if (lane == 0) part[(int64_t)row * gridDim.x + blockIdx.x] = v;
+    return;
+  }
+  if (p.ep == EP_TOP2) {
+    // one thread per (row, column); the 16 columns of a row are 16
+    // consecutive lanes of one wave
+    for (int base = 0; base < S; base += W * 64) {
+      const int idx = base + tid;
+      const int row = row_of(idx);
+      const int col = tile * 16 + (idx & 15);
+      Top2 v = top2_empty();
+      if (idx < S && row < p.M && col < p.N) {
+        const float z = red[idx];
+        v.m1 = z;
+        v.i1 = col;
+        v.s = 1.f;
+        if (p.logits != nullptr) {
+          const int br = p.rowmap[row];
+          if (br >= 0)
+            p.logits[((int64_t)(br / p.K) * (p.K - 1) + (br % p.K) - 1) *
+                         p.logits_ld + col] = z;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) v = top2_merge(v, top2_shfl_xor(v, o));
+      if (idx < S && (idx & 15) == 0 && row < p.M)
+        p.top2[(int64_t)row * (p.N / 16) + tile] = v;
+    }
+    return;
+  }
+  // pair epilogues: tile column c < 8 with its partner c + 8
+  const int half = p.d / 2;
+  for (int q = tid; q < MT * 128; q += W * 64) {
+    const int c = q & 7, rg = (q >> 3) & 3, j = (q >> 5) & 3, m = q >> 7;
+    const int idx = (m * 4 + j) * 64 + rg * 16 + c;
+    const float a = red[idx], b = red[idx + 8];
+    const int row = m_base + 16 * m + 4 * rg + j;
+    if (row >= p.M) continue;
+    const int col = map_col(p.cmap, p.pair_group, p.pair_off, tile, c);
+    if (p.ep == EP_SWIGLU) {
+      T* act = static_cast<T*>(p.out_t);
+      const int64_t off = packed_offset<T>(row, col, p.pair_off) / sizeof(T);
+      store_elem(act, off, a / (1.f + __expf(-a)) * b);
+      continue;
+    }
+    const int head = col / p.d, i = col % p.d;  // i < d/2
+    if (p.ep == EP_QKV) {
+      const int bs = row / p.K;
+      int L = p.ctx_len[bs];
+      if (L < 0 || L > p.max_len) {
+        set_error(p.err, DFLASH_DEVERR_CTX_LEN);
+        L = min(max(L, 0), p.max_len);
+      }
+      const int pos = L + row % p.K;
+      const float2 cs = p.rope[(int64_t)pos * half + i];
+      float ra, rb;
+      T* dst;
+      if (head < p.Hq) {
+        dst = static_cast<T*>(p.out_t) + (int64_t)row * p.Hq * p.d + head * p.d;
+        rope_pair(a, b, cs, ra, rb);
+      } else {
+        const bool is_k = head < p.Hq + p.Hkv;
+        const int h = is_k ? head - p.Hq : head - p.Hq - p.Hkv;
+        dst = static_cast<T*>(p.kv) +
+              (is_k ? 0 : (int64_t)p.max_batch * p.Hkv * p.P * p.d) +
+              (((int64_t)bs * p.Hkv + h) * p.P + pos) * p.d;
+        if (is_k) {
+          rope_pair(a, b, cs, ra, rb);
+        } else {
+          ra = a;
+          rb = b;
+        }
+      }
+      store_elem(dst, i, ra);
+      store_elem(dst, i + half, rb);
+    } else {  // EP_KV: injected context rows
+      const int seq = p.row_seq[row], pos = p.row_pos[row];
+      if (seq < 0 || seq >= p.max_batch) {
+        set_error(p.err, DFLASH_DEVERR_SLOT);
+        continue;
+      }
+      if (pos < 0 || pos >= p.max_ctx) {
+        set_error(p.err, DFLASH_DEVERR_POS);
+        continue;
+      }
+      const int l = head / (2 * p.Hkv), w = head % (2 * p.Hkv);
+      const bool is_k = w < p.Hkv;
+      const int h = is_k ? w : w - p.Hkv;
+      const int64_t plane = (int64_t)p.max_batch * p.Hkv * p.P * p.d;
+      T* dst = static_cast<T*>(p.kv) + (2 * l + (is_k ? 0 : 1)) * plane +
+               (((int64_t)seq * p.Hkv + h) * p.P + pos) * p.d;
+      float ra = a, rb = b;
+      if (is_k) rope_pair(a, b, p.rope[(int64_t)pos * half + i], ra, rb);
+      store_elem(dst, i, ra);
+      store_elem(dst, i + half, rb);
+    }
   }
 }
 
+template <typename T, int MT, int AP>
+__global__ __launch_bounds__(64 * waves_for<MT>()) void gemm_kernel(GemmArgs p) {
+  constexpr int W = waves_for<MT>();
+  __shared__ float red[W * MT * 256];
+  const int tile = blockIdx.x, m_base = blockIdx.y * 16 * MT;
+  f32x4 acc[MT];
+  gemm_core<T, MT, AP>(p, tile, m_base, acc);
+  reduce_waves<MT, W>(acc, red);
+  apply_epilogue<T, MT, W>(p, tile, m_base, red);
+}
+
+// One 16-byte chunk of the packed matrix per thread.
 template <typename T>
+__global__ void pack_kernel(PackArgs a) {
+  constexpr int E = Storage<T>::E, KC = Storage<T>::KC;
+  const int nsteps = a.K / KC;
+  const int64_t total = (int64_t)a.N / 16 * nsteps * 64;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(q & 63);
+    const int64_t ts = q >> 6;
+    const int s = (int)(ts % nsteps), t = (int)(ts / nsteps);
+    const int row = map_col(a.cmap, a.pair_group, a.pair_off, t, l & 15);
+    int sg = 0;
+    while (sg + 1 < a.nseg && row >= a.n0[sg + 1]) ++sg;
+    const char* src = static_cast<const char*>(a.src[sg]) +
+                      ((int64_t)(row - a.n0[sg]) * a.K + s * KC + (l >> 4) * E) *
+                          (int64_t)sizeof(T);
+    *reinterpret_cast<u32x4*>(static_cast<char*>(a.dst) + q * 16) = load16(src);
+  }
+}
+
+template <typename T, int AP>
 hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream_t s) {
-  dim3 grid(pl.gx, pl.gy, pl.gz), block(256);
+  dim3 grid(pl.gx, pl.gy, 1), block(pl.waves * 64);
   switch (pl.MT) {
-    case 1: hipLaunchKernelGGL((gemm_partial_kernel<T, 1, kGemmNT>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_partial_kernel<T, 2, kGemmNT>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_partial_kernel<T, 4, kGemmNT>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gemm_kernel<T, 1, AP>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_kernel<T, 2, AP>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_kernel<T, 4, AP>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
-
-template <typename T>
-hipError_t launch_lmhead_t(const GemmPlan& pl, const GemmArgs& a, Top2* part,
-                           float* logits, const int* rowmap, int64_t ld,
-                           hipStream_t s) {
-  dim3 grid(pl.gx, pl.gy, 1), block(256);
-  switch (pl.MT) {
-    case 1: hipLaunchKernelGGL((lmhead_kernel<T, 1>), grid, block, 0, s, a, part, logits, rowmap, ld); break;
-    case 2: hipLaunchKernelGGL((lmhead_kernel<T, 2>), grid, block, 0, s, a, part, logits, rowmap, ld); break;
-    case 4: hipLaunchKernelGGL((lmhead_kernel<T, 4>), grid, block, 0, s, a, part, logits, rowmap, ld); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-int pick_mt(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
 }  // namespace
 
-GemmPlan plan_gemm(int M, int N, int Kd, bool bf16, int num_cu) {
-  const int KC = bf16 ? Storage<bf16_t>::KC : Storage<float>::KC;
+GemmPlan plan_gemm(int M, int N) {
   GemmPlan pl;
-  pl.MT = pick_mt(M);
-  pl.gx = (N + 16 * kGemmNT - 1) / (16 * kGemmNT);
+  pl.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  pl.waves = pl.MT == 1 ? 8 : (pl.MT == 2 ? 4 : 2);
+  pl.gx = N / 16;
   pl.gy = (M + 16 * pl.MT - 1) / (16 * pl.MT);
-  const int chunks = Kd / KC;
-  const int base = pl.gx * pl.gy;
-  const int target = 4 * num_cu;
-  // at least four steps per wave in every slice
-  const int max_split = chunks / 16 > 1 ? chunks / 16 : 1;
-  int gz = (target + base - 1) / base;
-  if (gz > max_split) gz = max_split;
-  if (gz < 1) gz = 1;
-  const int per = (chunks + gz - 1) / gz;
-  pl.k_split = per * KC;
-  pl.gz = (Kd + pl.k_split - 1) / pl.k_split;
-  pl.partial_floats = (size_t)pl.gz * M * N;
-  return pl;
-}
-
-GemmPlan plan_lmhead(int M, int N, int Kd, bool bf16) {
-  GemmPlan pl;
-  pl.MT = pick_mt(M);
-  pl.gx = (N + 63) / 64;
-  pl.gy = (M + 16 * pl.MT - 1) / (16 * pl.MT);
-  pl.gz = 1;
-  pl.k_split = Kd;
-  pl.partial_floats = 0;
-  (void)bf16;
   return pl;
 }
 
 hipError_t launch_gemm(bool bf16, const GemmPlan& pl, const GemmArgs& a,
                        hipStream_t s) {
-  return bf16 ? launch_gemm_t<bf16_t>(pl, a, s) : launch_gemm_t<float>(pl, a, s);
+  if (bf16)
+    return a.a_packed ? launch_gemm_t<bf16_t, 1>(pl, a, s)
+                      : launch_gemm_t<bf16_t, 0>(pl, a, s);
+  return a.a_packed ? launch_gemm_t<float, 1>(pl, a, s)
+                    : launch_gemm_t<float, 0>(pl, a, s);
 }
 
-hipError_t launch_lmhead(bool bf16, const GemmPlan& pl, const GemmArgs& a,
-                         Top2* part, float* logits, const int* rowmap,
-                         int64_t logits_ld, hipStream_t s) {
-  return bf16 ? launch_lmhead_t<bf16_t>(pl, a, part, logits, rowmap, logits_ld, s)
-              : launch_lmhead_t<float>(pl, a, part, logits, rowmap, logits_ld, s);
+hipError_t launch_pack(bool bf16, const PackArgs& a, hipStream_t s) {
+  const int E = bf16 ? Storage<bf16_t>::E : Storage<float>::E;
+  const int64_t chunks = (int64_t)a.N * a.K / E;
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (bf16)
+    hipLaunchKernelGGL(pack_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL(pack_kernel<float>, dim3((unsigned)blocks), dim3(256), 0,
+                       s, a);
+  return hipGetLastError();
 }
 
 }  // namespace dflash

@@ -11,88 +11,127 @@ namespace dflash {
 constexpr int kMaxASeg = 8;
 constexpr int kMaxBSeg = 16;
 
-// C[M, N] = A[M, Kd] . B[N, Kd]^T, one grid-z slice of the contraction per
-// partial.  A is split along the contraction into segments of a_seg_k
-// elements (the concatenated target layers); B is split along N into
-// segments with separate base pointers (e.g. Wq | Wk | Wv).
+// ---------------------------------------------------------------------------
+// Fragment-major ("packed") operands.
+//
+// An MFMA fragment is 16 rows x KC contraction elements, 16 bytes per lane:
+// lane l holds row l % 16, elements [(l / 16) * E, +E) of the step.  A packed
+// matrix with R rows (R % 16 == 0) and contraction K stores fragment
+// (row tile t, step s) as 1 KiB at byte ((t * (K / KC) + s) * 64 + l) * 16, so
+// every wave-wide operand load is one contiguous 1 KiB.  Weights are packed
+// once at create time, activations are written packed by the kernel that
+// produces them.
+// ---------------------------------------------------------------------------
+template <typename T>
+__host__ __device__ __forceinline__ int64_t packed_offset(int row, int k,
+                                                          int K) {
+  constexpr int E = Storage<T>::E, KC = Storage<T>::KC;
+  const int t = row >> 4, r = row & 15, s = k / KC, g = (k % KC) / E;
+  return ((((int64_t)t * (K / KC) + s) * 64 + g * 16 + r) * 16) +
+         (int64_t)(k % E) * (int64_t)sizeof(T);
+}
+
+// Column order inside packed weight tiles.
+enum ColMap : int {
+  MAP_LINEAR = 0,  // tile t = output columns [16t, 16t + 16)
+  MAP_PAIRS = 1,   // tile t = 8 "low" columns (lanes 0-7) and their partners
+                   // at +pair_off (lanes 8-15); low column i is
+                   // (i / pair_off) * pair_group + i % pair_off
+};
+
+__host__ __device__ __forceinline__ int map_col(int cmap, int pair_group,
+                                                int pair_off, int tile,
+                                                int lane16) {
+  if (cmap == MAP_LINEAR) return tile * 16 + lane16;
+  const int i = tile * 8 + (lane16 & 7);
+  const int low = (i / pair_off) * pair_group + i % pair_off;
+  return lane16 < 8 ? low : low + pair_off;
+}
+
+// What a workgroup does with its finished 16-column output tile.
+enum Epilogue : int {
+  EP_STORE = 0,   // out_f32 = sum (row-major)
+  EP_RESID = 1,   // out_f32 += sum (the residual stream)
+  EP_QKV = 2,     // q -> RoPE -> q buffer; block k -> RoPE, v -> layer cache
+  EP_KV = 3,      // injected rows: k -> RoPE, v -> cache of every layer
+  EP_SWIGLU = 4,  // out_t (packed, contraction I) = silu(gate) * up
+  EP_TOP2 = 5,    // LM head: per row (max, argmax, 2nd max, sum exp)
+};
+
+// C[M, N] = A[M, Kd] . W[N, Kd]^T.  W is packed; A is packed (a_packed) or
+// row-major with up to kMaxASeg segments along the contraction (the
+// concatenated target layers).  A workgroup owns one 16-column tile and 16*MT
+// rows over the whole contraction, which its waves split.
 struct GemmArgs {
   const void* a_ptr[kMaxASeg];
-  int64_t lda;       // row stride of every A segment, elements
-  int a_seg_k;       // contraction width of each A segment
-  const void* b_ptr[kMaxBSeg];
-  int b_n0[kMaxBSeg + 1];  // segment s = output columns [b_n0[s], b_n0[s+1])
-  int b_nseg;
+  int64_t lda;      // row-major A: row stride, elements
+  int a_seg_k;      // row-major A: contraction width of each segment
+  int a_packed;
+  const void* w;    // packed weights [N rows][Kd]
   int M, N, Kd;
-  int k_split;       // contraction elements per grid-z slice
-  float* out;        // [gridDim.z][M][N] fp32 partial sums
-};
-
-struct GemmPlan {
-  int MT;            // 16-row tiles per wave
-  int gx, gy, gz;    // grid: column groups, row groups, contraction slices
-  int k_split;
-  size_t partial_floats;  // gz * M * N
-};
-
-constexpr int kGemmNT = 4;  // 16-column tiles per workgroup
-
-GemmPlan plan_gemm(int M, int N, int Kd, bool bf16, int num_cu);
-GemmPlan plan_lmhead(int M, int N, int Kd, bool bf16);
-hipError_t launch_gemm(bool bf16, const GemmPlan& pl, const GemmArgs& a,
-                       hipStream_t s);
-// LM head: full contraction per workgroup; per row and 64-column tile writes
-// one Top2 record to part[row * gx + tile]; optional logits rows via rowmap.
-hipError_t launch_lmhead(bool bf16, const GemmPlan& pl, const GemmArgs& a,
-                         Top2* part, float* logits, const int* rowmap,
-                         int64_t logits_ld, hipStream_t s);
-
-// ---- epilogues (epilogue.hip) ------------------------------------------
-struct BlockState {
-  int32_t* tokens;     // [B][K] current block ids
-  int32_t* committed;  // [B][K] 1 = fixed
-  int32_t* rowmap;     // [B * n_cap] compact LM-head row -> b*(K-1) + i-1
+  int cmap, pair_group, pair_off;
+  // epilogue
+  int ep;
+  float* out_f32;   // EP_STORE / EP_RESID rows, ld = ldo
+  int64_t ldo;
+  void* out_t;      // EP_QKV: q [M][Hq*d]; EP_SWIGLU: packed act
+  void* kv;         // EP_QKV: this layer's cache; EP_KV: the whole cache
+  const float2* rope;
+  const int32_t* ctx_len;  // EP_QKV
+  int max_len, K;
+  const int32_t* row_seq;  // EP_KV
+  const int32_t* row_pos;
+  int Hq, Hkv, d, max_batch, P, max_ctx;
+  Top2* top2;              // EP_TOP2: [M][N / 16]
+  float* logits;           // EP_TOP2 debug rows (via rowmap), may be null
+  const int32_t* rowmap;   //   LM-head row -> block row b*K + i, or -1
+  int64_t logits_ld;
   int* err;
 };
 
+struct GemmPlan {
+  int MT, waves, gx, gy;
+};
+GemmPlan plan_gemm(int M, int N);
+hipError_t launch_gemm(bool bf16, const GemmPlan& pl, const GemmArgs& a,
+                       hipStream_t s);
+
+// Packs rows of up to kMaxBSeg row-major segments [n_s][K] (concatenated
+// along rows) into dst with the given column map.
+struct PackArgs {
+  const void* src[kMaxBSeg];
+  int n0[kMaxBSeg + 1];
+  int nseg;
+  int N, K, cmap, pair_group, pair_off;
+  void* dst;
+};
+hipError_t launch_pack(bool bf16, const PackArgs& a, hipStream_t s);
+
+// ---- row kernels (epilogue.hip) -------------------------------------------
+struct BlockState {
+  int32_t* tokens;     // [B][K] current block ids
+  int32_t* committed;  // [B][K] 1 = fixed
+  int32_t* rowmap;     // [B * n_cap] LM-head row -> block row b*K + i, or -1
+  int* err;
+};
+
+// x = E[token] (fp32); pass 0 also fills the block state; every pass
+// rebuilds the LM-head row map.
 hipError_t launch_embed(bool bf16, int B, int K, int D, int V, int mask_id,
                         int pass, int n_cap, const int32_t* anchor,
                         const int32_t* block_tokens, BlockState st,
-                        const void* embed, const void* gain, float eps,
-                        float* x, void* h, void* hf, int32_t* draft,
+                        const void* embed, float* x, int32_t* draft,
                         hipStream_t s);
 
-hipError_t launch_rows_rmsnorm(bool bf16, int rows, int D, int nsplit,
-                               const float* part, const void* gain, float eps,
-                               void* out, hipStream_t s);
-
-hipError_t launch_kv_inject_epilogue(bool bf16, int T, int nlayers, int Hkv,
-                                     int d, int nsplit, const float* part,
-                                     const int32_t* row_seq,
-                                     const int32_t* row_pos,
-                                     const float2* rope, int max_batch,
-                                     int max_ctx, int P, void* kv, int* err,
-                                     hipStream_t s);
-
-hipError_t launch_qkv_epilogue(bool bf16, int B, int K, int Hq, int Hkv, int d,
-                               int nsplit, const float* part,
-                               const int32_t* ctx_len, int max_len,
-                               const float2* rope, int P, int max_batch,
-                               void* q, void* kv_layer, int* err,
-                               hipStream_t s);
-
-// x += sum of partials; then either h = RMSNorm(x) * g (all rows) or, in
-// final mode, compact still-masked rows into hf with the final gain.
-hipError_t launch_resid_norm(bool bf16, int rows, int K, int D, int nsplit,
-                             const float* part, float* x, const void* gain,
-                             float eps, void* h, bool final_mode, int n_cap,
-                             BlockState st, hipStream_t s);
-
-hipError_t launch_swiglu(bool bf16, int rows, int I, int nsplit,
-                         const float* part, void* act, hipStream_t s);
+// out = RMSNorm(x[rowmap ? rowmap[r] : r]) * gain, packed (contraction D);
+// rows with rowmap < 0 and rows up to the next multiple of 16 are zero.
+hipError_t launch_rmsnorm(bool bf16, int rows, int D, const float* x,
+                          const int32_t* rowmap, const void* gain, float eps,
+                          void* out, hipStream_t s);
 
 // ---- attention (attention.hip) -----------------------------------------
 struct AttnArgs {
-  const void* q;        // [B*K][Hq*d]
+  const void* q;        // [B*K][Hq*d] row-major
   const void* kc;       // this layer's K cache [max_batch][Hkv][P][d]
   const void* vc;       // this layer's V cache
   const int32_t* ctx_len;
@@ -102,24 +141,19 @@ struct AttnArgs {
   float scale_log2;     // log2(e) / sqrt(d)
   float* part_o;        // [B][Hq][nch][K][d]
   float* part_ml;       // [B][Hq][nch][K][2]
-  void* o;              // [B*K][Hq*d]
+  void* o;              // packed [B*K rows][Hq*d]
 };
 hipError_t launch_attention(bool bf16, int d, int B, const AttnArgs& a,
                             hipStream_t s);
 
 // ---- head (head.hip) -----------------------------------------------------
-struct RowResult {
-  int32_t token;
-  float conf;
-  float margin;
-  float lse;
-};
-hipError_t launch_lm_merge(int rows, int ntiles, const Top2* part,
-                           RowResult* res, hipStream_t s);
+constexpr int kMergeChunks = 16;
+// part [rows][ntiles] -> part2 [rows][kMergeChunks], merged in tile order
+hipError_t launch_lm_merge(int rows, int ntiles, const Top2* part, Top2* part2,
+                           hipStream_t s);
 hipError_t launch_commit(int B, int K, int n_cap, int commit, bool last,
-                         const RowResult* res, BlockState st,
-                         int32_t* draft, float* conf, float* margin,
-                         hipStream_t s);
+                         const Top2* part2, BlockState st, int32_t* draft,
+                         float* conf, float* margin, hipStream_t s);
 hipError_t launch_verify(int B, int K, const int32_t* draft,
                          const int32_t* target, int32_t* accept,
                          int32_t* next_anchor, hipStream_t s);

@@ -67,7 +67,7 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
 /* Device error word bits (dflash_check_device_errors). */
 #define DFLASH_DEVERR_TOKEN    0x1  /* token id outside [0, vocab) */
-#define DFLASH_DEVERR_CTX_LEN  0x2  /* context length outside [0, max ctx] */
+#define DFLASH_DEVERR_CTX_LEN  0x2  /* context length outside [0, max_ctx_len] */
 #define DFLASH_DEVERR_SLOT     0x4  /* inject row's sequence slot out of range */
 #define DFLASH_DEVERR_POS      0x8  /* inject row's position out of range */
 
@@ -96,8 +96,10 @@ typedef struct {
 } dflash_config;
 
 /* Drafter weights, PyTorch Linear layout [out, in], row-major, dtype of the
- * config.  Per-layer entries are HOST arrays of num_layers DEVICE pointers;
- * the library copies those arrays at dflash_create, the weights themselves
+ * config.  Per-layer entries are HOST arrays of num_layers DEVICE pointers.
+ * dflash_create copies every projection matrix (fc, wq, wk, wv, wo, w_gate,
+ * w_up, w_down, lm_head) into the context's own fragment-major layout and
+ * never reads them again; embed and the norm gains are read in place and
  * must stay alive and unchanged until dflash_destroy. */
 typedef struct {
   const void* embed;        /* [V, D] */
@@ -119,7 +121,8 @@ typedef struct {
 typedef struct dflash_ctx dflash_ctx;
 
 /* Create a drafting context on the current HIP device: validates the config
- * and weights, allocates the context's own workspace (activations, split-K
+ * and weights, repacks the projection matrices (synchronises the device once),
+ * and allocates the context's workspace (activations, attention and LM-head
  * partials, RoPE table, device error word).  *out is set on success. */
 dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
                             dflash_ctx** out);
@@ -143,6 +146,22 @@ const char* dflash_last_error(void);
  * then clears them.  bits may be NULL. */
 dflash_status dflash_check_device_errors(dflash_ctx* ctx, void* stream,
                                          int32_t* bits);
+
+/* Benchmark timing of one kernel class, on the stream it runs on.
+ * kind: 0 = off, DFLASH_TIME_LMHEAD, DFLASH_TIME_ATTENTION (partial + merge),
+ * DFLASH_TIME_GEMM (every projection GEMM launch, epilogues excluded).
+ * While enabled, each launch of that class is bracketed by a pair of HIP
+ * events created here (up to 8192 launches are kept; later ones overwrite
+ * the oldest).  dflash_get_kernel_timing synchronises those events, returns
+ * how many launches were recorded and their summed duration in
+ * milliseconds, and clears the record.  Creating the events is the only
+ * work set_kernel_timing does on the device. */
+#define DFLASH_TIME_LMHEAD    1
+#define DFLASH_TIME_ATTENTION 2
+#define DFLASH_TIME_GEMM      3
+dflash_status dflash_set_kernel_timing(dflash_ctx* ctx, int32_t kind);
+dflash_status dflash_get_kernel_timing(dflash_ctx* ctx, int32_t* launches,
+                                       double* total_ms);
 
 /* KV injection of T context rows.
  *
