@@ -34,7 +34,9 @@ def hipcc() -> str:
 
 
 def common_flags():
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # DFLASH_HIPCC_FLAGS adds compiler flags (e.g. -D tuning overrides)
+    extra = os.environ.get("DFLASH_HIPCC_FLAGS", "").split()
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", *extra,
             # hipcc -O3 forms packed fp32 ops by itself; keep them off
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,

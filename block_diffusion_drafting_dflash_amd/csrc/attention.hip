@@ -5,7 +5,8 @@
 // query heads sharing that kv head (GQA group), each owning its 16 block
 // queries.  K and V tiles of 64 keys are staged once in LDS for all waves
 // (V transposed so the P.V product can use MFMA with keys as the contraction
-// index).  Each wave computes S^T = K Q^T with MFMA, keeps an online softmax
+// index); the next tile is fetched into registers while the current one is
+// computed.  Each wave computes S^T = K Q^T with MFMA, keeps an online softmax
 // per query in its own lanes, and accumulates O^T = V^T P^T.  Chunks write
 // unnormalised partial outputs with their running max and sum; a merge
 // kernel combines the chunks of a sequence in chunk order.
@@ -18,19 +19,50 @@ namespace {
 constexpr int kKeyTile = 64;
 constexpr int kVPad = 4;  // elements of padding per transposed V row
 
-template <typename T, int D>
-__global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
+// Each thread carries NP 16-byte pieces of K and of V for one 64-key tile;
+// the next tile's pieces are loaded into registers while the current tile is
+// computed from LDS.
+template <typename T, int D, int G>
+struct TileRegs {
+  static constexpr int PIECES = D / Storage<T>::E;  // 16-byte pieces per key
+  static constexpr int NP = kKeyTile * PIECES / (64 * G);
+  u32x4 k[NP], v[NP];
+};
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void load_tile(TileRegs<T, D, G>& t, const char* kb,
+                                          const char* vb, int kt, int n_valid,
+                                          int tid) {
+  constexpr int SZ = sizeof(T), E = Storage<T>::E;
+  constexpr int PIECES = TileRegs<T, D, G>::PIECES;
+#pragma unroll
+  for (int j = 0; j < TileRegs<T, D, G>::NP; ++j) {
+    const int idx = tid + j * 64 * G;
+    const int key = idx / PIECES, pc = idx % PIECES;
+    t.k[j] = u32x4{0u, 0u, 0u, 0u};
+    t.v[j] = u32x4{0u, 0u, 0u, 0u};
+    if (key < n_valid) {
+      const int64_t off = ((int64_t)(kt + key) * D + pc * E) * SZ;
+      t.k[j] = load16(kb + off);
+      t.v[j] = load16(vb + off);
+    }
+  }
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
   constexpr int E = Storage<T>::E, KC = Storage<T>::KC, SZ = sizeof(T);
   constexpr int DC = D / KC;
   constexpr int KROWB = D * SZ + 16;           // padded K row, bytes
   constexpr int VROW = kKeyTile + kVPad;       // transposed V row, elements
   constexpr int VROWB = VROW * SZ;
-  constexpr int PIECES = D / E;                // 16-byte pieces per key row
+  constexpr int PIECES = TileRegs<T, D, G>::PIECES;
+  constexpr int NP = TileRegs<T, D, G>::NP;
+  static_assert(NP * 64 * G == kKeyTile * PIECES, "tile pieces per thread");
   __shared__ __attribute__((aligned(16))) char ks[kKeyTile * KROWB];
   __shared__ __attribute__((aligned(16))) char vt[D * VROWB];
 
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int G = p.Hq / p.Hkv;
   int L = p.ctx_len[b];
   L = min(max(L, 0), p.max_len);
   const int nkeys = L + p.K;
@@ -38,10 +70,16 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
   if (k0 >= nkeys) return;
   const int k1 = min(nkeys, k0 + p.chunk);
 
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int hq = kvh * G + wave;
+
+  const int64_t head_off = ((int64_t)b * p.Hkv + kvh) * p.P * D;
+  const char* kbase = static_cast<const char*>(p.kc) + head_off * SZ;
+  const char* vbase = static_cast<const char*>(p.vc) + head_off * SZ;
+  TileRegs<T, D, G> regs;
+  load_tile<T, D, G>(regs, kbase, vbase, k0, min(kKeyTile, k1 - k0), tid);
 
   // Q fragments of this wave's head: lane (query r, group g)
   const char* qrow = static_cast<const char*>(p.q) +
@@ -50,10 +88,6 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) qf[dc] = load16(qrow + dc * KC * SZ);
 
-  const int64_t head_off = ((int64_t)b * p.Hkv + kvh) * p.P * D;
-  const char* kbase = static_cast<const char*>(p.kc) + head_off * SZ;
-  const char* vbase = static_cast<const char*>(p.vc) + head_off * SZ;
-
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
@@ -61,22 +95,21 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
 
   for (int kt = k0; kt < k1; kt += kKeyTile) {
     const int n_valid = min(kKeyTile, k1 - kt);
-    __syncthreads();
-    for (int idx = tid; idx < kKeyTile * PIECES; idx += nthr) {
+    __syncthreads();  // the previous tile's readers are done with LDS
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int idx = tid + j * 64 * G;
       const int key = idx / PIECES, pc = idx % PIECES;
-      u32x4 kv4 = {0u, 0u, 0u, 0u}, vv4 = {0u, 0u, 0u, 0u};
-      if (key < n_valid) {
-        const int64_t off = ((int64_t)(kt + key) * D + pc * E) * SZ;
-        kv4 = load16(kbase + off);
-        vv4 = load16(vbase + off);
-      }
-      *reinterpret_cast<u32x4*>(ks + key * KROWB + pc * E * SZ) = kv4;
-      const T* ve = reinterpret_cast<const T*>(&vv4);
+      *reinterpret_cast<u32x4*>(ks + key * KROWB + pc * E * SZ) = regs.k[j];
+      const T* ve = reinterpret_cast<const T*>(&regs.v[j]);
       T* vcol = reinterpret_cast<T*>(vt) + key;
 #pragma unroll
       for (int e = 0; e < E; ++e) vcol[(pc * E + e) * VROW] = ve[e];
     }
     __syncthreads();
+    if (kt + kKeyTile < k1)
+      load_tile<T, D, G>(regs, kbase, vbase, kt + kKeyTile,
+                         min(kKeyTile, k1 - kt - kKeyTile), tid);
 
     // S^T tile: rows = 64 keys (4 MFMA row tiles), columns = 16 queries
     f32x4 s[4];
@@ -152,76 +185,107 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
 
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  const int64_t base = (((int64_t)b * p.Hq + hq) * p.nch + c) * p.K + r;
+  // partials are chunk-major within (sequence, query head, query):
+  // part_o[((b*Hq + hq)*K + i)*nch + c][D], part_ml[... same index][2]
+  const int64_t base = (((int64_t)b * p.Hq + hq) * p.K + r) * p.nch + c;
   float* po = p.part_o + base * D;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) po[16 * dt + 4 * g + j] = o[dt][j];
-  if (g == 0) {
-    p.part_ml[base * 2] = m_run;
-    p.part_ml[base * 2 + 1] = l_tot;
-  }
+    *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt];
+  if (g == 0)
+    *reinterpret_cast<float2*>(p.part_ml + base * 2) = float2{m_run, l_tot};
 }
 
 // o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the sequence's
-// chunks (M = the largest m_c), in chunk order, written packed for the output
-// projection.  One workgroup per (sequence, query head, 4 block queries);
-// 32 lanes per query, each owning D/32 consecutive channels.
+// chunks (M = the largest m_c), written packed for the output projection.
+// One wave per (sequence, query head, block query): lane c reads chunk c's
+// (m, l) so the weights come from wave reductions (fixed butterfly order);
+// the partial outputs are then summed in chunk order, lane owning D/64
+// consecutive channels, with kMergeBatch independent loads in flight.
+constexpr int kMergeBatch = 16;
+
 template <typename T, int D>
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs p) {
-  constexpr int DPT = D / 32;
-  const int groups = p.K / 4;
-  const int bh = blockIdx.x / groups, qg = blockIdx.x % groups;
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
+  constexpr int DPL = D / 64;
+  const int wrow = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wrow >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int i = wrow % p.K, bh = wrow / p.K;
   const int b = bh / p.Hq, hq = bh % p.Hq;
-  const int i = qg * 4 + (threadIdx.x >> 5);
-  const int d0 = (threadIdx.x & 31) * DPT;
   int L = p.ctx_len[b];
   L = min(max(L, 0), p.max_len);
   const int nc = (L + p.K + p.chunk - 1) / p.chunk;
-  const int64_t base = ((int64_t)b * p.Hq + hq) * p.nch * p.K + i;
-  const float* ml = p.part_ml + base * 2;
-  const int64_t cstride = (int64_t)p.K;  // entries between chunks
+  const int64_t base = (int64_t)wrow * p.nch;  // == ((b*Hq + hq)*K + i)*nch
+  const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + base;
+
+  // chunk weights: lanes c, c + 64, ... (nc <= nch, any size)
   float M = -INFINITY;
-#pragma unroll 8
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[c * cstride * 2]);
-  float ls = 0.f, acc[DPT];
+  for (int c = lane; c < nc; c += 64) M = fmaxf(M, ml[c].x);
+  M = warp_max(M);
+  float ls = 0.f;
+  for (int c = lane; c < nc; c += 64) ls += exp2f(ml[c].x - M) * ml[c].y;
+  ls = warp_sum(ls);
+
+  float acc[DPL];
 #pragma unroll
-  for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
-#pragma unroll 8
-  for (int c = 0; c < nc; ++c) {
-    const float w = exp2f(ml[c * cstride * 2] - M);
-    ls += w * ml[c * cstride * 2 + 1];
-    const float* oc = p.part_o + (base + c * cstride) * D + d0;
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  const float* ob = p.part_o + base * D + lane * DPL;
+  for (int c0 = 0; c0 < nc; c0 += kMergeBatch) {
+    float v[kMergeBatch][DPL], w[kMergeBatch];
 #pragma unroll
-    for (int k = 0; k < DPT; ++k) acc[k] += w * oc[k];
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int c = c0 + u;
+      w[u] = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) v[u][e] = 0.f;
+      if (c < nc) {
+        w[u] = exp2f(ml[c].x - M);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) v[u][e] = ob[(int64_t)c * D + e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += w[u] * v[u][e];
   }
   const float inv = 1.f / ls;
-  const int row = b * p.K + i, Kd = p.Hq * D;
+  const int row = b * p.K + i, Kd = p.Hq * D, d0 = lane * DPL;
   T* dst = reinterpret_cast<T*>(static_cast<char*>(p.o) +
                                 packed_offset<T>(row, hq * D + d0, Kd));
 #pragma unroll
-  for (int k = 0; k < DPT; ++k) store_elem(dst, k, acc[k] * inv);
+  for (int e = 0; e < DPL; ++e) store_elem(dst, e, acc[e] * inv);
 }
 
-template <typename T, int D>
+template <typename T, int D, int G>
 hipError_t attn_t(int B, const AttnArgs& a, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  hipLaunchKernelGGL((attn_partial_kernel<T, D>), dim3(a.nch, a.Hkv, B),
+  hipLaunchKernelGGL((attn_partial_kernel<T, D, G>), dim3(a.nch, a.Hkv, B),
                      dim3(64 * G), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(B * a.Hq * (a.K / 4)),
-                     dim3(128), 0, s, a);
+  const int rows = B * a.Hq * a.K;
+  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3((rows + 3) / 4),
+                     dim3(256), 0, s, a, rows);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t attn_g(int B, const AttnArgs& a, hipStream_t s) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return attn_t<T, D, 1>(B, a, s);
+    case 2: return attn_t<T, D, 2>(B, a, s);
+    case 4: return attn_t<T, D, 4>(B, a, s);
+    case 8: return attn_t<T, D, 8>(B, a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_attention(bool bf16, int d, int B, const AttnArgs& a,
                             hipStream_t s) {
-  if (d == 128) return bf16 ? attn_t<bf16_t, 128>(B, a, s) : attn_t<float, 128>(B, a, s);
-  if (d == 64) return bf16 ? attn_t<bf16_t, 64>(B, a, s) : attn_t<float, 64>(B, a, s);
+  if (d == 128) return bf16 ? attn_g<bf16_t, 128>(B, a, s) : attn_g<float, 128>(B, a, s);
+  if (d == 64) return bf16 ? attn_g<bf16_t, 64>(B, a, s) : attn_g<float, 64>(B, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -145,10 +145,11 @@ dflash_status check_config(const dflash_config* c) {
     return fail(DFLASH_E_UNSUPPORTED, "head_dim %d (64 or 128)", c->head_dim);
   if (c->dtype == DFLASH_F32 && c->head_dim != 64)
     return fail(DFLASH_E_UNSUPPORTED, "f32 drafter needs head_dim 64");
+  const int group = c->num_kv_heads > 0 ? c->num_q_heads / c->num_kv_heads : 0;
   if (c->num_q_heads % c->num_kv_heads != 0 ||
-      c->num_q_heads / c->num_kv_heads > 8)
+      (group != 1 && group != 2 && group != 4 && group != 8))
     return fail(DFLASH_E_UNSUPPORTED,
-                "num_q_heads %d must be a multiple (<= 8x) of num_kv_heads %d",
+                "num_q_heads %d must be 1, 2, 4 or 8 times num_kv_heads %d",
                 c->num_q_heads, c->num_kv_heads);
   if (c->hidden % 64 || c->intermediate % 64 || c->target_hidden % 64 ||
       (c->num_q_heads * c->head_dim) % 64)
@@ -168,20 +169,27 @@ dflash_status check_config(const dflash_config* c) {
   return DFLASH_OK;
 }
 
-// Keys per attention workgroup: about 2 workgroups per CU over the batch,
-// at least one 64-key tile each.
+// Keys per attention workgroup: about DFLASH_ATTN_WG_PER_CU workgroups per
+// CU over the batch, at least DFLASH_ATTN_MIN_CHUNK keys (whole 64-key tiles)
+// each so that the chunk merge stays short.
+#ifndef DFLASH_ATTN_WG_PER_CU
+#define DFLASH_ATTN_WG_PER_CU 2
+#endif
+#ifndef DFLASH_ATTN_MIN_CHUNK
+#define DFLASH_ATTN_MIN_CHUNK 128
+#endif
 int attn_chunk(int B, int Hkv, int max_keys, int num_cu) {
-  int target = (2 * num_cu + B * Hkv - 1) / (B * Hkv);
+  int target = (DFLASH_ATTN_WG_PER_CU * num_cu + B * Hkv - 1) / (B * Hkv);
   if (target < 1) target = 1;
   int ch = (max_keys + target - 1) / target;
   ch = (ch + 63) / 64 * 64;
-  if (ch < 64) ch = 64;
+  if (ch < DFLASH_ATTN_MIN_CHUNK) ch = DFLASH_ATTN_MIN_CHUNK;
   return ch;
 }
 
 dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
                        int kind = DFLASH_TIME_GEMM) {
-  const GemmPlan pl = plan_gemm(a.M, a.N);
+  const GemmPlan pl = plan_gemm(a.M, a.N, a.ep == EP_TOP2);
   a.err = c->err;
   TimedLaunch tl(c, kind, s);
   DF_HIP(launch_gemm(c->bf16, pl, a, s));
@@ -372,7 +380,8 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
   const int TI = c.max_inject_rows;
   const int TI16 = (TI + 15) / 16 * 16;
   const int G = c.num_q_heads / c.num_kv_heads;
-  x->attn_floats = (size_t)G * (2 * x->num_cu + c.max_batch * c.num_kv_heads) * K;
+  x->attn_floats =
+      (size_t)G * (DFLASH_ATTN_WG_PER_CU * x->num_cu + c.max_batch * c.num_kv_heads) * K;
   const int lm_rows = c.max_batch * (K - 1);
   x->lm_part_count = (size_t)lm_rows * (c.vocab / 16);
 

@@ -23,18 +23,26 @@ __device__ __forceinline__ void rope_pair(float a, float b, float2 cs,
   rb = b * cs.x + a * cs.y;
 }
 
-template <int MT>
-constexpr int waves_for() {
-  return MT == 1 ? 8 : (MT == 2 ? 4 : 2);
-}
+// Waves per workgroup and fragment steps in flight per wave at batch 1
+// (one 16-row tile); measured on MI355X, see the design notes.
+#ifndef DFLASH_GEMM_W
+#define DFLASH_GEMM_W 8
+#endif
+#ifndef DFLASH_GEMM_U
+#define DFLASH_GEMM_U 8
+#endif
+#ifndef DFLASH_LM_W
+#define DFLASH_LM_W 16
+#endif
+#ifndef DFLASH_LM_U
+#define DFLASH_LM_U 8
+#endif
 
 // acc[m] over this wave's share of the contraction.
-template <typename T, int MT, int AP>
+template <typename T, int MT, int AP, int W, int U>
 __device__ __forceinline__ void gemm_core(const GemmArgs& p, int tile,
                                           int m_base, f32x4 (&acc)[MT]) {
   constexpr int E = Storage<T>::E, KC = Storage<T>::KC, SZ = sizeof(T);
-  constexpr int W = waves_for<MT>();
-  constexpr int U = 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int nsteps = p.Kd / KC;
@@ -224,13 +232,12 @@ __device__ void apply_epilogue(const GemmArgs& p, int tile, int m_base,
   }
 }
 
-template <typename T, int MT, int AP>
-__global__ __launch_bounds__(64 * waves_for<MT>()) void gemm_kernel(GemmArgs p) {
-  constexpr int W = waves_for<MT>();
+template <typename T, int MT, int AP, int W, int U>
+__global__ __launch_bounds__(64 * W) void gemm_kernel(GemmArgs p) {
   __shared__ float red[W * MT * 256];
   const int tile = blockIdx.x, m_base = blockIdx.y * 16 * MT;
   f32x4 acc[MT];
-  gemm_core<T, MT, AP>(p, tile, m_base, acc);
+  gemm_core<T, MT, AP, W, U>(p, tile, m_base, acc);
   reduce_waves<MT, W>(acc, red);
   apply_epilogue<T, MT, W>(p, tile, m_base, red);
 }
@@ -259,21 +266,28 @@ __global__ void pack_kernel(PackArgs a) {
 template <typename T, int AP>
 hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream_t s) {
   dim3 grid(pl.gx, pl.gy, 1), block(pl.waves * 64);
-  switch (pl.MT) {
-    case 1: hipLaunchKernelGGL((gemm_kernel<T, 1, AP>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_kernel<T, 2, AP>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_kernel<T, 4, AP>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (pl.MT == 1 && a.ep == EP_TOP2)
+    hipLaunchKernelGGL((gemm_kernel<T, 1, AP, DFLASH_LM_W, DFLASH_LM_U>), grid,
+                       block, 0, s, a);
+  else if (pl.MT == 1)
+    hipLaunchKernelGGL((gemm_kernel<T, 1, AP, DFLASH_GEMM_W, DFLASH_GEMM_U>),
+                       grid, block, 0, s, a);
+  else if (pl.MT == 2)
+    hipLaunchKernelGGL((gemm_kernel<T, 2, AP, 4, 8>), grid, block, 0, s, a);
+  else if (pl.MT == 4)
+    hipLaunchKernelGGL((gemm_kernel<T, 4, AP, 2, 8>), grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 }  // namespace
 
-GemmPlan plan_gemm(int M, int N) {
+GemmPlan plan_gemm(int M, int N, bool lm_head) {
   GemmPlan pl;
   pl.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  pl.waves = pl.MT == 1 ? 8 : (pl.MT == 2 ? 4 : 2);
+  pl.waves = pl.MT == 1 ? (lm_head ? DFLASH_LM_W : DFLASH_GEMM_W)
+                        : (pl.MT == 2 ? 4 : 2);
   pl.gx = N / 16;
   pl.gy = (M + 16 * pl.MT - 1) / (16 * pl.MT);
   return pl;

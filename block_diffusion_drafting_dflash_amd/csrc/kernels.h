@@ -92,7 +92,7 @@ struct GemmArgs {
 struct GemmPlan {
   int MT, waves, gx, gy;
 };
-GemmPlan plan_gemm(int M, int N);
+GemmPlan plan_gemm(int M, int N, bool lm_head);
 hipError_t launch_gemm(bool bf16, const GemmPlan& pl, const GemmArgs& a,
                        hipStream_t s);
 
