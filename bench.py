@@ -119,6 +119,45 @@ def kernel_cost(wl, lens, kind):
 
 # ---------------------------------------------------------------------------
 
+KERNEL_SOURCES = {
+    "lmhead": ["gemm.hip"],
+    "gemm": ["gemm.hip"],
+    "attention": ["attention.hip"],
+}
+
+
+def kernel_source_sha(kind):
+    """sha256 over the sources that define the timed kernel."""
+    import hashlib
+    csrc = os.path.join(ROOT, "block_diffusion_drafting_dflash_amd", "csrc")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind] + ["common.h", "kernels.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(wl, kind):
+    """HBM bytes per launch from the committed FETCH_SIZE + WRITE_SIZE
+    counter summary of this kernel and workload, or None when there is none
+    or the kernel's sources have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{wl.name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_sha(kind):
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def setup(wl, torch, dfl, dev):
     weights = W.gen_weights(wl, device=dev)
     lens = W.gen_ctx_lens(wl)
@@ -323,7 +362,8 @@ def main():
                    "new_rows_per_seq": wl.new_rows},
         "roofline": {"kernel": kind, "bound": bound, "achieved": round(ach, 1),
                      "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
-                     "traffic": None, "launches": n_launch,
+                     "traffic": measured_traffic(wl, kind),
+                     "launches": n_launch,
                      "avg_us": round(k_avg_s * 1e6, 2),
                      "alg_bytes_per_launch": int(kb),
                      "alg_flops_per_launch": kf},

@@ -1,0 +1,193 @@
+"""C-ABI checks that need no GPU: the shared libraries load, export every
+function that include/*.h declares (and nothing the binding expects is
+missing), and host-side validation rejects bad calls before any launch.
+
+No call here reaches a HIP runtime function: every case fails validation
+first (the entry points validate all host arguments before launching)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_diffusion_drafting_dflash_amd as dfl
+from block_diffusion_drafting_dflash_amd import binding
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = {"dflash.h": binding.LIB_PATH,
+           "dflash_harness.h": binding.HARNESS_PATH}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not (os.path.exists(binding.LIB_PATH) and
+            os.path.exists(binding.HARNESS_PATH)):
+        from block_diffusion_drafting_dflash_amd import build
+        build.build()
+
+
+def declared_functions(header: str):
+    """Names of the functions a header declares inside its extern "C"
+    block (comments stripped)."""
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return sorted(set(re.findall(r"\b(dflash_[a-z0-9_]+)\s*\(", text)))
+
+
+def exported(lib_path: str):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path],
+                         capture_output=True, text=True, check=True).stdout
+    return {line.split()[-1] for line in out.splitlines()
+            if len(line.split()) >= 3 and line.split()[1] == "T"}
+
+
+@pytest.mark.parametrize("header", sorted(HEADERS))
+def test_every_declared_function_is_exported(header):
+    names = declared_functions(header)
+    assert names, f"no declarations parsed from {header}"
+    syms = exported(HEADERS[header])
+    missing = [n for n in names if n not in syms]
+    assert not missing, f"{header}: not exported by the library: {missing}"
+    lib = ctypes.CDLL(HEADERS[header])
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_binding_symbol_lists_match_headers():
+    assert sorted(binding.LIB_SYMBOLS) == declared_functions("dflash.h")
+    assert sorted(binding.HARNESS_SYMBOLS) == declared_functions(
+        "dflash_harness.h")
+
+
+def test_exports_are_only_the_declared_c_functions():
+    """The library exports its C entry points unmangled; every exported
+    dflash_* symbol is declared in the header."""
+    syms = {s for s in exported(binding.LIB_PATH) if s.startswith("dflash_")}
+    assert syms == set(declared_functions("dflash.h"))
+
+
+def test_status_codes_match_header():
+    text = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    codes = dict((n, int(v)) for n, v in
+                 re.findall(r"(DFLASH_(?:OK|E_[A-Z]+))\s*=\s*(-?\d+)", text))
+    assert {v: k for k, v in codes.items()} == binding.STATUS
+
+
+# ---------------------------------------------------------------------------
+# host-side validation (returns before any device work)
+
+def lib():
+    return binding.load_library()
+
+
+def last_error():
+    return lib().dflash_last_error().decode()
+
+
+def good_config(**kw):
+    wl = W.small_bf16()
+    cfg = binding.make_config(wl)
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+@pytest.mark.parametrize("field,value,status,msg", [
+    ("block_size", 8, "DFLASH_E_UNSUPPORTED", "block_size"),
+    ("head_dim", 96, "DFLASH_E_UNSUPPORTED", "head_dim"),
+    ("num_kv_heads", 3, "DFLASH_E_UNSUPPORTED", "num_kv_heads"),
+    ("vocab", 4001, "DFLASH_E_UNSUPPORTED", "vocab"),
+    ("hidden", 520, "DFLASH_E_UNSUPPORTED", "multiples of 64"),
+    ("num_layers", 0, "DFLASH_E_INVALID", None),
+    ("max_batch", 0, "DFLASH_E_INVALID", None),
+    ("rope_theta", 0.0, "DFLASH_E_INVALID", "rope_theta"),
+    ("num_target_layers", 9, "DFLASH_E_UNSUPPORTED", "num_target_layers"),
+    ("mask_token_id", 4000, "DFLASH_E_INVALID", None),
+])
+def test_create_rejects_bad_config(field, value, status, msg):
+    cfg = good_config(**{field: value})
+    out = ctypes.c_void_p()
+    st = lib().dflash_create(ctypes.byref(cfg), None, ctypes.byref(out))
+    assert binding.STATUS[st] == status, (st, last_error())
+    assert out.value is None
+    if msg:
+        assert msg in last_error()
+
+
+def test_create_rejects_null_weights_and_out():
+    cfg = good_config()
+    out = ctypes.c_void_p()
+    st = lib().dflash_create(ctypes.byref(cfg), None, ctypes.byref(out))
+    assert binding.STATUS[st] == "DFLASH_E_INVALID"
+    assert "weights" in last_error()
+    st = lib().dflash_create(ctypes.byref(cfg), None, None)
+    assert binding.STATUS[st] == "DFLASH_E_INVALID"
+    w = binding.Weights()
+    st = lib().dflash_create(ctypes.byref(cfg), ctypes.byref(w),
+                             ctypes.byref(out))
+    assert binding.STATUS[st] == "DFLASH_E_INVALID"
+    assert "NULL" in last_error()
+
+
+def test_kv_cache_bytes_layout():
+    wl = W.small_bf16()
+    cfg = binding.make_config(wl, max_batch=5, max_ctx=1000)
+    want = (wl.num_layers * 2 * 5 * wl.num_kv_heads * (1000 + 16) *
+            wl.head_dim * 2)
+    assert lib().dflash_kv_cache_bytes(ctypes.byref(cfg)) == want
+    cfg.dtype = binding.DTYPE["f32"]
+    assert lib().dflash_kv_cache_bytes(ctypes.byref(cfg)) == 2 * want
+    cfg.max_batch = 0
+    assert lib().dflash_kv_cache_bytes(ctypes.byref(cfg)) == 0
+
+
+def test_calls_with_null_context_are_rejected():
+    L = lib()
+    p = ctypes.c_void_p(16)
+    st = L.dflash_inject_kv(None, None, None, 64, 1, p, p, p)
+    assert binding.STATUS[st] == "DFLASH_E_INVALID"
+    st = L.dflash_draft_block(None, None, 1, p, None, p, 10, p, 1, 0, p,
+                              None, None, None)
+    assert binding.STATUS[st] == "DFLASH_E_INVALID"
+    assert binding.STATUS[L.dflash_set_kernel_timing(None, 1)] == \
+        "DFLASH_E_INVALID"
+    assert binding.STATUS[L.dflash_check_device_errors(None, None, None)] == \
+        "DFLASH_E_INVALID"
+
+
+@pytest.mark.parametrize("batch,block,null,status", [
+    (0, 16, False, "DFLASH_E_SHAPE"),
+    (4, 0, False, "DFLASH_E_SHAPE"),
+    (4, 65, False, "DFLASH_E_SHAPE"),
+    (4, 16, True, "DFLASH_E_INVALID"),
+])
+def test_verify_validation(batch, block, null, status):
+    p = ctypes.c_void_p(16)
+    args = [None if null else p, p, p, p]
+    st = lib().dflash_verify_greedy(None, batch, block, *args)
+    assert binding.STATUS[st] == status
+
+
+def test_harness_validation():
+    h = binding.load_harness()
+    p = ctypes.c_void_p(16)
+    st = h.dflash_harness_synth_target(None, 0, 16, 100, p, p, p, p, p, p)
+    assert st != 0
+    st = h.dflash_harness_synth_target(None, 2, 16, 100, None, p, p, p, p, p)
+    assert st != 0
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """The package never imports the oracle and fails loudly without its
+    library."""
+    pkg = os.path.dirname(dfl.__file__)
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            src = open(os.path.join(pkg, f)).read()
+            assert not re.search(r"^\s*(from|import)\s+oracle", src, re.M), f
+    assert "raise RuntimeError" in open(binding.__file__).read()
