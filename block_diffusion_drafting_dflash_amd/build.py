@@ -17,8 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-LIB_SOURCES = ["dflash_api.hip", "gemm.hip", "epilogue.hip", "attention.hip",
-               "head.hip"]
+LIB_SOURCES = ["dflash_api.hip", "gemm.hip", "gemm_tiled.hip", "epilogue.hip",
+               "attention.hip", "head.hip"]
 HARNESS_SOURCES = ["harness.hip"]
 
 LIB = os.path.join(PKG, "libdflash.so")

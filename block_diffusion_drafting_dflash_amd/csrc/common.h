@@ -85,6 +85,17 @@ __device__ __forceinline__ void mma16(f32x4& acc, u32x4 a, u32x4 b, float) {
                                              __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
+// 32x32 output tile, contraction 16 (bf16).  Lane l supplies row (A) or
+// column (B) l % 32 with contraction elements 8*(l/32) .. +8; register j of
+// the result holds row 8*(j/4) + 4*(l/32) + j%4, column l % 32 (checked on
+// gfx950 against a host product).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ void mma32(f32x16& acc, u32x4 a, u32x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0, 0,
+      0);
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

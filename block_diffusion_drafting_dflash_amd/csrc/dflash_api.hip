@@ -72,6 +72,7 @@ struct dflash_ctx {
   float2* rope = nullptr;
   float* u = nullptr;        // fused target features before RMSNorm [TI][D]
   void* cond = nullptr;      // H_cond, packed [TI16][D]
+  void* hpk = nullptr;       // target hidden states, packed [TI16][n_t * D_t]
   float* x = nullptr;        // residual rows [R][D]
   void* h = nullptr;         // RMSNorm(x) * g, packed [R][D]
   void* hf = nullptr;        // final-norm rows of still-masked positions, packed
@@ -187,10 +188,26 @@ int attn_chunk(int B, int Hkv, int max_keys, int num_cu) {
   return ch;
 }
 
+// Up to 16 rows (and up to 64 outside the LM head) a GEMM is a weight
+// stream: wide workgroups over one 16-column tile (gemm.hip).  Beyond that
+// it is a dense contraction: MFMA tiles staged through LDS (gemm_tiled.hip,
+// bf16 only); a row-major activation operand is packed first.
 dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
                        int kind = DFLASH_TIME_GEMM) {
-  const GemmPlan pl = plan_gemm(a.M, a.N, a.ep == EP_TOP2);
   a.err = c->err;
+  const bool lm = a.ep == EP_TOP2;
+  if (c->bf16 && (a.M > 64 || (lm && a.M > 16))) {
+    if (!a.a_packed) {
+      DF_HIP(launch_pack_act(true, a, c->hpk, s));
+      a.a_ptr[0] = c->hpk;
+      a.a_packed = 1;
+      a.a_seg_k = a.Kd;
+    }
+    TimedLaunch tl(c, kind, s);
+    DF_HIP(launch_gemm_tiled(true, plan_tiled(a.M, a.N), a, s));
+    return DFLASH_OK;
+  }
+  const GemmPlan pl = plan_gemm(a.M, a.N, lm);
   TimedLaunch tl(c, kind, s);
   DF_HIP(launch_gemm(c->bf16, pl, a, s));
   return DFLASH_OK;
@@ -390,6 +407,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
       {(void**)&x->rope, (size_t)x->P * (d / 2) * sizeof(float2)},
       {(void**)&x->u, (size_t)TI * D * sizeof(float)},
       {&x->cond, (size_t)TI16 * D * esz},
+      {&x->hpk, (size_t)TI16 * c.num_target_layers * c.target_hidden * esz},
       {(void**)&x->x, (size_t)R * D * sizeof(float)},
       {&x->h, (size_t)R * D * esz},
       {&x->hf, (size_t)R * D * esz},

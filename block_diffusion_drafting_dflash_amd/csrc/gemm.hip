@@ -10,18 +10,11 @@
 // finished tile is handled by the same workgroup (residual add, RoPE and the
 // KV-cache scatter, SwiGLU, the LM-head top-2 reduction), so no workgroup
 // ever waits on another.
-#include "../../include/dflash.h"
-#include "kernels.h"
+#include "gemm_epilogue.h"
 
 namespace dflash {
 
 namespace {
-
-__device__ __forceinline__ void rope_pair(float a, float b, float2 cs,
-                                          float& ra, float& rb) {
-  ra = a * cs.x - b * cs.y;
-  rb = b * cs.x + a * cs.y;
-}
 
 // Waves per workgroup and fragment steps in flight per wave at batch 1
 // (one 16-row tile); measured on MI355X, see the design notes.
@@ -149,12 +142,7 @@ __device__ void apply_epilogue(const GemmArgs& p, int tile, int m_base,
         v.m1 = z;
         v.i1 = col;
         v.s = 1.f;
-        if (p.logits != nullptr) {
-          const int br = p.rowmap[row];
-          if (br >= 0)
-            p.logits[((int64_t)(br / p.K) * (p.K - 1) + (br % p.K) - 1) *
-                         p.logits_ld + col] = z;
-        }
+        if (p.logits != nullptr) store_debug_logit(p, row, col, z);
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) v = top2_merge(v, top2_shfl_xor(v, o));
@@ -164,71 +152,13 @@ __device__ void apply_epilogue(const GemmArgs& p, int tile, int m_base,
     return;
   }
   // pair epilogues: tile column c < 8 with its partner c + 8
-  const int half = p.d / 2;
   for (int q = tid; q < MT * 128; q += W * 64) {
     const int c = q & 7, rg = (q >> 3) & 3, j = (q >> 5) & 3, m = q >> 7;
     const int idx = (m * 4 + j) * 64 + rg * 16 + c;
-    const float a = red[idx], b = red[idx + 8];
     const int row = m_base + 16 * m + 4 * rg + j;
     if (row >= p.M) continue;
     const int col = map_col(p.cmap, p.pair_group, p.pair_off, tile, c);
-    if (p.ep == EP_SWIGLU) {
-      T* act = static_cast<T*>(p.out_t);
-      const int64_t off = packed_offset<T>(row, col, p.pair_off) / sizeof(T);
-      store_elem(act, off, a / (1.f + __expf(-a)) * b);
-      continue;
-    }
-    const int head = col / p.d, i = col % p.d;  // i < d/2
-    if (p.ep == EP_QKV) {
-      const int bs = row / p.K;
-      int L = p.ctx_len[bs];
-      if (L < 0 || L > p.max_len) {
-        set_error(p.err, DFLASH_DEVERR_CTX_LEN);
-        L = min(max(L, 0), p.max_len);
-      }
-      const int pos = L + row % p.K;
-      const float2 cs = p.rope[(int64_t)pos * half + i];
-      float ra, rb;
-      T* dst;
-      if (head < p.Hq) {
-        dst = static_cast<T*>(p.out_t) + (int64_t)row * p.Hq * p.d + head * p.d;
-        rope_pair(a, b, cs, ra, rb);
-      } else {
-        const bool is_k = head < p.Hq + p.Hkv;
-        const int h = is_k ? head - p.Hq : head - p.Hq - p.Hkv;
-        dst = static_cast<T*>(p.kv) +
-              (is_k ? 0 : (int64_t)p.max_batch * p.Hkv * p.P * p.d) +
-              (((int64_t)bs * p.Hkv + h) * p.P + pos) * p.d;
-        if (is_k) {
-          rope_pair(a, b, cs, ra, rb);
-        } else {
-          ra = a;
-          rb = b;
-        }
-      }
-      store_elem(dst, i, ra);
-      store_elem(dst, i + half, rb);
-    } else {  // EP_KV: injected context rows
-      const int seq = p.row_seq[row], pos = p.row_pos[row];
-      if (seq < 0 || seq >= p.max_batch) {
-        set_error(p.err, DFLASH_DEVERR_SLOT);
-        continue;
-      }
-      if (pos < 0 || pos >= p.max_ctx) {
-        set_error(p.err, DFLASH_DEVERR_POS);
-        continue;
-      }
-      const int l = head / (2 * p.Hkv), w = head % (2 * p.Hkv);
-      const bool is_k = w < p.Hkv;
-      const int h = is_k ? w : w - p.Hkv;
-      const int64_t plane = (int64_t)p.max_batch * p.Hkv * p.P * p.d;
-      T* dst = static_cast<T*>(p.kv) + (2 * l + (is_k ? 0 : 1)) * plane +
-               (((int64_t)seq * p.Hkv + h) * p.P + pos) * p.d;
-      float ra = a, rb = b;
-      if (is_k) rope_pair(a, b, p.rope[(int64_t)pos * half + i], ra, rb);
-      store_elem(dst, i, ra);
-      store_elem(dst, i + half, rb);
-    }
+    pair_epilogue<T>(p, row, col, red[idx], red[idx + 8]);
   }
 }
 
@@ -275,7 +205,7 @@ hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream_t s) {
   else if (pl.MT == 2)
     hipLaunchKernelGGL((gemm_kernel<T, 2, AP, 4, 8>), grid, block, 0, s, a);
   else if (pl.MT == 4)
-    hipLaunchKernelGGL((gemm_kernel<T, 4, AP, 2, 8>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<T, 4, AP, 16, 2>), grid, block, 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -287,7 +217,7 @@ GemmPlan plan_gemm(int M, int N, bool lm_head) {
   GemmPlan pl;
   pl.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   pl.waves = pl.MT == 1 ? (lm_head ? DFLASH_LM_W : DFLASH_GEMM_W)
-                        : (pl.MT == 2 ? 4 : 2);
+                        : (pl.MT == 2 ? 4 : 16);
   pl.gx = N / 16;
   pl.gy = (M + 16 * pl.MT - 1) / (16 * pl.MT);
   return pl;

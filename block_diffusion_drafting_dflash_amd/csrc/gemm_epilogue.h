@@ -1,0 +1,95 @@
+// Per-element GEMM epilogues shared by the wide (batch-1) and tiled
+// (batched) projection kernels.
+#pragma once
+
+#include "../../include/dflash.h"
+#include "kernels.h"
+
+namespace dflash {
+
+__device__ __forceinline__ void rope_pair(float a, float b, float2 cs,
+                                          float& ra, float& rb) {
+  ra = a * cs.x - b * cs.y;
+  rb = b * cs.x + a * cs.y;
+}
+
+// One finished output pair of a MAP_PAIRS GEMM: `a` is low column `col`,
+// `b` its partner at col + pair_off, both of output row `row` (< M).
+//   EP_SWIGLU: act[row][col] = silu(a) * b (packed, contraction pair_off)
+//   EP_QKV:    q -> RoPE -> q buffer; block k -> RoPE and v -> this layer's
+//              cache at position L_b + i
+//   EP_KV:     injected row -> RoPE(k), v -> cache of layer col / (2 Hkv d)
+template <typename T>
+__device__ __forceinline__ void pair_epilogue(const GemmArgs& p, int row,
+                                              int col, float a, float b) {
+  if (p.ep == EP_SWIGLU) {
+    T* act = static_cast<T*>(p.out_t);
+    const int64_t off = packed_offset<T>(row, col, p.pair_off) / sizeof(T);
+    store_elem(act, off, a / (1.f + __expf(-a)) * b);
+    return;
+  }
+  const int half = p.d / 2;
+  const int head = col / p.d, i = col % p.d;  // i < d/2
+  if (p.ep == EP_QKV) {
+    const int bs = row / p.K;
+    int L = p.ctx_len[bs];
+    if (L < 0 || L > p.max_len) {
+      set_error(p.err, DFLASH_DEVERR_CTX_LEN);
+      L = min(max(L, 0), p.max_len);
+    }
+    const int pos = L + row % p.K;
+    const float2 cs = p.rope[(int64_t)pos * half + i];
+    float ra, rb;
+    T* dst;
+    if (head < p.Hq) {
+      dst = static_cast<T*>(p.out_t) + (int64_t)row * p.Hq * p.d + head * p.d;
+      rope_pair(a, b, cs, ra, rb);
+    } else {
+      const bool is_k = head < p.Hq + p.Hkv;
+      const int h = is_k ? head - p.Hq : head - p.Hq - p.Hkv;
+      dst = static_cast<T*>(p.kv) +
+            (is_k ? 0 : (int64_t)p.max_batch * p.Hkv * p.P * p.d) +
+            (((int64_t)bs * p.Hkv + h) * p.P + pos) * p.d;
+      if (is_k) {
+        rope_pair(a, b, cs, ra, rb);
+      } else {
+        ra = a;
+        rb = b;
+      }
+    }
+    store_elem(dst, i, ra);
+    store_elem(dst, i + half, rb);
+    return;
+  }
+  // EP_KV: injected context rows
+  const int seq = p.row_seq[row], pos = p.row_pos[row];
+  if (seq < 0 || seq >= p.max_batch) {
+    set_error(p.err, DFLASH_DEVERR_SLOT);
+    return;
+  }
+  if (pos < 0 || pos >= p.max_ctx) {
+    set_error(p.err, DFLASH_DEVERR_POS);
+    return;
+  }
+  const int l = head / (2 * p.Hkv), w = head % (2 * p.Hkv);
+  const bool is_k = w < p.Hkv;
+  const int h = is_k ? w : w - p.Hkv;
+  const int64_t plane = (int64_t)p.max_batch * p.Hkv * p.P * p.d;
+  T* dst = static_cast<T*>(p.kv) + (2 * l + (is_k ? 0 : 1)) * plane +
+           (((int64_t)seq * p.Hkv + h) * p.P + pos) * p.d;
+  float ra = a, rb = b;
+  if (is_k) rope_pair(a, b, p.rope[(int64_t)pos * half + i], ra, rb);
+  store_elem(dst, i, ra);
+  store_elem(dst, i + half, rb);
+}
+
+// Debug copy of one LM-head logit (row -> block row via the row map).
+__device__ __forceinline__ void store_debug_logit(const GemmArgs& p, int row,
+                                                  int col, float z) {
+  const int br = p.rowmap[row];
+  if (br >= 0)
+    p.logits[((int64_t)(br / p.K) * (p.K - 1) + (br % p.K) - 1) * p.logits_ld +
+             col] = z;
+}
+
+}  // namespace dflash

@@ -96,6 +96,26 @@ GemmPlan plan_gemm(int M, int N, bool lm_head);
 hipError_t launch_gemm(bool bf16, const GemmPlan& pl, const GemmArgs& a,
                        hipStream_t s);
 
+// Tiled MFMA GEMM for batched rows (gemm_tiled.hip): output block shapes
+// rows x columns; each instance keeps its fragments in LDS per step.
+enum TileCfg : int {
+  TILE_64x64 = 0,
+  TILE_128x128 = 1,
+  TILE_256x64 = 2,
+  TILE_256x128 = 3,
+  TILE_128x256 = 4,
+  TILE_256x256 = 5,
+  TILE_NCFG = 6,
+};
+int plan_tiled(int M, int N);
+// bf16 only; a.a_packed must be set; a.M any size, a.N % 16 == 0,
+// a.Kd % 64 == 0
+hipError_t launch_gemm_tiled(bool bf16, int cfg, const GemmArgs& a,
+                             hipStream_t s);
+// dst = packed copy of a's row-major A segments (M rows, contraction a.Kd)
+hipError_t launch_pack_act(bool bf16, const GemmArgs& a, void* dst,
+                           hipStream_t s);
+
 // Packs rows of up to kMaxBSeg row-major segments [n_s][K] (concatenated
 // along rows) into dst with the given column map.
 struct PackArgs {

@@ -41,15 +41,18 @@ def bf16_ulp(x):
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
-def check_bf16_close(gpu, ref, what="", rel_rms=2e-3):
+def check_bf16_close(gpu, ref, what="", rel_rms=1e-2):
     """bf16 tensors computed from bf16-stored intermediates.
 
     The stored intermediate (e.g. H_cond) is rounded to bf16 from an fp32
     value on the GPU and an fp64 value in the oracle; about 1e-3 of its
     elements land on neighbouring bf16 values, and each such flip moves every
-    element computed from that row by |W| * ulp(c), an absolute amount.  So:
+    element computed from that row by |W_ij| * ulp(c_j), an absolute amount.
+    Worst case at these shapes: |c_j| up to ~4.5 (unit-RMS features times
+    gains up to 1.5) has ulp 2^-5, |W_ij| up to 4 sigma = 0.08, and RoPE adds
+    two such terms: ~5e-3, about 1% of RMS(K) ~ 0.46.  So:
     |gpu - ref| <= 1 ulp(max magnitude) + rel_rms * RMS(ref), and at least
-    99% of elements within 1 ulp.
+    99% of elements within 1 ulp (the common case stays tight).
     """
     gpu, ref = np.asarray(gpu), np.asarray(ref)
     np.testing.assert_array_equal(round_bf16(gpu), gpu)  # stored as bf16

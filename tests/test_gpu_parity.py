@@ -19,13 +19,22 @@ pytestmark = pytest.mark.gpu
 dfl = pytest.importorskip("block_diffusion_drafting_dflash_amd")
 
 
-def small_s2():
-    return W.small_bf16(num_passes=2, commit_per_pass=8, name="small-bf16-S2")
+def small_s2(**kw):
+    return W.small_bf16(num_passes=2, commit_per_pass=8, name="small-bf16-S2",
+                        **kw)
 
 
+# Batch sizes pick the GEMM paths: 3 sequences (48 block rows) stream the
+# weights with wide workgroups; 8 (128 rows) and 36 (576 rows) take the
+# LDS-tiled MFMA kernel with 64x64 and 128x128 blocks (as do the LM head
+# and the injection of every prefix above 64 rows).
 WLS = {
     "tiny-f32": W.WORKLOADS["tiny-f32"],
     "small-bf16": W.small_bf16(),
+    "small-bf16-b8": W.small_bf16(batch=8, ctx_min=20, ctx_max=150,
+                                  name="small-bf16-b8", seed=78),
+    "small-bf16-b36": W.small_bf16(batch=36, ctx_min=16, ctx_max=80,
+                                   name="small-bf16-b36", seed=79),
 }
 
 
@@ -189,8 +198,9 @@ def test_draft_single_pass_parity(name):
     assert np.abs(g["margin"] - mg).max() <= 2 * LOGIT_TOL[wl.dtype]
 
 
-def test_draft_two_pass_parity_and_teacher_forcing():
-    wl = small_s2()
+@pytest.mark.parametrize("batch", [3, 8])
+def test_draft_two_pass_parity_and_teacher_forcing(batch):
+    wl = small_s2(batch=batch)
     say("[draft S=2] small-bf16")
     w_cpu, w_dev, ctx = _setup(wl)
     model = OracleModel(wl, w_cpu)
