@@ -66,14 +66,15 @@ __global__ __launch_bounds__(256) void embed_kernel(
 
 // out[row] = RMSNorm(x[src]) * g written packed, src = rowmap ? rowmap[row]
 // : row; rows without a source (padding to a multiple of 16, unmapped LM-head
-// rows) are written as zeros.  One thread per 16-byte chunk of the row.
+// rows) are written as zeros.  One workgroup per row, one thread per 16-byte
+// chunk: the fastest form up to a few hundred rows.
 constexpr int kNormChunks = 4;  // chunks per thread: D <= 256 * E * 4
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(int rows, int D,
-                                                      const float* x,
-                                                      const int32_t* rowmap,
-                                                      const T* g, float eps,
-                                                      T* out) {
+__global__ __launch_bounds__(256) void rmsnorm_row_kernel(int rows, int D,
+                                                          const float* x,
+                                                          const int32_t* rowmap,
+                                                          const T* g, float eps,
+                                                          T* out) {
   constexpr int E = Storage<T>::E;
   __shared__ float scratch[4];
   const int row = blockIdx.x, tid = threadIdx.x;
@@ -118,6 +119,82 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int rows, int D,
   }
 }
 
+// The same, one workgroup per 16-row tile of the packed output, wave r on
+// row r (faster from ~512 rows, where the row form's partial-fragment
+// stores dominate).
+// First each wave reduces its row's sum of squares (the row map picks the
+// source row; -1 and rows past `rows` give a zero row); then every wave
+// writes whole 1 KiB fragments of the packed tile (lane l: tile row l % 16,
+// contraction group l / 16), so every store is part of one contiguous
+// wave-wide write.
+template <typename T>
+__global__ __launch_bounds__(1024) void rmsnorm_tile_kernel(int rows, int D,
+                                                       const float* x,
+                                                       const int32_t* rowmap,
+                                                       const T* g, float eps,
+                                                       T* out) {
+  constexpr int E = Storage<T>::E, KC = Storage<T>::KC;
+  __shared__ float inv_s[16];
+  __shared__ int src_s[16];
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  {
+    const int row = t * 16 + wave;
+    const int src = row < rows ? (rowmap ? rowmap[row] : row) : -1;
+    float ss = 0.f;
+    if (src >= 0) {
+      const float* xr = x + (int64_t)src * D;
+#pragma unroll 8
+      for (int c = lane * 4; c < D; c += 256) {
+        const f32x4 q = __builtin_bit_cast(f32x4, load16(xr + c));
+        ss += q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w;
+      }
+    }
+    ss = warp_sum(ss);
+    if (lane == 0) {
+      inv_s[wave] = 1.f / sqrtf(ss / (float)D + eps);
+      src_s[wave] = src;
+    }
+  }
+  __syncthreads();
+  const int r = lane & 15, grp = lane >> 4;
+  const int src = src_s[r];
+  const float inv = inv_s[r];
+  const int nsteps = D / KC;
+  char* ob = reinterpret_cast<char*>(out) + ((int64_t)t * nsteps * 64 + lane) * 16;
+  if (src < 0) {  // lanes of rows without a source write zeros
+    for (int s = wave; s < nsteps; s += 16)
+      *reinterpret_cast<u32x4*>(ob + (int64_t)s * 1024) = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const float* xr = x + (int64_t)src * D + grp * E;
+  const T* gk = g + grp * E;
+  constexpr int U = 4;  // fragments whose loads are in flight together
+  for (int s0 = wave; s0 < nsteps; s0 += 16 * U) {
+    u32x4 gv[U], q[U][E / 4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + 16 * u, nsteps - 1);
+      gv[u] = load16(gk + s * KC);
+#pragma unroll
+      for (int e = 0; e < E / 4; ++e) q[u][e] = load16(xr + s * KC + 4 * e);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + 16 * u;
+      if (s >= nsteps) break;
+      const T* gt = reinterpret_cast<const T*>(&gv[u]);
+      u32x4 v;
+      T* vt = reinterpret_cast<T*>(&v);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        store_elem(vt, e,
+                   __builtin_bit_cast(f32x4, q[u][e / 4])[e % 4] * inv *
+                       load_elem(gt, e));
+      *reinterpret_cast<u32x4*>(ob + (int64_t)s * 1024) = v;
+    }
+  }
+}
+
 template <typename T>
 hipError_t embed_t(int B, int K, int D, int V, int mask_id, int pass,
                    int n_cap, const int32_t* anchor, const int32_t* block_tokens,
@@ -145,15 +222,28 @@ hipError_t launch_embed(bool bf16, int B, int K, int D, int V, int mask_id,
 hipError_t launch_rmsnorm(bool bf16, int rows, int D, const float* x,
                           const int32_t* rowmap, const void* gain, float eps,
                           void* out, hipStream_t s) {
-  const int padded = (rows + 15) / 16 * 16;
+  const int tiles = (rows + 15) / 16;
+  if (tiles < 32 && D <= 256 * 4 * (bf16 ? 8 : 4)) {
+    if (bf16)
+      hipLaunchKernelGGL(rmsnorm_row_kernel<bf16_t>, dim3(tiles * 16), dim3(256),
+                         0, s, rows, D, x, rowmap,
+                         static_cast<const bf16_t*>(gain), eps,
+                         static_cast<bf16_t*>(out));
+    else
+      hipLaunchKernelGGL(rmsnorm_row_kernel<float>, dim3(tiles * 16), dim3(256),
+                         0, s, rows, D, x, rowmap,
+                         static_cast<const float*>(gain), eps,
+                         static_cast<float*>(out));
+    return hipGetLastError();
+  }
   if (bf16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(padded), dim3(256), 0, s,
-                       rows, D, x, rowmap, static_cast<const bf16_t*>(gain),
+    hipLaunchKernelGGL(rmsnorm_tile_kernel<bf16_t>, dim3(tiles), dim3(1024), 0,
+                       s, rows, D, x, rowmap, static_cast<const bf16_t*>(gain),
                        eps, static_cast<bf16_t*>(out));
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(padded), dim3(256), 0, s,
-                       rows, D, x, rowmap, static_cast<const float*>(gain), eps,
-                       static_cast<float*>(out));
+    hipLaunchKernelGGL(rmsnorm_tile_kernel<float>, dim3(tiles), dim3(1024), 0,
+                       s, rows, D, x, rowmap, static_cast<const float*>(gain),
+                       eps, static_cast<float*>(out));
   return hipGetLastError();
 }
 

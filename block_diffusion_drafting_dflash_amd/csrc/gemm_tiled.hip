@@ -24,6 +24,21 @@ namespace dflash {
 
 namespace {
 
+// Staging loads of the main loop are issued as inline assembly so that the
+// compiler's wait insertion (which drains every outstanding load at the loop
+// header) does not see them; the loop waits for exactly the loads it needs
+// with vm_wait<N>, tied to the register it is about to read.  Every such
+// load is waited for (vm_drain) before the registers can be reused.
+__device__ __forceinline__ u32x4 stage_load(const char* p) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void vm_wait(u32x4& v) {
+  asm volatile("s_waitcnt vmcnt(%1)" : "+v"(v) : "n"(N));
+}
+
 // Epilogue of one 32 x 32 accumulator tile: rows row0.., 16-column tiles
 // ctile and ctile + 1 (lanes 16-31 of each half-wave take the second).
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, int row0,
@@ -86,17 +101,28 @@ struct Tiled {
   static_assert(NF % NW == 0, "fragments must split evenly over the waves");
 };
 
-// One LDS stage = SK contraction steps: publish the staged fragments in LDS,
-// refill the same registers PD stages ahead, then multiply from LDS.  The
-// refill is unconditional (clamped to the last stage) and pinned next to
-// the publish, so the loop is straight-line code.
-template <int TM, int TN, int WM, int WN, int SK>
+// One LDS stage = SK contraction steps: wait for this stage's staged
+// fragments (loaded PD stages ago: the PD - 1 later stages' loads may still
+// be in flight), publish them in LDS, refill the same registers PD stages
+// ahead, then multiply from LDS.  The refill is unconditional (clamped to
+// the last stage), so the loop is straight-line code.
+template <int I, int LIM, int AHEAD>
+__device__ __forceinline__ void stage_wait(u32x4* st) {
+  if constexpr (I < LIM) {
+    vm_wait<AHEAD + LIM - 1 - I>(st[I]);
+    stage_wait<I + 1, LIM, AHEAD>(st);
+  }
+}
+
+template <int TM, int TN, int WM, int WN, int SK, int PD>
 __device__ __forceinline__ void tiled_stage(
     int next, u32x4 (&st)[Tiled<TM, TN, WM, WN>::LPW * SK],
     const char* const (&src)[Tiled<TM, TN, WM, WN>::LPW], u32x4* buf,
     int wave, int lane, int a_off, int w_off, f32x16 (&acc)[TM][TN]) {
   using C = Tiled<TM, TN, WM, WN>;
+  constexpr int NL = C::LPW * SK;  // loads per stage per lane
   __builtin_amdgcn_sched_barrier(0);
+  stage_wait<0, NL, (PD - 1) * NL>(st);
 #pragma unroll
   for (int k = 0; k < SK; ++k)
 #pragma unroll
@@ -107,7 +133,8 @@ __device__ __forceinline__ void tiled_stage(
   for (int k = 0; k < SK; ++k)
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i)
-      st[k * C::LPW + i] = load16(src[i] + ((int64_t)next * SK + k) * 1024);
+      st[k * C::LPW + i] =
+          stage_load(src[i] + ((int64_t)next * SK + k) * 1024);
   __builtin_amdgcn_sched_barrier(0);
   // step k, half h: contraction 32k + 16h .. + 16
 #pragma unroll
@@ -181,17 +208,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(GemmArgs p,
     for (int kk = 0; kk < SK; ++kk)
 #pragma unroll
       for (int i = 0; i < C::LPW; ++i)
-        st[j][kk * C::LPW + i] =
-            load16(src[i] + ((int64_t)min(j, nstages - 1) * SK + kk) * 1024);
+        st[j][kk * C::LPW + i] = stage_load(
+            src[i] + ((int64_t)min(j, nstages - 1) * SK + kk) * 1024);
   // nstages is a multiple of PD; LDS buffers alternate by stage parity
   for (int s = 0; s < nstages; s += PD) {
 #pragma unroll
     for (int j = 0; j < PD; ++j)
-      tiled_stage<TM, TN, WM, WN, SK>(
+      tiled_stage<TM, TN, WM, WN, SK, PD>(
           min(s + j + PD, nstages - 1), st[j], src,
           lds + ((s + j) & 1) * SK * C::NF * 64, wave, lane, a_off, w_off,
           acc);
   }
+  // the last PD stages' refills (clamped repeats) are still in flight
+#pragma unroll
+  for (int j = 0; j < PD; ++j)
+#pragma unroll
+    for (int i = 0; i < C::LPW * SK; ++i) vm_wait<0>(st[j][i]);
 
   // One copy of the epilogue code in a rolled loop; each tile is selected
   // out of the accumulators with compile-time indices (a dynamic index would
