@@ -17,6 +17,24 @@ namespace dflash {
 namespace {
 
 constexpr int kKeyTile = 64;
+
+// Accuracy of P.V: P is split into DFLASH_ATTN_PSPLIT bf16 parts (2: ~16
+// significant bits, 3: exact fp32); each 64-key tile's P.V is summed by the
+// MFMAs in fp32 and added to running accumulators of type float, or double
+// with DFLASH_ATTN_F64.  Rounding P to a single bf16 part measurably moves
+// the drafted logits; more than two parts or float64 accumulation does not
+// (the bf16 rounding of the attention output dominates).
+#ifndef DFLASH_ATTN_PSPLIT
+#define DFLASH_ATTN_PSPLIT 2
+#endif
+#ifndef DFLASH_ATTN_F64
+#define DFLASH_ATTN_F64 0
+#endif
+#if DFLASH_ATTN_F64
+using attn_acc_t = double;
+#else
+using attn_acc_t = float;
+#endif
 constexpr int kVPad = 4;  // elements of padding per transposed V row
 
 // Each thread carries NP 16-byte pieces of K and of V for one 64-key tile;
@@ -88,10 +106,14 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) qf[dc] = load16(qrow + dc * KC * SZ);
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[D / 16];
+  // running max (log2 domain), softmax numerator o and denominator l
+  float m_run = -INFINITY;
+  attn_acc_t l_run = 0;
+  attn_acc_t o[D / 16][4];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[dt][j] = 0;
 
   for (int kt = k0; kt < k1; kt += kKeyTile) {
     const int n_valid = min(kKeyTile, k1 - kt);
@@ -135,37 +157,58 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+    // the same factor scales numerator and denominator, so its rounding
+    // cancels in o = numerator / denominator
+    const attn_acc_t alpha = (attn_acc_t)exp2f(m_run - m_new);
+    attn_acc_t lt = 0;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float pv = exp2f(s[mt][j] - m_new);
         s[mt][j] = pv;
-        l_run += pv;
+        lt += (attn_acc_t)pv;
       }
+    l_run = l_run * alpha + lt;
     m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[dt][j] *= alpha;
+    f32x4 ot[D / 16];  // this tile's P.V (fp32)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) ot[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // O^T += V^T P^T; contraction slots of lane group g hold the keys that
     // this lane's S^T registers hold
     if constexpr (SZ == 2) {
+      // P = p1 + p2 (+ p3) in bf16 parts of 8 significant bits each
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        u32x4 bfrag;
-        bfrag.x = f32_to_bf16(s[2 * cc][0]) | (f32_to_bf16(s[2 * cc][1]) << 16);
-        bfrag.y = f32_to_bf16(s[2 * cc][2]) | (f32_to_bf16(s[2 * cc][3]) << 16);
-        bfrag.z = f32_to_bf16(s[2 * cc + 1][0]) | (f32_to_bf16(s[2 * cc + 1][1]) << 16);
-        bfrag.w = f32_to_bf16(s[2 * cc + 1][2]) | (f32_to_bf16(s[2 * cc + 1][3]) << 16);
+        constexpr int NP3 = DFLASH_ATTN_PSPLIT;
+        uint32_t pp[NP3][8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float rem = s[2 * cc + e / 4][e % 4];
+#pragma unroll
+          for (int t = 0; t < NP3; ++t) {
+            pp[t][e] = f32_to_bf16(rem);
+            rem -= bf16_to_f32(pp[t][e]);
+          }
+        }
+        u32x4 bp[NP3];
+#pragma unroll
+        for (int t = 0; t < NP3; ++t)
+          bp[t] = u32x4{pp[t][0] | (pp[t][1] << 16), pp[t][2] | (pp[t][3] << 16),
+                        pp[t][4] | (pp[t][5] << 16), pp[t][6] | (pp[t][7] << 16)};
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
           const char* vrow = vt + (16 * dt + r) * VROWB;
           const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + (32 * cc + 4 * g) * SZ);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (32 * cc + 16 + 4 * g) * SZ);
           const u32x4 afrag = {lo.x, lo.y, hi.x, hi.y};
-          mma16(o[dt], afrag, bfrag, T());
+#pragma unroll
+          for (int t = 0; t < NP3; ++t) mma16(ot[dt], afrag, bp[t], T());
         }
       }
     } else {
@@ -177,13 +220,17 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
         for (int dt = 0; dt < D / 16; ++dt) {
           const char* vrow = vt + (16 * dt + r) * VROWB;
           const u32x4 afrag = *reinterpret_cast<const u32x4*>(vrow + (16 * cc + 4 * g) * SZ);
-          mma16(o[dt], afrag, bfrag, T());
+          mma16(ot[dt], afrag, bfrag, T());
         }
       }
     }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[dt][j] += (attn_acc_t)ot[dt][j];
   }
 
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  attn_acc_t l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   // partials are chunk-major within (sequence, query head, query):
   // part_o[((b*Hq + hq)*K + i)*nch + c][D], part_ml[... same index][2]
@@ -191,9 +238,10 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
   float* po = p.part_o + base * D;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
-    *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt];
+    *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) =
+        f32x4{(float)o[dt][0], (float)o[dt][1], (float)o[dt][2], (float)o[dt][3]};
   if (g == 0)
-    *reinterpret_cast<float2*>(p.part_ml + base * 2) = float2{m_run, l_tot};
+    *reinterpret_cast<float2*>(p.part_ml + base * 2) = float2{m_run, (float)l_tot};
 }
 
 // o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the sequence's
@@ -222,13 +270,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
   float M = -INFINITY;
   for (int c = lane; c < nc; c += 64) M = fmaxf(M, ml[c].x);
   M = warp_max(M);
-  float ls = 0.f;
-  for (int c = lane; c < nc; c += 64) ls += exp2f(ml[c].x - M) * ml[c].y;
-  ls = warp_sum(ls);
-
-  float acc[DPL];
+  double ls = 0.0;
+  for (int c = lane; c < nc; c += 64)
+    ls += (double)exp2f(ml[c].x - M) * (double)ml[c].y;
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
+
+  double acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.0;
   const float* ob = p.part_o + base * D + lane * DPL;
   for (int c0 = 0; c0 < nc; c0 += kMergeBatch) {
     float v[kMergeBatch][DPL], w[kMergeBatch];
@@ -247,14 +297,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] += w[u] * v[u][e];
+      for (int e = 0; e < DPL; ++e) acc[e] += (double)w[u] * (double)v[u][e];
   }
-  const float inv = 1.f / ls;
+  const double inv = 1.0 / ls;
   const int row = b * p.K + i, Kd = p.Hq * D, d0 = lane * DPL;
   T* dst = reinterpret_cast<T*>(static_cast<char*>(p.o) +
                                 packed_offset<T>(row, hq * D + d0, Kd));
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) store_elem(dst, e, acc[e] * inv);
+  for (int e = 0; e < DPL; ++e) store_elem(dst, e, (float)(acc[e] * inv));
 }
 
 template <typename T, int D, int G>
@@ -284,7 +334,8 @@ hipError_t attn_g(int B, const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attention(bool bf16, int d, int B, const AttnArgs& a,
                             hipStream_t s) {
-  if (d == 128) return bf16 ? attn_g<bf16_t, 128>(B, a, s) : attn_g<float, 128>(B, a, s);
+  // fp32 drafters have head_dim 64 (checked at create)
+  if (d == 128) return bf16 ? attn_g<bf16_t, 128>(B, a, s) : hipErrorInvalidValue;
   if (d == 64) return bf16 ? attn_g<bf16_t, 64>(B, a, s) : attn_g<float, 64>(B, a, s);
   return hipErrorInvalidValue;
 }

@@ -42,6 +42,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Round a float64 value to the nearest bf16, ties to even, in one rounding:
+// float64 -> float32 rounded to odd (toward zero, then the last bit set if
+// anything was discarded), then to bf16 nearest-even; the intermediate has
+// more than two extra bits, so the result equals a direct rounding.
+__device__ __forceinline__ uint32_t f64_to_bf16(double v) {
+  const float f = __double2float_rz(v);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != v) u |= 1u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
 __device__ __forceinline__ float load_elem(const bf16_t* p, int64_t i) {
   return bf16_to_f32(p[i].bits);
 }
@@ -53,6 +65,12 @@ __device__ __forceinline__ void store_elem(bf16_t* p, int64_t i, float v) {
 }
 __device__ __forceinline__ void store_elem(float* p, int64_t i, float v) {
   p[i] = v;
+}
+__device__ __forceinline__ void store_elem(bf16_t* p, int64_t i, double v) {
+  p[i].bits = (uint16_t)f64_to_bf16(v);
+}
+__device__ __forceinline__ void store_elem(float* p, int64_t i, double v) {
+  p[i] = (float)v;
 }
 // Value after rounding to the storage type (what a store then load returns).
 __device__ __forceinline__ float round_to(bf16_t, float v) {
@@ -109,13 +127,14 @@ __device__ __forceinline__ float warp_max(float v) {
 }
 
 // Block-wide sum for blockDim.x == 64 * nwaves (nwaves <= 16), fixed order.
-template <int NWAVES>
-__device__ __forceinline__ float block_sum(float v, float* scratch) {
-  v = warp_sum(v);
+template <int NWAVES, typename F>
+__device__ __forceinline__ F block_sum(F v, F* scratch) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) scratch[w] = v;
   __syncthreads();
-  float t = 0.f;
+  F t = 0;
 #pragma unroll
   for (int i = 0; i < NWAVES; ++i) t += scratch[i];
   __syncthreads();

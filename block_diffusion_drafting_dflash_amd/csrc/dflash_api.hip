@@ -69,7 +69,7 @@ struct dflash_ctx {
   // workspace
   void* ws = nullptr;
   size_t attn_floats = 0, lm_part_count = 0;
-  float2* rope = nullptr;
+  double2* rope = nullptr;   // cos, sin of pos * theta^(-2i/d) [P][d/2]
   float* u = nullptr;        // fused target features before RMSNorm [TI][D]
   void* cond = nullptr;      // H_cond, packed [TI16][D]
   void* hpk = nullptr;       // target hidden states, packed [TI16][n_t * D_t]
@@ -404,7 +404,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
 
   struct Item { void** p; size_t bytes; };
   std::vector<Item> items = {
-      {(void**)&x->rope, (size_t)x->P * (d / 2) * sizeof(float2)},
+      {(void**)&x->rope, (size_t)x->P * (d / 2) * sizeof(double2)},
       {(void**)&x->u, (size_t)TI * D * sizeof(float)},
       {&x->cond, (size_t)TI16 * D * esz},
       {&x->hpk, (size_t)TI16 * c.num_target_layers * c.target_hidden * esz},
@@ -437,15 +437,14 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
     }
   }
   // RoPE table: angle pos * theta^(-2i/d) evaluated in double precision.
-  std::vector<float2> tab((size_t)x->P * (d / 2));
+  std::vector<double2> tab((size_t)x->P * (d / 2));
   for (int pos = 0; pos < x->P; ++pos)
     for (int i = 0; i < d / 2; ++i) {
       const double inv = std::pow((double)c.rope_theta, -2.0 * i / d);
       const double ang = (double)pos * inv;
-      tab[(size_t)pos * (d / 2) + i] = make_float2((float)std::cos(ang),
-                                                   (float)std::sin(ang));
+      tab[(size_t)pos * (d / 2) + i] = make_double2(std::cos(ang), std::sin(ang));
     }
-  if (hipMemcpy(x->rope, tab.data(), tab.size() * sizeof(float2),
+  if (hipMemcpy(x->rope, tab.data(), tab.size() * sizeof(double2),
                 hipMemcpyHostToDevice) != hipSuccess ||
       hipMemset(x->err, 0, 256) != hipSuccess ||
       hipMemset(x->committed, 0, (size_t)R * sizeof(int32_t)) != hipSuccess) {

@@ -64,7 +64,8 @@ __global__ __launch_bounds__(256) void embed_kernel(
   for (int c = threadIdx.x; c < D; c += 256) xr[c] = load_elem(src, c);
 }
 
-// out[row] = RMSNorm(x[src]) * g written packed, src = rowmap ? rowmap[row]
+// out[row] = RMSNorm(x[src]) * g written packed (statistics and scaling in
+// float64, one rounding to the storage type), src = rowmap ? rowmap[row]
 // : row; rows without a source (padding to a multiple of 16, unmapped LM-head
 // rows) are written as zeros.  One workgroup per row, one thread per 16-byte
 // chunk: the fastest form up to a few hundred rows.
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(int rows, int D,
                                                           const T* g, float eps,
                                                           T* out) {
   constexpr int E = Storage<T>::E;
-  __shared__ float scratch[4];
+  __shared__ double scratch[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int src = row < rows ? (rowmap ? rowmap[row] : row) : -1;
   char* ob = reinterpret_cast<char*>(out);
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(int rows, int D,
   }
   const float* xr = x + (int64_t)src * D;
   float v[kNormChunks][E];
-  float ss = 0.f;
+  double ss = 0.0;
 #pragma unroll
   for (int ci = 0; ci < kNormChunks; ++ci) {
     const int c = tid + ci * 256;
@@ -101,12 +102,13 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(int rows, int D,
         v[ci][e + 1] = q.y;
         v[ci][e + 2] = q.z;
         v[ci][e + 3] = q.w;
-        ss += q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w;
+        ss += (double)q.x * q.x + (double)q.y * q.y + (double)q.z * q.z +
+              (double)q.w * q.w;
       }
     }
   }
-  const float tot = block_sum<4>(ss, scratch);
-  const float inv = 1.f / sqrtf(tot / (float)D + eps);
+  const double tot = block_sum<4>(ss, scratch);
+  const double inv = 1.0 / sqrt(tot / (double)D + (double)eps);
 #pragma unroll
   for (int ci = 0; ci < kNormChunks; ++ci) {
     const int c = tid + ci * 256;
@@ -114,7 +116,8 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(int rows, int D,
       T* dst = reinterpret_cast<T*>(ob + packed_offset<T>(row, c * E, D));
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        store_elem(dst, e, v[ci][e] * inv * load_elem(g, c * E + e));
+        store_elem(dst, e,
+                   (double)v[ci][e] * inv * (double)load_elem(g, c * E + e));
     }
   }
 }
@@ -134,31 +137,33 @@ __global__ __launch_bounds__(1024) void rmsnorm_tile_kernel(int rows, int D,
                                                        const T* g, float eps,
                                                        T* out) {
   constexpr int E = Storage<T>::E, KC = Storage<T>::KC;
-  __shared__ float inv_s[16];
+  __shared__ double inv_s[16];
   __shared__ int src_s[16];
   const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   {
     const int row = t * 16 + wave;
     const int src = row < rows ? (rowmap ? rowmap[row] : row) : -1;
-    float ss = 0.f;
+    double ss = 0.0;
     if (src >= 0) {
       const float* xr = x + (int64_t)src * D;
 #pragma unroll 8
       for (int c = lane * 4; c < D; c += 256) {
         const f32x4 q = __builtin_bit_cast(f32x4, load16(xr + c));
-        ss += q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w;
+        ss += (double)q.x * q.x + (double)q.y * q.y + (double)q.z * q.z +
+              (double)q.w * q.w;
       }
     }
-    ss = warp_sum(ss);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
     if (lane == 0) {
-      inv_s[wave] = 1.f / sqrtf(ss / (float)D + eps);
+      inv_s[wave] = 1.0 / sqrt(ss / (double)D + (double)eps);
       src_s[wave] = src;
     }
   }
   __syncthreads();
   const int r = lane & 15, grp = lane >> 4;
   const int src = src_s[r];
-  const float inv = inv_s[r];
+  const double inv = inv_s[r];
   const int nsteps = D / KC;
   char* ob = reinterpret_cast<char*>(out) + ((int64_t)t * nsteps * 64 + lane) * 16;
   if (src < 0) {  // lanes of rows without a source write zeros
@@ -188,8 +193,8 @@ __global__ __launch_bounds__(1024) void rmsnorm_tile_kernel(int rows, int D,
 #pragma unroll
       for (int e = 0; e < E; ++e)
         store_elem(vt, e,
-                   __builtin_bit_cast(f32x4, q[u][e / 4])[e % 4] * inv *
-                       load_elem(gt, e));
+                   (double)__builtin_bit_cast(f32x4, q[u][e / 4])[e % 4] * inv *
+                       (double)load_elem(gt, e));
       *reinterpret_cast<u32x4*>(ob + (int64_t)s * 1024) = v;
     }
   }

@@ -31,10 +31,16 @@ namespace {
 #define DFLASH_LM_U 8
 #endif
 
-// acc[m] over this wave's share of the contraction.
-template <typename T, int MT, int AP, int W, int U>
+
+// acc[m] over this wave's share of the contraction.  With F64 each MFMA
+// step (32 contraction elements) is summed in fp32 from zero and added to a
+// float64 accumulator: the projections feed bf16-rounded activations of the
+// next step, where fp32 accumulation error over thousands of terms flips
+// roundings that then spread through the layer.  The LM head's logits feed
+// nothing further and accumulate in fp32.
+template <typename T, int MT, int AP, int W, int U, bool F64>
 __device__ __forceinline__ void gemm_core(const GemmArgs& p, int tile,
-                                          int m_base, f32x4 (&acc)[MT]) {
+                                          int m_base, double (&acc)[MT][4]) {
   constexpr int E = Storage<T>::E, KC = Storage<T>::KC, SZ = sizeof(T);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -42,7 +48,16 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& p, int tile,
   const char* wbase =
       static_cast<const char*>(p.w) + ((int64_t)tile * nsteps * 64 + lane) * 16;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[m][j] = 0.0;
+  auto fold = [&](int m, const f32x4& t) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[m][j] += (double)t[j];
+  };
+  f32x4 acc32[MT];  // without F64: fp32 across all steps
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc32[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // A operand addressing: packed fragments, or row-major segments
   const int sps = AP ? nsteps : p.a_seg_k / KC;  // steps per segment
@@ -79,36 +94,56 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& p, int tile,
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) mma16(acc[m], af[u][m], bf[u], T());
+        for (int m = 0; m < MT; ++m) {
+          if constexpr (F64) {
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+            mma16(t, af[u][m], bf[u], T());
+            fold(m, t);
+          } else {
+            mma16(acc32[m], af[u][m], bf[u], T());
+          }
+        }
     }
     for (; s < s1; s += W) {
       const u32x4 bf = load16(wbase + (int64_t)s * 1024);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) mma16(acc[m], load16(a_at(m, s)), bf, T());
+      for (int m = 0; m < MT; ++m) {
+        if constexpr (F64) {
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+          mma16(t, load16(a_at(m, s)), bf, T());
+          fold(m, t);
+        } else {
+          mma16(acc32[m], load16(a_at(m, s)), bf, T());
+        }
+      }
     }
+  }
+  if constexpr (!F64) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) fold(m, acc32[m]);
   }
 }
 
-// Sums the waves' tiles in wave order; red[(m*4 + j)*64 + lane] then holds
-// row 16m + 4(lane/16) + j, tile column lane % 16.
+// Sums the waves' tiles in wave order (float64, one row tile at a time
+// through redd); red[(m*4 + j)*64 + lane] then holds row 16m + 4(lane/16) + j,
+// tile column lane % 16.
 template <int MT, int W>
-__device__ __forceinline__ void reduce_waves(const f32x4 (&acc)[MT],
-                                             float* red) {
-  constexpr int S = MT * 256;
+__device__ __forceinline__ void reduce_waves(const double (&acc)[MT][4],
+                                             double* redd, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+  for (int m = 0; m < MT; ++m) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      red[(wave * MT + m) * 256 + j * 64 + lane] = acc[m][j];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < S; idx += W * 64) {
-    float v = red[idx];
+    for (int j = 0; j < 4; ++j) redd[wave * 256 + j * 64 + lane] = acc[m][j];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 256; idx += W * 64) {
+      double v = redd[idx];
 #pragma unroll
-    for (int w = 1; w < W; ++w) v += red[w * S + idx];
-    red[idx] = v;
+      for (int w = 1; w < W; ++w) v += redd[w * 256 + idx];
+      red[m * 256 + idx] = (float)v;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
 template <typename T, int MT, int W>
@@ -162,13 +197,14 @@ __device__ void apply_epilogue(const GemmArgs& p, int tile, int m_base,
   }
 }
 
-template <typename T, int MT, int AP, int W, int U>
+template <typename T, int MT, int AP, int W, int U, bool F64>
 __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmArgs p) {
-  __shared__ float red[W * MT * 256];
+  __shared__ double redd[W * 256];
+  __shared__ float red[MT * 256];
   const int tile = blockIdx.x, m_base = blockIdx.y * 16 * MT;
-  f32x4 acc[MT];
-  gemm_core<T, MT, AP, W, U>(p, tile, m_base, acc);
-  reduce_waves<MT, W>(acc, red);
+  double acc[MT][4];
+  gemm_core<T, MT, AP, W, U, F64>(p, tile, m_base, acc);
+  reduce_waves<MT, W>(acc, redd, red);
   apply_epilogue<T, MT, W>(p, tile, m_base, red);
 }
 
@@ -197,15 +233,18 @@ template <typename T, int AP>
 hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream_t s) {
   dim3 grid(pl.gx, pl.gy, 1), block(pl.waves * 64);
   if (pl.MT == 1 && a.ep == EP_TOP2)
-    hipLaunchKernelGGL((gemm_kernel<T, 1, AP, DFLASH_LM_W, DFLASH_LM_U>), grid,
-                       block, 0, s, a);
-  else if (pl.MT == 1)
-    hipLaunchKernelGGL((gemm_kernel<T, 1, AP, DFLASH_GEMM_W, DFLASH_GEMM_U>),
+    hipLaunchKernelGGL((gemm_kernel<T, 1, AP, DFLASH_LM_W, DFLASH_LM_U, false>),
                        grid, block, 0, s, a);
+  else if (pl.MT == 1)
+    hipLaunchKernelGGL(
+        (gemm_kernel<T, 1, AP, DFLASH_GEMM_W, DFLASH_GEMM_U, true>), grid,
+        block, 0, s, a);
   else if (pl.MT == 2)
-    hipLaunchKernelGGL((gemm_kernel<T, 2, AP, 4, 8>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<T, 2, AP, 4, 8, true>), grid, block, 0, s,
+                       a);
   else if (pl.MT == 4)
-    hipLaunchKernelGGL((gemm_kernel<T, 4, AP, 16, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<T, 4, AP, 16, 2, true>), grid, block, 0,
+                       s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -7,8 +7,10 @@
 
 namespace dflash {
 
-__device__ __forceinline__ void rope_pair(float a, float b, float2 cs,
-                                          float& ra, float& rb) {
+// Rotation of one (x_i, x_{i+d/2}) pair, in float64 so that the result is
+// rounded once, to the storage type.
+__device__ __forceinline__ void rope_pair(double a, double b, double2 cs,
+                                          double& ra, double& rb) {
   ra = a * cs.x - b * cs.y;
   rb = b * cs.x + a * cs.y;
 }
@@ -25,7 +27,8 @@ __device__ __forceinline__ void pair_epilogue(const GemmArgs& p, int row,
   if (p.ep == EP_SWIGLU) {
     T* act = static_cast<T*>(p.out_t);
     const int64_t off = packed_offset<T>(row, col, p.pair_off) / sizeof(T);
-    store_elem(act, off, a / (1.f + __expf(-a)) * b);
+    const double da = a;
+    store_elem(act, off, da / (1.0 + exp(-da)) * (double)b);
     return;
   }
   const int half = p.d / 2;
@@ -38,8 +41,8 @@ __device__ __forceinline__ void pair_epilogue(const GemmArgs& p, int row,
       L = min(max(L, 0), p.max_len);
     }
     const int pos = L + row % p.K;
-    const float2 cs = p.rope[(int64_t)pos * half + i];
-    float ra, rb;
+    const double2 cs = p.rope[(int64_t)pos * half + i];
+    double ra, rb;
     T* dst;
     if (head < p.Hq) {
       dst = static_cast<T*>(p.out_t) + (int64_t)row * p.Hq * p.d + head * p.d;
@@ -77,7 +80,7 @@ __device__ __forceinline__ void pair_epilogue(const GemmArgs& p, int row,
   const int64_t plane = (int64_t)p.max_batch * p.Hkv * p.P * p.d;
   T* dst = static_cast<T*>(p.kv) + (2 * l + (is_k ? 0 : 1)) * plane +
            (((int64_t)seq * p.Hkv + h) * p.P + pos) * p.d;
-  float ra = a, rb = b;
+  double ra = a, rb = b;
   if (is_k) rope_pair(a, b, p.rope[(int64_t)pos * half + i], ra, rb);
   store_elem(dst, i, ra);
   store_elem(dst, i + half, rb);

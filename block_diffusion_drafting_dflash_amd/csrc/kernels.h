@@ -76,7 +76,7 @@ struct GemmArgs {
   int64_t ldo;
   void* out_t;      // EP_QKV: q [M][Hq*d]; EP_SWIGLU: packed act
   void* kv;         // EP_QKV: this layer's cache; EP_KV: the whole cache
-  const float2* rope;
+  const double2* rope;     // cos, sin [P][d/2]
   const int32_t* ctx_len;  // EP_QKV
   int max_len, K;
   const int32_t* row_seq;  // EP_KV

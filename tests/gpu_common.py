@@ -80,14 +80,16 @@ def oracle_inject_sequence(model: OracleModel, wl, hid_chunks, pos):
     return inject_rows(model, hid_chunks, pos)
 
 
-def compare_draft(wl, gpu_res, oracle_res, rows_per_seq=None):
+def compare_draft(wl, gpu_res, oracle_res, rows_per_seq=None, tol=None,
+                  margin_min=None):
     """Token / logit / confidence parity for one pass.
 
     gpu_res: dict of numpy arrays draft [B, K-1], conf, margin, logits
     [B, K-1, V] (rows computed in this pass); oracle_res: list of
     draft_sequence results.  Returns counts of compared / excluded tokens.
     """
-    tol = LOGIT_TOL[wl.dtype]
+    tol = LOGIT_TOL[wl.dtype] if tol is None else tol
+    margin_min = MARGIN_MIN if margin_min is None else margin_min
     compared = excluded = 0
     max_dl = 0.0
     for b, o in enumerate(oracle_res):
@@ -99,7 +101,7 @@ def compare_draft(wl, gpu_res, oracle_res, rows_per_seq=None):
         assert dl <= tol, f"seq {b}: logits max-abs diff {dl:.3e} > {tol}"
         for j, i in enumerate(rows):
             m = o["pass_margin"][0][int(i)]
-            if m > MARGIN_MIN:
+            if m > margin_min:
                 compared += 1
                 assert gpu_res["draft"][b, i - 1] == o["pass_token"][0][int(i)], (
                     f"seq {b} pos {i}: token {gpu_res['draft'][b, i - 1]} vs "
