@@ -249,8 +249,8 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
 // One wave per (sequence, query head, block query): lane c reads chunk c's
 // (m, l) so the weights come from wave reductions (fixed butterfly order);
 // the partial outputs are then summed in chunk order, lane owning D/64
-// consecutive channels, with kMergeBatch independent loads in flight.
-constexpr int kMergeBatch = 16;
+// consecutive channels, with kMergeBatch chunks' loads in flight.
+constexpr int kMergeBatch = 32;
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
@@ -265,13 +265,33 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
   const int nc = (L + p.K + p.chunk - 1) / p.chunk;
   const int64_t base = (int64_t)wrow * p.nch;  // == ((b*Hq + hq)*K + i)*nch
   const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + base;
+  const float* ob = p.part_o + base * D + lane * DPL;
 
-  // chunk weights: lanes c, c + 64, ... (nc <= nch, any size)
-  float M = -INFINITY;
-  for (int c = lane; c < nc; c += 64) M = fmaxf(M, ml[c].x);
+  // the first batch of partial outputs does not depend on the weights:
+  // issue its loads before the reductions
+  float v[kMergeBatch][DPL];
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e)
+        v[u][e] = c0 + u < nc ? ob[(int64_t)(c0 + u) * D + e] : 0.f;
+  };
+  load_batch(0);
+  // chunk weights 2^(m_c - M): lane c holds chunk c (c < 64); further
+  // chunks, if any, are read again where needed
+  float m_l = -INFINITY, l_l = 0.f;
+  if (lane < nc) {
+    const float2 t = ml[lane];
+    m_l = t.x;
+    l_l = t.y;
+  }
+  float M = m_l;
+  for (int c = lane + 64; c < nc; c += 64) M = fmaxf(M, ml[c].x);
   M = warp_max(M);
-  double ls = 0.0;
-  for (int c = lane; c < nc; c += 64)
+  const float w_l = lane < nc ? exp2f(m_l - M) : 0.f;
+  double ls = (double)w_l * (double)l_l;
+  for (int c = lane + 64; c < nc; c += 64)
     ls += (double)exp2f(ml[c].x - M) * (double)ml[c].y;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
@@ -279,32 +299,24 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
   double acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0;
-  const float* ob = p.part_o + base * D + lane * DPL;
   for (int c0 = 0; c0 < nc; c0 += kMergeBatch) {
-    float v[kMergeBatch][DPL], w[kMergeBatch];
+    if (c0 > 0) load_batch(c0);
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const int c = c0 + u;
-      w[u] = 0.f;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) v[u][e] = 0.f;
+      const int c = c0 + u;  // uniform across the wave
       if (c < nc) {
-        w[u] = exp2f(ml[c].x - M);
+        const float w = c < 64 ? __shfl(w_l, c, 64) : exp2f(ml[c].x - M);
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) v[u][e] = ob[(int64_t)c * D + e];
+        for (int e = 0; e < DPL; ++e) acc[e] += (double)w * (double)v[u][e];
       }
     }
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] += (double)w[u] * (double)v[u][e];
   }
   const double inv = 1.0 / ls;
   const int row = b * p.K + i, Kd = p.Hq * D, d0 = lane * DPL;
   T* dst = reinterpret_cast<T*>(static_cast<char*>(p.o) +
                                 packed_offset<T>(row, hq * D + d0, Kd));
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) store_elem(dst, e, (float)(acc[e] * inv));
+  for (int e = 0; e < DPL; ++e) store_elem(dst, e, acc[e] * inv);
 }
 
 template <typename T, int D, int G>

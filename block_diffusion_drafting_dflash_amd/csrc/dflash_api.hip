@@ -192,17 +192,23 @@ int attn_chunk(int B, int Hkv, int max_keys, int num_cu) {
 // stream: wide workgroups over one 16-column tile (gemm.hip).  Beyond that
 // it is a dense contraction: MFMA tiles staged through LDS (gemm_tiled.hip,
 // bf16 only); a row-major activation operand is packed first.
+#ifndef DFLASH_PACK_ROWMAJOR
+#define DFLASH_PACK_ROWMAJOR 1
+#endif
 dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
                        int kind = DFLASH_TIME_GEMM) {
   a.err = c->err;
   const bool lm = a.ep == EP_TOP2;
-  if (c->bf16 && (a.M > 64 || (lm && a.M > 16))) {
-    if (!a.a_packed) {
-      DF_HIP(launch_pack_act(true, a, c->hpk, s));
-      a.a_ptr[0] = c->hpk;
-      a.a_packed = 1;
-      a.a_seg_k = a.Kd;
-    }
+  const bool tiled = c->bf16 && (a.M > 64 || (lm && a.M > 16));
+  if (!a.a_packed && (tiled || DFLASH_PACK_ROWMAJOR)) {
+    // row-major activations (the target hidden states): pack once, so every
+    // workgroup's operand loads are whole 1 KiB fragments
+    DF_HIP(launch_pack_act(c->bf16, a, c->hpk, s));
+    a.a_ptr[0] = c->hpk;
+    a.a_packed = 1;
+    a.a_seg_k = a.Kd;
+  }
+  if (tiled) {
     TimedLaunch tl(c, kind, s);
     DF_HIP(launch_gemm_tiled(true, plan_tiled(a.M, a.N), a, s));
     return DFLASH_OK;
@@ -640,15 +646,20 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
   for (int pass = 0; pass < num_passes; ++pass) {
     const int n_cap = (K - 1) - pass * commit_per_pass;
     const bool last = pass == num_passes - 1;
+    // up to 512 rows the embedding kernel also writes the first layer's
+    // normalised input (one row per workgroup is the faster form there)
+    const bool fuse_norm = R <= 512;
     DF_HIP(launch_embed(bf, batch, K, D, V, c.mask_token_id, pass, n_cap,
                         anchor, block_tokens, bs, ctx->embed, ctx->x,
-                        draft_tokens, s));
+                        draft_tokens, fuse_norm ? ctx->attn_norm[0] : nullptr,
+                        c.rms_eps, ctx->h, s));
     for (int l = 0; l < c.num_layers; ++l) {
       char* kvl = static_cast<char*>(kv_cache) + l * layer_elems * ctx->esz;
       // q, k, v of RMSNorm(x); RoPE; q -> q buffer, block k, v -> cache
       // positions L_b + i
-      DF_HIP(launch_rmsnorm(bf, R, D, ctx->x, nullptr, ctx->attn_norm[l],
-                            c.rms_eps, ctx->h, s));
+      if (l > 0 || !fuse_norm)
+        DF_HIP(launch_rmsnorm(bf, R, D, ctx->x, nullptr, ctx->attn_norm[l],
+                              c.rms_eps, ctx->h, s));
       GemmArgs a = packed_args(ctx->h, ctx->pk_qkv[l], R, qd + 2 * kvd, D);
       set_pairs(a, d, d / 2);
       set_cache_geometry(a, ctx);

@@ -21,47 +21,86 @@ __device__ __forceinline__ bool masked_at(int pass, int b, int i, int K,
   return block_tokens == nullptr || block_tokens[b * K + i] == mask_id;
 }
 
+// One workgroup per block row.  Wave 0 sets up the row (pass 0: token from
+// the anchor / caller block, validated; committed flag; caller-committed ids
+// into the draft) and, in the workgroup of a sequence's index 0, the LM-head
+// row map (lane j = block index j; rank among masked positions by ballot).
+// Then x[row] = E[token] in fp32.  With a gain g0 the workgroup also writes
+// RMSNorm(x[row]) * g0 packed into h0 (the first layer's input; statistics
+// in float64, one rounding), which saves a separate pass over x.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(
     int K, int D, int V, int mask_id, int pass, int n_cap,
     const int32_t* anchor, const int32_t* block_tokens, BlockState st,
-    const T* E, float* x, int32_t* draft) {
+    const T* E, float* x, int32_t* draft, const T* g0, float eps, T* h0) {
+  constexpr int EL = Storage<T>::E;
   __shared__ int tok_s;
+  __shared__ double red_s[4];
   const int row = blockIdx.x, b = row / K, i = row % K;
-  if (threadIdx.x == 0) {
-    if (pass == 0) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    if (lane == 0) {
       int tok;
-      if (block_tokens != nullptr) {
-        tok = block_tokens[row];
+      if (pass == 0) {
+        tok = block_tokens != nullptr ? block_tokens[row]
+                                      : (i == 0 ? anchor[b] : mask_id);
+        const int com = !masked_at(0, b, i, K, mask_id, block_tokens, nullptr);
+        if (tok < 0 || tok >= V) {
+          set_error(st.err, DFLASH_DEVERR_TOKEN);
+          tok = min(max(tok, 0), V - 1);
+        }
+        st.tokens[row] = tok;
+        st.committed[row] = com;
+        // a caller-committed position is part of the returned draft as given
+        if (com && i > 0) draft[b * (K - 1) + i - 1] = tok;
       } else {
-        tok = (i == 0) ? anchor[b] : mask_id;
+        tok = st.tokens[row];
       }
-      const int com = !masked_at(0, b, i, K, mask_id, block_tokens, nullptr);
-      if (tok < 0 || tok >= V) {
-        set_error(st.err, DFLASH_DEVERR_TOKEN);
-        tok = min(max(tok, 0), V - 1);
-      }
-      st.tokens[row] = tok;
-      st.committed[row] = com;
-      // a caller-committed position is part of the returned draft as given
-      if (com && i > 0) draft[b * (K - 1) + i - 1] = tok;
+      tok_s = tok;
     }
-    tok_s = st.tokens[row];
     if (i == 0) {
       // LM-head rows of this sequence: still-masked positions by index
-      int rank = 0;
-      for (int j = 1; j < K; ++j)
-        if (masked_at(pass, b, j, K, mask_id, block_tokens, st.committed) &&
-            rank < n_cap)
-          st.rowmap[b * n_cap + rank++] = b * K + j;
-      for (; rank < n_cap; ++rank) st.rowmap[b * n_cap + rank] = -1;
+      const bool m = lane > 0 && lane < K &&
+                     masked_at(pass, b, lane, K, mask_id, block_tokens,
+                               st.committed);
+      const unsigned long long ball = __ballot(m);
+      const int rank = __popcll(ball & ((1ull << lane) - 1ull));
+      if (m && rank < n_cap) st.rowmap[b * n_cap + rank] = b * K + lane;
+      const int count = min(__popcll(ball), n_cap);
+      if (lane >= count && lane < n_cap) st.rowmap[b * n_cap + lane] = -1;
     }
   }
   __syncthreads();
   const int tok = tok_s;
-  const T* src = E + (int64_t)tok * D;
+  const char* src = reinterpret_cast<const char*>(E + (int64_t)tok * D);
   float* xr = x + (int64_t)row * D;
-  for (int c = threadIdx.x; c < D; c += 256) xr[c] = load_elem(src, c);
+  const int nch = D / EL;
+  double ss = 0.0;
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    const u32x4 v = load16(src + (int64_t)c * 16);
+    const T* vt = reinterpret_cast<const T*>(&v);
+#pragma unroll
+    for (int e = 0; e < EL; e += 4) {
+      const f32x4 f = {load_elem(vt, e), load_elem(vt, e + 1),
+                       load_elem(vt, e + 2), load_elem(vt, e + 3)};
+      *reinterpret_cast<f32x4*>(xr + c * EL + e) = f;
+      ss += (double)f.x * f.x + (double)f.y * f.y + (double)f.z * f.z +
+            (double)f.w * f.w;
+    }
+  }
+  if (g0 == nullptr) return;
+  const double inv = 1.0 / sqrt(block_sum<4>(ss, red_s) / (double)D + (double)eps);
+  char* ob = reinterpret_cast<char*>(h0);
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    const u32x4 v = load16(src + (int64_t)c * 16);  // cached: just read
+    const u32x4 gv = load16(g0 + c * EL);
+    const T* vt = reinterpret_cast<const T*>(&v);
+    const T* gt = reinterpret_cast<const T*>(&gv);
+    T* dst = reinterpret_cast<T*>(ob + packed_offset<T>(row, c * EL, D));
+#pragma unroll
+    for (int e = 0; e < EL; ++e)
+      store_elem(dst, e, (double)load_elem(vt, e) * inv * (double)load_elem(gt, e));
+  }
 }
 
 // out[row] = RMSNorm(x[src]) * g written packed (statistics and scaling in
@@ -204,10 +243,12 @@ template <typename T>
 hipError_t embed_t(int B, int K, int D, int V, int mask_id, int pass,
                    int n_cap, const int32_t* anchor, const int32_t* block_tokens,
                    BlockState st, const void* embed, float* x,
-                   int32_t* draft, hipStream_t s) {
+                   int32_t* draft, const void* g0, float eps, void* h0,
+                   hipStream_t s) {
   hipLaunchKernelGGL(embed_kernel<T>, dim3(B * K), dim3(256), 0, s, K, D, V,
                      mask_id, pass, n_cap, anchor, block_tokens, st,
-                     static_cast<const T*>(embed), x, draft);
+                     static_cast<const T*>(embed), x, draft,
+                     static_cast<const T*>(g0), eps, static_cast<T*>(h0));
   return hipGetLastError();
 }
 
@@ -217,11 +258,13 @@ hipError_t launch_embed(bool bf16, int B, int K, int D, int V, int mask_id,
                         int pass, int n_cap, const int32_t* anchor,
                         const int32_t* block_tokens, BlockState st,
                         const void* embed, float* x, int32_t* draft,
-                        hipStream_t s) {
+                        const void* g0, float eps, void* h0, hipStream_t s) {
   return bf16 ? embed_t<bf16_t>(B, K, D, V, mask_id, pass, n_cap, anchor,
-                                block_tokens, st, embed, x, draft, s)
+                                block_tokens, st, embed, x, draft, g0, eps, h0,
+                                s)
               : embed_t<float>(B, K, D, V, mask_id, pass, n_cap, anchor,
-                               block_tokens, st, embed, x, draft, s);
+                               block_tokens, st, embed, x, draft, g0, eps, h0,
+                               s);
 }
 
 hipError_t launch_rmsnorm(bool bf16, int rows, int D, const float* x,

@@ -136,12 +136,13 @@ struct BlockState {
 };
 
 // x = E[token] (fp32); pass 0 also fills the block state; every pass
-// rebuilds the LM-head row map.
+// rebuilds the LM-head row map.  With g0 != null also h0 = RMSNorm(x) * g0
+// packed (the first layer's input), as launch_rmsnorm would write it.
 hipError_t launch_embed(bool bf16, int B, int K, int D, int V, int mask_id,
                         int pass, int n_cap, const int32_t* anchor,
                         const int32_t* block_tokens, BlockState st,
                         const void* embed, float* x, int32_t* draft,
-                        hipStream_t s);
+                        const void* g0, float eps, void* h0, hipStream_t s);
 
 // out = RMSNorm(x[rowmap ? rowmap[r] : r]) * gain, packed (contraction D);
 // rows with rowmap < 0 and rows up to the next multiple of 16 are zero.
