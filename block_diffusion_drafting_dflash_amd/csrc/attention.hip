@@ -5,8 +5,8 @@
 // query heads sharing that kv head (GQA group), each owning its 16 block
 // queries.  K and V tiles of 64 keys are staged once in LDS for all waves
 // (V transposed so the P.V product can use MFMA with keys as the contraction
-// index); the next tile is fetched into registers while the current one is
-// computed.  Each wave computes S^T = K Q^T with MFMA, keeps an online softmax
+// index); the next two tiles are fetched into registers while the current
+// one is computed.  Each wave computes S^T = K Q^T with MFMA, keeps an online softmax
 // per query in its own lanes, and accumulates O^T = V^T P^T.  Chunks write
 // unnormalised partial outputs with their running max and sum; a merge
 // kernel combines the chunks of a sequence in chunk order.
@@ -37,9 +37,9 @@ using attn_acc_t = float;
 #endif
 constexpr int kVPad = 4;  // elements of padding per transposed V row
 
-// Each thread carries NP 16-byte pieces of K and of V for one 64-key tile;
-// the next tile's pieces are loaded into registers while the current tile is
-// computed from LDS.
+// Each thread carries NP 16-byte pieces of K and of V for one 64-key tile.
+// Two such register sets are in flight: while tile t is computed from LDS,
+// tiles t + 1 and t + 2 are being loaded.
 template <typename T, int D, int G>
 struct TileRegs {
   static constexpr int PIECES = D / Storage<T>::E;  // 16-byte pieces per key
@@ -47,23 +47,33 @@ struct TileRegs {
   u32x4 k[NP], v[NP];
 };
 
+// Loads are unconditional: keys past the chunk read the chunk's last key
+// (finite values whose scores are masked to -inf, so P = 0 for them).
 template <typename T, int D, int G>
 __device__ __forceinline__ void load_tile(TileRegs<T, D, G>& t, const char* kb,
-                                          const char* vb, int kt, int n_valid,
+                                          const char* vb, int kt, int last_key,
                                           int tid) {
   constexpr int SZ = sizeof(T), E = Storage<T>::E;
   constexpr int PIECES = TileRegs<T, D, G>::PIECES;
 #pragma unroll
   for (int j = 0; j < TileRegs<T, D, G>::NP; ++j) {
     const int idx = tid + j * 64 * G;
-    const int key = idx / PIECES, pc = idx % PIECES;
-    t.k[j] = u32x4{0u, 0u, 0u, 0u};
-    t.v[j] = u32x4{0u, 0u, 0u, 0u};
-    if (key < n_valid) {
-      const int64_t off = ((int64_t)(kt + key) * D + pc * E) * SZ;
-      t.k[j] = load16(kb + off);
-      t.v[j] = load16(vb + off);
-    }
+    const int key = min(kt + idx / PIECES, last_key), pc = idx % PIECES;
+    const int64_t off = ((int64_t)key * D + pc * E) * SZ;
+    t.k[j] = stage_load(kb + off);
+    t.v[j] = stage_load(vb + off);
+  }
+}
+
+// Wait for a register set whose loads are older than the other set's
+// 2 * NP loads.
+template <typename T, int D, int G>
+__device__ __forceinline__ void wait_tile(TileRegs<T, D, G>& t) {
+  constexpr int NP = TileRegs<T, D, G>::NP;
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    vm_wait<2 * NP>(t.k[j]);
+    vm_wait<2 * NP>(t.v[j]);
   }
 }
 
@@ -96,8 +106,9 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
   const int64_t head_off = ((int64_t)b * p.Hkv + kvh) * p.P * D;
   const char* kbase = static_cast<const char*>(p.kc) + head_off * SZ;
   const char* vbase = static_cast<const char*>(p.vc) + head_off * SZ;
-  TileRegs<T, D, G> regs;
-  load_tile<T, D, G>(regs, kbase, vbase, k0, min(kKeyTile, k1 - k0), tid);
+  TileRegs<T, D, G> regs0, regs1;
+  load_tile<T, D, G>(regs0, kbase, vbase, k0, k1 - 1, tid);
+  load_tile<T, D, G>(regs1, kbase, vbase, k0 + kKeyTile, k1 - 1, tid);
 
   // Q fragments of this wave's head: lane (query r, group g)
   const char* qrow = static_cast<const char*>(p.q) +
@@ -115,23 +126,25 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[dt][j] = 0;
 
-  for (int kt = k0; kt < k1; kt += kKeyTile) {
-    const int n_valid = min(kKeyTile, k1 - kt);
+  // one 64-key tile at kt from register set rg, which is then refilled with
+  // the tile two ahead
+  auto step = [&](TileRegs<T, D, G>& rg, int kt) {
+    wait_tile<T, D, G>(rg);
     __syncthreads();  // the previous tile's readers are done with LDS
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int idx = tid + j * 64 * G;
       const int key = idx / PIECES, pc = idx % PIECES;
-      *reinterpret_cast<u32x4*>(ks + key * KROWB + pc * E * SZ) = regs.k[j];
-      const T* ve = reinterpret_cast<const T*>(&regs.v[j]);
+      *reinterpret_cast<u32x4*>(ks + key * KROWB + pc * E * SZ) = rg.k[j];
+      const T* ve = reinterpret_cast<const T*>(&rg.v[j]);
       T* vcol = reinterpret_cast<T*>(vt) + key;
 #pragma unroll
       for (int e = 0; e < E; ++e) vcol[(pc * E + e) * VROW] = ve[e];
     }
     __syncthreads();
-    if (kt + kKeyTile < k1)
-      load_tile<T, D, G>(regs, kbase, vbase, kt + kKeyTile,
-                         min(kKeyTile, k1 - kt - kKeyTile), tid);
+    load_tile<T, D, G>(rg, kbase, vbase, kt + 2 * kKeyTile, k1 - 1, tid);
+    if (kt >= k1) return;  // odd tile count: nothing left to compute
+    const int n_valid = min(kKeyTile, k1 - kt);
 
     // S^T tile: rows = 64 keys (4 MFMA row tiles), columns = 16 queries
     f32x4 s[4];
@@ -228,6 +241,18 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[dt][j] += (attn_acc_t)ot[dt][j];
+  };
+  for (int kt = k0; kt < k1; kt += 2 * kKeyTile) {
+    step(regs0, kt);
+    step(regs1, kt + kKeyTile);
+  }
+  // the last refills are still in flight: wait before the registers die
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    vm_wait<0>(regs0.k[j]);
+    vm_wait<0>(regs0.v[j]);
+    vm_wait<0>(regs1.k[j]);
+    vm_wait<0>(regs1.v[j]);
   }
 
   attn_acc_t l_tot = l_run + __shfl_xor(l_run, 16, 64);
@@ -333,8 +358,7 @@ hipError_t attn_t(int B, const AttnArgs& a, hipStream_t s) {
 
 template <typename T, int D>
 hipError_t attn_g(int B, const AttnArgs& a, hipStream_t s) {
-  switch (a.Hq / a.Hkv) {
-    case 1: return attn_t<T, D, 1>(B, a, s);
+  switch (a.Hq / a.Hkv) {  // group sizes allowed at create
     case 2: return attn_t<T, D, 2>(B, a, s);
     case 4: return attn_t<T, D, 4>(B, a, s);
     case 8: return attn_t<T, D, 8>(B, a, s);

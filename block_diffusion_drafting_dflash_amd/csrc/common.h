@@ -114,6 +114,22 @@ __device__ __forceinline__ void mma32(f32x16& acc, u32x4 a, u32x4 b) {
       0);
 }
 
+// Prefetch loads of pipelined loops are issued as inline assembly, so that
+// the compiler's wait insertion (which drains every outstanding load at a
+// loop header or a branch) does not see them; the loop waits for exactly the
+// loads it needs with vm_wait<N>, tied to the register it is about to read.
+// Every such load is waited for (vm_wait<0>) before its register can be
+// reused or the wave ends.
+__device__ __forceinline__ u32x4 stage_load(const void* p) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void vm_wait(u32x4& v) {
+  asm volatile("s_waitcnt vmcnt(%1)" : "+v"(v) : "n"(N));
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -148,9 +148,9 @@ dflash_status check_config(const dflash_config* c) {
     return fail(DFLASH_E_UNSUPPORTED, "f32 drafter needs head_dim 64");
   const int group = c->num_kv_heads > 0 ? c->num_q_heads / c->num_kv_heads : 0;
   if (c->num_q_heads % c->num_kv_heads != 0 ||
-      (group != 1 && group != 2 && group != 4 && group != 8))
+      (group != 2 && group != 4 && group != 8))
     return fail(DFLASH_E_UNSUPPORTED,
-                "num_q_heads %d must be 1, 2, 4 or 8 times num_kv_heads %d",
+                "num_q_heads %d must be 2, 4 or 8 times num_kv_heads %d",
                 c->num_q_heads, c->num_kv_heads);
   if (c->hidden % 64 || c->intermediate % 64 || c->target_hidden % 64 ||
       (c->num_q_heads * c->head_dim) % 64)

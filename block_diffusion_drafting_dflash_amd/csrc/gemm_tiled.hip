@@ -24,21 +24,6 @@ namespace dflash {
 
 namespace {
 
-// Staging loads of the main loop are issued as inline assembly so that the
-// compiler's wait insertion (which drains every outstanding load at the loop
-// header) does not see them; the loop waits for exactly the loads it needs
-// with vm_wait<N>, tied to the register it is about to read.  Every such
-// load is waited for (vm_drain) before the registers can be reused.
-__device__ __forceinline__ u32x4 stage_load(const char* p) {
-  u32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p));
-  return v;
-}
-template <int N>
-__device__ __forceinline__ void vm_wait(u32x4& v) {
-  asm volatile("s_waitcnt vmcnt(%1)" : "+v"(v) : "n"(N));
-}
-
 // Epilogue of one 32 x 32 accumulator tile: rows row0.., 16-column tiles
 // ctile and ctile + 1 (lanes 16-31 of each half-wave take the second).
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, int row0,

@@ -72,7 +72,7 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 #define DFLASH_DEVERR_POS      0x8  /* inject row's position out of range */
 
 /* Drafter shape and capacities.  Supported: block_size == 16; head_dim 64 or
- * 128; num_q_heads equal to 1, 2, 4 or 8 times num_kv_heads; hidden,
+ * 128; num_q_heads equal to 2, 4 or 8 times num_kv_heads; hidden,
  * intermediate, target_hidden and num_q_heads*head_dim multiples of 64;
  * vocab a multiple of 16.  Anything else returns DFLASH_E_UNSUPPORTED. */
 typedef struct {

@@ -101,6 +101,7 @@ def good_config(**kw):
     ("block_size", 8, "DFLASH_E_UNSUPPORTED", "block_size"),
     ("head_dim", 96, "DFLASH_E_UNSUPPORTED", "head_dim"),
     ("num_kv_heads", 3, "DFLASH_E_UNSUPPORTED", "num_kv_heads"),
+    ("num_kv_heads", 8, "DFLASH_E_UNSUPPORTED", "num_kv_heads"),
     ("vocab", 4001, "DFLASH_E_UNSUPPORTED", "vocab"),
     ("hidden", 520, "DFLASH_E_UNSUPPORTED", "multiples of 64"),
     ("num_layers", 0, "DFLASH_E_INVALID", None),
