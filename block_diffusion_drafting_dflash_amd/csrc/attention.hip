@@ -3,10 +3,12 @@
 //
 // One workgroup per (context chunk, kv head, sequence); its waves are the
 // query heads sharing that kv head (GQA group), each owning its 16 block
-// queries.  K and V tiles of 64 keys are staged once in LDS for all waves
-// (V transposed so the P.V product can use MFMA with keys as the contraction
-// index); the next two tiles are fetched into registers while the current
-// one is computed.  Each wave computes S^T = K Q^T with MFMA, keeps an online softmax
+// queries.  K and V tiles of 64 keys are staged once in LDS for all waves;
+// the next two tiles are fetched into registers while the current one is
+// computed.  The P.V product contracts over keys, so its MFMA operand needs
+// several keys of one channel per lane: bf16 V is stored key-major like K and
+// read back transposed by the LDS transpose read, fp32 V is transposed as it
+// is written.  Each wave computes S^T = K Q^T with MFMA, keeps an online softmax
 // per query in its own lanes, and accumulates O^T = V^T P^T.  Chunks write
 // unnormalised partial outputs with their running max and sum; a merge
 // kernel combines the chunks of a sequence in chunk order.
@@ -35,7 +37,19 @@ using attn_acc_t = double;
 #else
 using attn_acc_t = float;
 #endif
-constexpr int kVPad = 4;  // elements of padding per transposed V row
+constexpr int kVPad = 4;  // elements of padding per transposed V row (fp32)
+
+// LDS transpose read of 16-bit elements (gfx950).  Within each group of 16
+// lanes, lane i receives element i % 4 of the 8 bytes read by lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of its group, in that order.  So
+// when lane 4e + q of a group points at channels c + 4q .. c + 4q + 3 of key
+// k_e, lane i receives channel c + i of keys k_0 .. k_3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 // Each thread carries NP 16-byte pieces of K and of V for one 64-key tile.
 // Two such register sets are in flight: while tile t is computed from LDS,
@@ -86,9 +100,11 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
   constexpr int VROWB = VROW * SZ;
   constexpr int PIECES = TileRegs<T, D, G>::PIECES;
   constexpr int NP = TileRegs<T, D, G>::NP;
+  // V in LDS: bf16 key-major with K's padded rows, fp32 transposed
+  constexpr int VBYTES = SZ == 2 ? kKeyTile * KROWB : D * VROWB;
   static_assert(NP * 64 * G == kKeyTile * PIECES, "tile pieces per thread");
   __shared__ __attribute__((aligned(16))) char ks[kKeyTile * KROWB];
-  __shared__ __attribute__((aligned(16))) char vt[D * VROWB];
+  __shared__ __attribute__((aligned(16))) char vt[VBYTES];
 
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   int L = p.ctx_len[b];
@@ -136,10 +152,14 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
       const int idx = tid + j * 64 * G;
       const int key = idx / PIECES, pc = idx % PIECES;
       *reinterpret_cast<u32x4*>(ks + key * KROWB + pc * E * SZ) = rg.k[j];
-      const T* ve = reinterpret_cast<const T*>(&rg.v[j]);
-      T* vcol = reinterpret_cast<T*>(vt) + key;
+      if constexpr (SZ == 2) {
+        *reinterpret_cast<u32x4*>(vt + key * KROWB + pc * E * SZ) = rg.v[j];
+      } else {
+        const T* ve = reinterpret_cast<const T*>(&rg.v[j]);
+        T* vcol = reinterpret_cast<T*>(vt) + key;
 #pragma unroll
-      for (int e = 0; e < E; ++e) vcol[(pc * E + e) * VROW] = ve[e];
+        for (int e = 0; e < E; ++e) vcol[(pc * E + e) * VROW] = ve[e];
+      }
     }
     __syncthreads();
     load_tile<T, D, G>(rg, kbase, vbase, kt + 2 * kKeyTile, k1 - 1, tid);
@@ -214,11 +234,14 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
         for (int t = 0; t < NP3; ++t)
           bp[t] = u32x4{pp[t][0] | (pp[t][1] << 16), pp[t][2] | (pp[t][3] << 16),
                         pp[t][4] | (pp[t][5] << 16), pp[t][6] | (pp[t][7] << 16)};
+        // lane (r, g) reads key 32cc + 4g + r/4 (+16), channels
+        // 16dt + 4(r%4) .. +3, and receives channel 16dt + r of keys
+        // 32cc + 4g + 0..3 (lo) and 32cc + 16 + 4g + 0..3 (hi)
+        const char* vsrc = vt + (32 * cc + 4 * g + (r >> 2)) * KROWB + 4 * (r & 3) * SZ;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-          const char* vrow = vt + (16 * dt + r) * VROWB;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + (32 * cc + 4 * g) * SZ);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (32 * cc + 16 + 4 * g) * SZ);
+          const u32x2 lo = lds_read_tr16(vsrc + 16 * dt * SZ);
+          const u32x2 hi = lds_read_tr16(vsrc + 16 * KROWB + 16 * dt * SZ);
           const u32x4 afrag = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
           for (int t = 0; t < NP3; ++t) mma16(ot[dt], afrag, bp[t], T());
