@@ -130,6 +130,17 @@ __device__ __forceinline__ void vm_wait(u32x4& v) {
   asm volatile("s_waitcnt vmcnt(%1)" : "+v"(v) : "n"(N));
 }
 
+// Waits for registers st[0 .. LIM) of one batch of staging loads, issued in
+// that order, with AHEAD further loads issued after the batch: register I
+// is complete once at most AHEAD + LIM - 1 - I loads are outstanding.
+template <int I, int LIM, int AHEAD>
+__device__ __forceinline__ void stage_wait(u32x4* st) {
+  if constexpr (I < LIM) {
+    vm_wait<AHEAD + LIM - 1 - I>(st[I]);
+    stage_wait<I + 1, LIM, AHEAD>(st);
+  }
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -22,7 +22,7 @@ namespace {
 #define DFLASH_GEMM_W 8
 #endif
 #ifndef DFLASH_GEMM_U
-#define DFLASH_GEMM_U 8
+#define DFLASH_GEMM_U 4
 #endif
 #ifndef DFLASH_LM_W
 #define DFLASH_LM_W 16
@@ -124,6 +124,98 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& p, int tile,
   }
 }
 
+// Packed A operand, software-pipelined: a wave takes the steps wave,
+// wave + W, ... of the contraction in blocks of U, and two register sets
+// alternate, so that while one block is multiplied the loads of the next
+// are in flight.  The loads are the staging loads with exact waits: the
+// compiler's own waits would drain both sets at every loop edge.
+template <int AHEAD, int NL, int U, int MT, typename T, bool F64>
+__device__ __forceinline__ void packed_block(u32x4 (&st)[NL], int first,
+                                             int n_i, double (&acc)[MT][4],
+                                             f32x4 (&acc32)[MT]) {
+  stage_wait<0, NL, AHEAD>(st);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (first + u >= n_i) break;  // uniform: past this wave's last step
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if constexpr (F64) {
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        mma16(t, st[u * (1 + MT) + 1 + m], st[u * (1 + MT)], T());
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m][j] += (double)t[j];
+      } else {
+        mma16(acc32[m], st[u * (1 + MT) + 1 + m], st[u * (1 + MT)], T());
+      }
+    }
+  }
+}
+
+template <typename T, int MT, int W, int U, bool F64>
+__device__ __forceinline__ void gemm_core_packed(const GemmArgs& p, int tile,
+                                                 int m_base,
+                                                 double (&acc)[MT][4]) {
+  constexpr int KC = Storage<T>::KC;
+  constexpr int NL = U * (1 + MT);  // loads per block: weight, then A tiles
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nsteps = p.Kd / KC;
+  const char* wbase =
+      static_cast<const char*>(p.w) + ((int64_t)tile * nsteps * 64 + lane) * 16;
+  const char* abase[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int mt = min(m_base / 16 + m, (p.M + 15) / 16 - 1);
+    abase[m] = static_cast<const char*>(p.a_ptr[0]) +
+               ((int64_t)mt * nsteps * 64 + lane) * 16;
+  }
+  f32x4 acc32[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    acc32[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[m][j] = 0.0;
+  }
+  const int n_i = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;
+  const int nb = (n_i + U - 1) / U;
+  // block b holds this wave's steps bU .. bU + U - 1 (clamped to the last)
+  auto load = [&](u32x4(&st)[NL], int blk) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = min(blk * U + u, n_i - 1);
+      const int64_t off = (int64_t)(wave + i * W) * 1024;
+      st[u * (1 + MT)] = stage_load(wbase + off);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) st[u * (1 + MT) + 1 + m] = stage_load(abase[m] + off);
+    }
+  };
+  if (nb > 0) {
+    // Straight-line shape: both sets loaded, pairs of blocks while a refill
+    // exists, then the last pair with no refill.  Every set has a single
+    // consumer, so no in-flight register is ever copied.  With an odd block
+    // count the last refill of s1 (or, for one block, s1 itself) repeats
+    // the wave's last step and is not multiplied.
+    u32x4 s0[NL], s1[NL];
+    load(s0, 0);
+    load(s1, 1);
+    int blk = 0;
+    for (; blk + 2 < nb; blk += 2) {
+      packed_block<NL, NL, U, MT, T, F64>(s0, blk * U, n_i, acc, acc32);
+      load(s0, blk + 2);
+      packed_block<NL, NL, U, MT, T, F64>(s1, (blk + 1) * U, n_i, acc, acc32);
+      load(s1, blk + 3);
+    }
+    packed_block<NL, NL, U, MT, T, F64>(s0, blk * U, n_i, acc, acc32);
+    packed_block<0, NL, U, MT, T, F64>(s1, (blk + 1) * U, n_i, acc, acc32);
+  }
+  if constexpr (!F64) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[m][j] += (double)acc32[m][j];
+  }
+}
+
 // Sums the waves' tiles in wave order (float64, one row tile at a time
 // through redd); red[(m*4 + j)*64 + lane] then holds row 16m + 4(lane/16) + j,
 // tile column lane % 16.
@@ -197,13 +289,19 @@ __device__ void apply_epilogue(const GemmArgs& p, int tile, int m_base,
   }
 }
 
-template <typename T, int MT, int AP, int W, int U, bool F64>
+// PIPE: the software-pipelined core (packed A only; it holds two blocks of
+// U steps in registers, so it suits workgroups of up to 8 waves)
+template <typename T, int MT, int AP, int W, int U, bool F64, bool PIPE>
 __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmArgs p) {
+  static_assert(!PIPE || AP, "the pipelined core reads packed A");
   __shared__ double redd[W * 256];
   __shared__ float red[MT * 256];
   const int tile = blockIdx.x, m_base = blockIdx.y * 16 * MT;
   double acc[MT][4];
-  gemm_core<T, MT, AP, W, U, F64>(p, tile, m_base, acc);
+  if constexpr (PIPE)
+    gemm_core_packed<T, MT, W, U, F64>(p, tile, m_base, acc);
+  else
+    gemm_core<T, MT, AP, W, U, F64>(p, tile, m_base, acc);
   reduce_waves<MT, W>(acc, redd, red);
   apply_epilogue<T, MT, W>(p, tile, m_base, red);
 }
@@ -233,18 +331,19 @@ template <typename T, int AP>
 hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream_t s) {
   dim3 grid(pl.gx, pl.gy, 1), block(pl.waves * 64);
   if (pl.MT == 1 && a.ep == EP_TOP2)
-    hipLaunchKernelGGL((gemm_kernel<T, 1, AP, DFLASH_LM_W, DFLASH_LM_U, false>),
-                       grid, block, 0, s, a);
-  else if (pl.MT == 1)
     hipLaunchKernelGGL(
-        (gemm_kernel<T, 1, AP, DFLASH_GEMM_W, DFLASH_GEMM_U, true>), grid,
+        (gemm_kernel<T, 1, AP, DFLASH_LM_W, DFLASH_LM_U, false, false>), grid,
         block, 0, s, a);
+  else if (pl.MT == 1)
+    hipLaunchKernelGGL((gemm_kernel<T, 1, AP, DFLASH_GEMM_W, DFLASH_GEMM_U,
+                                    true, AP == 1>),
+                       grid, block, 0, s, a);
   else if (pl.MT == 2)
-    hipLaunchKernelGGL((gemm_kernel<T, 2, AP, 4, 8, true>), grid, block, 0, s,
-                       a);
+    hipLaunchKernelGGL((gemm_kernel<T, 2, AP, 4, 8, true, false>), grid, block,
+                       0, s, a);
   else if (pl.MT == 4)
-    hipLaunchKernelGGL((gemm_kernel<T, 4, AP, 16, 2, true>), grid, block, 0,
-                       s, a);
+    hipLaunchKernelGGL((gemm_kernel<T, 4, AP, 16, 2, true, false>), grid,
+                       block, 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

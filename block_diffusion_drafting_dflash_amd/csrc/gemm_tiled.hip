@@ -91,13 +91,6 @@ struct Tiled {
 // be in flight), publish them in LDS, refill the same registers PD stages
 // ahead, then multiply from LDS.  The refill is unconditional (clamped to
 // the last stage), so the loop is straight-line code.
-template <int I, int LIM, int AHEAD>
-__device__ __forceinline__ void stage_wait(u32x4* st) {
-  if constexpr (I < LIM) {
-    vm_wait<AHEAD + LIM - 1 - I>(st[I]);
-    stage_wait<I + 1, LIM, AHEAD>(st);
-  }
-}
 
 template <int TM, int TN, int WM, int WN, int SK, int PD>
 __device__ __forceinline__ void tiled_stage(
