@@ -715,9 +715,17 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
                     ? logits_debug + (size_t)pass * batch * (K - 1) * V
                     : nullptr;
     hd.logits_ld = V;
-    dflash_status st = run_gemm(ctx, hd, s, DFLASH_TIME_LMHEAD);
-    if (st != DFLASH_OK) return st;
-    DF_HIP(launch_lm_merge(Mh, V / 16, ctx->lm_part, ctx->lm_part2, s));
+    hd.err = ctx->err;
+    const int parts = lm_head_parts(bf, Mh, V, D, ctx->num_cu);
+    if (parts > 0) {
+      TimedLaunch tl(ctx, DFLASH_TIME_LMHEAD, s);
+      DF_HIP(launch_lm_head(bf, parts, hd, s));
+    } else {
+      dflash_status st = run_gemm(ctx, hd, s, DFLASH_TIME_LMHEAD);
+      if (st != DFLASH_OK) return st;
+    }
+    DF_HIP(launch_lm_merge(Mh, parts > 0 ? parts : V / 16, ctx->lm_part,
+                           ctx->lm_part2, s));
     DF_HIP(launch_commit(batch, K, n_cap, commit_per_pass, last,
                          ctx->lm_part2, bs, draft_tokens, confidence,
                          top2_margin, s));

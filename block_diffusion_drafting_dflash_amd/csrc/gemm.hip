@@ -30,6 +30,15 @@ namespace {
 #ifndef DFLASH_LM_U
 #define DFLASH_LM_U 8
 #endif
+// Persistent LM head (batches of up to 16 rows): waves per workgroup and the
+// most contraction steps a wave holds (bf16 hidden <= 16 * 8 * 32, fp32
+// hidden <= 16 * 8 * 16).
+#ifndef DFLASH_LMP_W
+#define DFLASH_LMP_W 16
+#endif
+#ifndef DFLASH_LMP_NS
+#define DFLASH_LMP_NS 8
+#endif
 
 
 // acc[m] over this wave's share of the contraction.  With F64 each MFMA
@@ -306,6 +315,112 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmArgs p) {
   apply_epilogue<T, MT, W>(p, tile, m_base, red);
 }
 
+// LM head for up to 16 drafted rows: one persistent workgroup per compute
+// unit streams every P-th 16-column vocabulary tile (the workgroups sweep
+// the matrix together).  Each wave keeps its share of the activation
+// fragments in registers for the workgroup's lifetime, and the weight
+// fragments of the next two tiles are in flight in two register sets while
+// the current tile is multiplied, summed over the waves and reduced to top-2
+// records, so the weight stream does not pause at tile boundaries.  A tile
+// is summed exactly as in gemm_kernel (fp32 over a wave's steps, then
+// float64 over the waves in wave order); each row's record is merged over
+// the workgroup's tiles in tile order and written once per workgroup:
+// part[row][workgroup].
+
+// AHEAD: staging loads issued after this tile's set (the other set's, or
+// none for the last tile).  The tile is multiplied from set b; with REFILL
+// b is then reloaded with the tile two ahead, before the wave sums.
+template <typename T, int W, int NS, int AHEAD, bool REFILL, typename LoadW>
+__device__ __forceinline__ void lm_tile(const GemmArgs& p, u32x4 (&a)[NS],
+                                        u32x4 (&b)[NS], int n_i, int i,
+                                        int tile, bool valid, double* redd,
+                                        Top2& run, const LoadW& load_w) {
+  stage_wait<0, NS, AHEAD>(b);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s < n_i) mma16(acc, a[s], b[s], T());
+  if constexpr (REFILL) load_w(b, i + 2);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) redd[wave * 256 + j * 64 + lane] = (double)acc[j];
+  __syncthreads();
+  if (threadIdx.x < 256 && valid) {
+    const int idx = threadIdx.x;
+    // idx = (j, row group, column): row 4 (idx % 64 / 16) + idx / 64
+    double v = redd[idx];
+#pragma unroll
+    for (int w = 1; w < W; ++w) v += redd[w * 256 + idx];
+    const float z = (float)v;
+    const int row = 4 * ((idx & 63) >> 4) + (idx >> 6);
+    const int col = tile * 16 + (idx & 15);
+    Top2 t = top2_empty();
+    if (row < p.M) {
+      t.m1 = z;
+      t.i1 = col;
+      t.s = 1.f;
+      if (p.logits != nullptr) store_debug_logit(p, row, col, z);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) t = top2_merge(t, top2_shfl_xor(t, o));
+    run = top2_merge(run, t);
+  }
+}
+
+template <typename T, int W, int NS>
+__global__ __launch_bounds__(64 * W) void lm_head_kernel(GemmArgs p) {
+  constexpr int KC = Storage<T>::KC;
+  __shared__ double redd[2][W * 256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nsteps = p.Kd / KC;
+  const int ntiles = p.N / 16, P = gridDim.x, wg = blockIdx.x;
+  // tiles wg, wg + P, ...: the workgroups sweep the matrix together
+  const int nt = (ntiles - 1 - wg) / P + 1;  // >= 1: P <= ntiles
+  auto tile_of = [&](int i) { return wg + min(i, nt - 1) * P; };
+  // this wave's steps: wave, wave + W, ... (n_i of them, n_i <= NS)
+  const int n_i = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;
+  const int64_t step_off = (int64_t)wave * 1024 + lane * 16;
+  // a step past the wave's last repeats the last (a wave with no steps
+  // reads step 0), a slot past the last tile repeats the last tile; neither
+  // is multiplied or summed
+  auto load_w = [&](u32x4(&b)[NS], int i) {  // this workgroup's i-th tile
+    const char* wt = static_cast<const char*>(p.w) +
+                     (int64_t)tile_of(i) * nsteps * 1024 + step_off;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      b[s] = stage_load(wt + (int64_t)min(s, max(n_i - 1, 0)) * W * 1024);
+  };
+  u32x4 a[NS], b0[NS], b1[NS];
+  {
+    const char* at = static_cast<const char*>(p.a_ptr[0]) + step_off;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      a[s] = stage_load(at + (int64_t)min(s, max(n_i - 1, 0)) * W * 1024);
+  }
+  load_w(b0, 0);
+  load_w(b1, 1);
+  stage_wait<0, NS, 2 * NS>(a);
+  Top2 run = top2_empty();
+  int i = 0;
+  for (; i + 2 < nt; i += 2) {
+    lm_tile<T, W, NS, NS, true>(p, a, b0, n_i, i, tile_of(i), true, redd[0],
+                                run, load_w);
+    lm_tile<T, W, NS, NS, true>(p, a, b1, n_i, i + 1, tile_of(i + 1), true,
+                                redd[1], run, load_w);
+  }
+  lm_tile<T, W, NS, NS, false>(p, a, b0, n_i, i, tile_of(i), true, redd[0],
+                               run, load_w);
+  // the second set was loaded whether or not its tile exists: wait for it
+  // either way (only its sums are skipped)
+  lm_tile<T, W, NS, 0, false>(p, a, b1, n_i, i + 1, tile_of(i + 1), i + 1 < nt,
+                              redd[1], run, load_w);
+  if (threadIdx.x < 256 && (threadIdx.x & 15) == 0) {
+    const int row = 4 * ((threadIdx.x & 63) >> 4) + (threadIdx.x >> 6);
+    if (row < p.M) p.top2[(int64_t)row * P + wg] = run;
+  }
+}
+
 // One 16-byte chunk of the packed matrix per thread.
 template <typename T>
 __global__ void pack_kernel(PackArgs a) {
@@ -368,6 +483,26 @@ hipError_t launch_gemm(bool bf16, const GemmPlan& pl, const GemmArgs& a,
                       : launch_gemm_t<bf16_t, 0>(pl, a, s);
   return a.a_packed ? launch_gemm_t<float, 1>(pl, a, s)
                     : launch_gemm_t<float, 0>(pl, a, s);
+}
+
+constexpr int kLmW = DFLASH_LMP_W, kLmNS = DFLASH_LMP_NS;
+
+int lm_head_parts(bool bf16, int M, int N, int Kd, int num_cu) {
+  const int KC = bf16 ? Storage<bf16_t>::KC : Storage<float>::KC;
+  if (M > 16 || Kd % KC != 0 || Kd / KC > kLmW * kLmNS) return 0;
+  return min(num_cu, N / 16);
+}
+
+hipError_t launch_lm_head(bool bf16, int parts, const GemmArgs& a,
+                          hipStream_t s) {
+  if (parts <= 0 || !a.a_packed) return hipErrorInvalidValue;
+  if (bf16)
+    hipLaunchKernelGGL((lm_head_kernel<bf16_t, kLmW, kLmNS>), dim3(parts),
+                       dim3(64 * kLmW), 0, s, a);
+  else
+    hipLaunchKernelGGL((lm_head_kernel<float, kLmW, kLmNS>), dim3(parts),
+                       dim3(64 * kLmW), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(bool bf16, const PackArgs& a, hipStream_t s) {

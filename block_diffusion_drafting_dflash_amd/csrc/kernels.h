@@ -96,6 +96,13 @@ GemmPlan plan_gemm(int M, int N, bool lm_head);
 hipError_t launch_gemm(bool bf16, const GemmPlan& pl, const GemmArgs& a,
                        hipStream_t s);
 
+// LM head (EP_TOP2) of at most 16 rows as a persistent stream: returns the
+// number of workgroups (> 0) when the shape is supported, else 0; the launch
+// writes one top-2 record per row and workgroup, a.top2[row][parts].
+int lm_head_parts(bool bf16, int M, int N, int Kd, int num_cu);
+hipError_t launch_lm_head(bool bf16, int parts, const GemmArgs& a,
+                          hipStream_t s);
+
 // Tiled MFMA GEMM for batched rows (gemm_tiled.hip): output block shapes
 // rows x columns; each instance keeps its fragments in LDS per step.
 enum TileCfg : int {
