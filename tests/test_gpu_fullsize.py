@@ -35,7 +35,7 @@ import torch
 import workloads as W
 from oracle import (OracleModel, draft_batch, inject_rows, synthetic_target,
                     verify_greedy as oracle_verify)
-from tests.gpu_common import (DEV, LOGCONF_TOL, LOGIT_TOL, MARGIN_MIN,
+from tests.gpu_common import (DEV, logconf_tol, logit_tol, margin_min,
                               check_bf16_close, compare_draft, f64, say)
 
 pytestmark = pytest.mark.gpu
@@ -147,19 +147,17 @@ def test_full_size_step_parity(name):
         per_seq.append(ctx_kv)
     ref = draft_batch(model, per_seq, lens, anchors=anchors, num_passes=S,
                       commit_per_pass=c, keep_logits=True, seqs=seqs)
-    depth = wl.num_layers
-    tol = LOGIT_TOL[wl.dtype] * depth
-    margin_min = MARGIN_MIN * depth
+    tol, mmin = logit_tol(wl), margin_min(wl)
     if S == 1:
         g["logits"] = g["logits_all"][0]
         comp, excl, dl = compare_draft(wl, g, ref, tol=tol,
-                                       margin_min=margin_min)
+                                       margin_min=mmin)
         say(f"  tokens compared {comp}, excluded {excl}, max |dlogit| {dl:.2e}"
             f" (bound {tol:.0e})")
         assert comp > 0
         lc = np.abs(np.log(g["conf"]) -
                     np.log(np.stack([o["conf"][1:] for o in ref])))
-        assert lc.max() <= LOGCONF_TOL[wl.dtype] * depth
+        assert lc.max() <= logconf_tol(wl)
         mg = np.stack([o["margin"][1:] for o in ref])
         assert np.abs(g["margin"] - mg).max() <= 2 * tol
     else:
@@ -175,13 +173,13 @@ def test_full_size_step_parity(name):
             oracle_set = set(np.nonzero(o["pass"] == 0)[0].tolist())
             gpu_set = set(range(1, 16)) - set(
                 np.nonzero(~np.isnan(g["logits_all"][1][j][:, 0]))[0] + 1)
-            if gap > margin_min:
+            if gap > mmin:
                 clear += 1
                 assert gpu_set == oracle_set, f"seq {b}: commit sets differ"
                 same = True
                 for i in oracle_set:
                     tok_ok = g["draft"][j, i - 1] == o["tokens"][i]
-                    if o["pass_margin"][0][i] > margin_min:
+                    if o["pass_margin"][0][i] > mmin:
                         assert tok_ok, f"seq {b} pos {i}: committed token differs"
                     same &= bool(tok_ok)
                 if same:  # else a near-tie went the other way: pass 2 differs
@@ -199,7 +197,7 @@ def test_full_size_step_parity(name):
             assert np.abs(tf["logits_all"][0][j][rows2 - 1] -
                           o["logits"][1]).max() <= tol
             for i in rows2:
-                if o["pass_margin"][1][int(i)] > margin_min:
+                if o["pass_margin"][1][int(i)] > mmin:
                     assert tf["draft"][j, i - 1] == o["pass_token"][1][int(i)]
     ctx.close()
     del kv, w_dev, H
