@@ -15,6 +15,25 @@ __device__ __forceinline__ void rope_pair(double a, double b, double2 cs,
   rb = b * cs.x + a * cs.y;
 }
 
+// bf16 of silu(a) * b, rounded exactly as the float64 evaluation would be.
+// The float evaluation (expf, one add, a correctly rounded divide, one
+// multiply) is within a few float ulps of the exact value; unless that lands
+// within kSiluGuard float ulps of a bf16 rounding midpoint (low 16 bits
+// 0x8000), it rounds to the same bf16 as the exact value and as the float64
+// evaluation.  Near a midpoint, for large |a| and for zero, denormal or
+// non-finite results the float64 evaluation decides.
+constexpr uint32_t kSiluGuard = 64;
+__device__ __forceinline__ uint32_t swiglu_bf16(float a, float b) {
+  const float r = a / (1.f + expf(-a)) * b;
+  const uint32_t u = __float_as_uint(r);
+  const uint32_t lo = u & 0xFFFFu, ex = u & 0x7F800000u;
+  const bool clear = fabsf(a) < 64.f && ex != 0u && ex != 0x7F800000u &&
+                     (lo + kSiluGuard < 0x8000u || lo > 0x8000u + kSiluGuard);
+  if (clear) return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const double da = a;
+  return f64_to_bf16(da / (1.0 + exp(-da)) * (double)b);
+}
+
 // One finished output pair of a MAP_PAIRS GEMM: `a` is low column `col`,
 // `b` its partner at col + pair_off, both of output row `row` (< M).
 //   EP_SWIGLU: act[row][col] = silu(a) * b (packed, contraction pair_off)
@@ -27,8 +46,12 @@ __device__ __forceinline__ void pair_epilogue(const GemmArgs& p, int row,
   if (p.ep == EP_SWIGLU) {
     T* act = static_cast<T*>(p.out_t);
     const int64_t off = packed_offset<T>(row, col, p.pair_off) / sizeof(T);
-    const double da = a;
-    store_elem(act, off, da / (1.0 + exp(-da)) * (double)b);
+    if constexpr (sizeof(T) == 2) {
+      act[off].bits = (uint16_t)swiglu_bf16(a, b);
+    } else {
+      const double da = a;
+      store_elem(act, off, da / (1.0 + exp(-da)) * (double)b);
+    }
     return;
   }
   const int half = p.d / 2;

@@ -264,10 +264,24 @@ hipError_t tiled_t(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+#ifndef DFLASH_T64_SK
+#define DFLASH_T64_SK 2
+#endif
+#ifndef DFLASH_T64_PD
+#define DFLASH_T64_PD 4
+#endif
+#ifndef DFLASH_T128_SK
+#define DFLASH_T128_SK 2
+#endif
+#ifndef DFLASH_T128_PD
+#define DFLASH_T128_PD 2
+#endif
 hipError_t tiled_cfg(int cfg, const GemmArgs& a, hipStream_t s) {
   switch (cfg) {
-    case TILE_64x64: return tiled_t<1, 1, 2, 2, 2, 2>(a, s);
-    case TILE_128x128: return tiled_t<2, 2, 2, 2, 2, 2>(a, s);
+    case TILE_64x64:
+      return tiled_t<1, 1, 2, 2, DFLASH_T64_SK, DFLASH_T64_PD>(a, s);
+    case TILE_128x128:
+      return tiled_t<2, 2, 2, 2, DFLASH_T128_SK, DFLASH_T128_PD>(a, s);
     case TILE_256x64: return tiled_t<4, 1, 2, 2, 2, 2>(a, s);
     case TILE_256x128: return tiled_t<4, 2, 2, 2, 2, 1>(a, s);
     case TILE_128x256: return tiled_t<2, 4, 2, 2, 2, 1>(a, s);
