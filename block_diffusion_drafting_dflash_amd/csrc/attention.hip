@@ -21,21 +21,12 @@ namespace {
 constexpr int kKeyTile = 64;
 
 // Accuracy of P.V: P is split into DFLASH_ATTN_PSPLIT bf16 parts (2: ~16
-// significant bits, 3: exact fp32); each 64-key tile's P.V is summed by the
-// MFMAs in fp32 and added to running accumulators of type float, or double
-// with DFLASH_ATTN_F64.  Rounding P to a single bf16 part measurably moves
-// the drafted logits; more than two parts or float64 accumulation does not
-// (the bf16 rounding of the attention output dominates).
+// significant bits, 3: exact fp32) and the MFMAs accumulate in fp32 into the
+// running output.  Rounding P to a single bf16 part measurably moves the
+// drafted logits; more than two parts, or float64 running sums, do not (the
+// bf16 rounding of the attention output dominates).
 #ifndef DFLASH_ATTN_PSPLIT
 #define DFLASH_ATTN_PSPLIT 2
-#endif
-#ifndef DFLASH_ATTN_F64
-#define DFLASH_ATTN_F64 0
-#endif
-#if DFLASH_ATTN_F64
-using attn_acc_t = double;
-#else
-using attn_acc_t = float;
 #endif
 constexpr int kVPad = 4;  // elements of padding per transposed V row (fp32)
 
@@ -79,20 +70,36 @@ __device__ __forceinline__ void load_tile(TileRegs<T, D, G>& t, const char* kb,
   }
 }
 
-// Wait for a register set whose loads are older than the other set's
-// 2 * NP loads.
+// Register sets of K/V tiles in flight (each 2 * NP loads per thread) for
+// groups of four or more query heads; groups of two hold twice the pieces
+// per thread and keep two sets.
+#ifndef DFLASH_ATTN_SETS
+#define DFLASH_ATTN_SETS 2
+#endif
+template <int G>
+constexpr int attn_sets() {
+  return G >= 4 ? DFLASH_ATTN_SETS : 2;
+}
+static_assert(DFLASH_ATTN_SETS == 2 || DFLASH_ATTN_SETS == 3,
+              "two or three register sets");
+
+// Wait for the oldest register set: the other sets' loads were issued
+// after it.
 template <typename T, int D, int G>
 __device__ __forceinline__ void wait_tile(TileRegs<T, D, G>& t) {
   constexpr int NP = TileRegs<T, D, G>::NP;
+  constexpr int AHEAD = (attn_sets<G>() - 1) * 2 * NP;
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
-    vm_wait<2 * NP>(t.k[j]);
-    vm_wait<2 * NP>(t.v[j]);
+    vm_wait<AHEAD>(t.k[j]);
+    vm_wait<AHEAD>(t.v[j]);
   }
 }
 
+// (at four waves, two workgroups per compute unit: at most 256 VGPRs)
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
+__global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
+    AttnArgs p) {
   constexpr int E = Storage<T>::E, KC = Storage<T>::KC, SZ = sizeof(T);
   constexpr int DC = D / KC;
   constexpr int KROWB = D * SZ + 16;           // padded K row, bytes
@@ -103,9 +110,11 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
   // V in LDS: bf16 key-major with K's padded rows, fp32 transposed
   constexpr int VBYTES = SZ == 2 ? kKeyTile * KROWB : D * VROWB;
   static_assert(NP * 64 * G == kKeyTile * PIECES, "tile pieces per thread");
-  __shared__ __attribute__((aligned(16))) char ks[kKeyTile * KROWB];
-  __shared__ __attribute__((aligned(16))) char vt[VBYTES];
+  // K and V tiles, double-buffered by tile parity
+  __shared__ __attribute__((aligned(16))) char ks2[2][kKeyTile * KROWB];
+  __shared__ __attribute__((aligned(16))) char vt2[2][VBYTES];
 
+  constexpr int kSets = attn_sets<G>();
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   int L = p.ctx_len[b];
   L = min(max(L, 0), p.max_len);
@@ -122,9 +131,11 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
   const int64_t head_off = ((int64_t)b * p.Hkv + kvh) * p.P * D;
   const char* kbase = static_cast<const char*>(p.kc) + head_off * SZ;
   const char* vbase = static_cast<const char*>(p.vc) + head_off * SZ;
-  TileRegs<T, D, G> regs0, regs1;
+  TileRegs<T, D, G> regs0, regs1, regs2;
   load_tile<T, D, G>(regs0, kbase, vbase, k0, k1 - 1, tid);
   load_tile<T, D, G>(regs1, kbase, vbase, k0 + kKeyTile, k1 - 1, tid);
+  if constexpr (kSets == 3)
+    load_tile<T, D, G>(regs2, kbase, vbase, k0 + 2 * kKeyTile, k1 - 1, tid);
 
   // Q fragments of this wave's head: lane (query r, group g)
   const char* qrow = static_cast<const char*>(p.q) +
@@ -134,19 +145,20 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
   for (int dc = 0; dc < DC; ++dc) qf[dc] = load16(qrow + dc * KC * SZ);
 
   // running max (log2 domain), softmax numerator o and denominator l
-  float m_run = -INFINITY;
-  attn_acc_t l_run = 0;
-  attn_acc_t o[D / 16][4];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[D / 16];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[dt][j] = 0;
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // one 64-key tile at kt from register set rg, which is then refilled with
-  // the tile two ahead
+  // the tile kSets ahead
   auto step = [&](TileRegs<T, D, G>& rg, int kt) {
     wait_tile<T, D, G>(rg);
-    __syncthreads();  // the previous tile's readers are done with LDS
+    // buffer (tile index) % 2: its readers two tiles back are done, since
+    // every wave has passed the previous tile's barrier
+    const int buf = ((kt - k0) / kKeyTile) & 1;
+    char* ks = ks2[buf];
+    char* vt = vt2[buf];
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int idx = tid + j * 64 * G;
@@ -162,8 +174,8 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
       }
     }
     __syncthreads();
-    load_tile<T, D, G>(rg, kbase, vbase, kt + 2 * kKeyTile, k1 - 1, tid);
-    if (kt >= k1) return;  // odd tile count: nothing left to compute
+    load_tile<T, D, G>(rg, kbase, vbase, kt + kSets * kKeyTile, k1 - 1, tid);
+    if (kt >= k1) return;  // past the chunk's last tile: nothing to compute
     const int n_valid = min(kKeyTile, k1 - kt);
 
     // S^T tile: rows = 64 keys (4 MFMA row tiles), columns = 16 queries
@@ -191,26 +203,26 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
     // the same factor scales numerator and denominator, so its rounding
-    // cancels in o = numerator / denominator
-    const attn_acc_t alpha = (attn_acc_t)exp2f(m_run - m_new);
-    attn_acc_t lt = 0;
+    // cancels in o = numerator / denominator; once the running maxima have
+    // settled the factor is 1 for every query and the rescale is skipped
+    const float alpha = exp2f(m_run - m_new);
+    float lt = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float pv = exp2f(s[mt][j] - m_new);
         s[mt][j] = pv;
-        lt += (attn_acc_t)pv;
+        lt += pv;
       }
     l_run = l_run * alpha + lt;
     m_run = m_new;
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
+      for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[dt][j] *= alpha;
-    f32x4 ot[D / 16];  // this tile's P.V (fp32)
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) ot[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j) o[dt][j] *= alpha;
+    }
 
     // O^T += V^T P^T; contraction slots of lane group g hold the keys that
     // this lane's S^T registers hold
@@ -244,7 +256,7 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
           const u32x2 hi = lds_read_tr16(vsrc + 16 * KROWB + 16 * dt * SZ);
           const u32x4 afrag = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-          for (int t = 0; t < NP3; ++t) mma16(ot[dt], afrag, bp[t], T());
+          for (int t = 0; t < NP3; ++t) mma16(o[dt], afrag, bp[t], T());
         }
       }
     } else {
@@ -256,18 +268,15 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
         for (int dt = 0; dt < D / 16; ++dt) {
           const char* vrow = vt + (16 * dt + r) * VROWB;
           const u32x4 afrag = *reinterpret_cast<const u32x4*>(vrow + (16 * cc + 4 * g) * SZ);
-          mma16(ot[dt], afrag, bfrag, T());
+          mma16(o[dt], afrag, bfrag, T());
         }
       }
     }
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[dt][j] += (attn_acc_t)ot[dt][j];
   };
-  for (int kt = k0; kt < k1; kt += 2 * kKeyTile) {
+  for (int kt = k0; kt < k1; kt += kSets * kKeyTile) {
     step(regs0, kt);
     step(regs1, kt + kKeyTile);
+    if constexpr (kSets == 3) step(regs2, kt + 2 * kKeyTile);
   }
   // the last refills are still in flight: wait before the registers die
 #pragma unroll
@@ -276,9 +285,13 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
     vm_wait<0>(regs0.v[j]);
     vm_wait<0>(regs1.k[j]);
     vm_wait<0>(regs1.v[j]);
+    if constexpr (kSets == 3) {
+      vm_wait<0>(regs2.k[j]);
+      vm_wait<0>(regs2.v[j]);
+    }
   }
 
-  attn_acc_t l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   // partials are chunk-major within (sequence, query head, query):
   // part_o[((b*Hq + hq)*K + i)*nch + c][D], part_ml[... same index][2]
@@ -286,10 +299,9 @@ __global__ __launch_bounds__(64 * G) void attn_partial_kernel(AttnArgs p) {
   float* po = p.part_o + base * D;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
-    *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) =
-        f32x4{(float)o[dt][0], (float)o[dt][1], (float)o[dt][2], (float)o[dt][3]};
+    *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt];
   if (g == 0)
-    *reinterpret_cast<float2*>(p.part_ml + base * 2) = float2{m_run, (float)l_tot};
+    *reinterpret_cast<float2*>(p.part_ml + base * 2) = float2{m_run, l_tot};
 }
 
 // o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the sequence's
