@@ -724,11 +724,14 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
       dflash_status st = run_gemm(ctx, hd, s, DFLASH_TIME_LMHEAD);
       if (st != DFLASH_OK) return st;
     }
-    DF_HIP(launch_lm_merge(Mh, parts > 0 ? parts : V / 16, ctx->lm_part,
-                           ctx->lm_part2, s));
+    // the persistent head leaves one record per row and workgroup, which
+    // the commit kernel merges itself; per-tile records are merged first
+    if (parts == 0)
+      DF_HIP(launch_lm_merge(Mh, V / 16, ctx->lm_part, ctx->lm_part2, s));
     DF_HIP(launch_commit(batch, K, n_cap, commit_per_pass, last,
-                         ctx->lm_part2, bs, draft_tokens, confidence,
-                         top2_margin, s));
+                         parts > 0 ? ctx->lm_part : ctx->lm_part2,
+                         parts > 0 ? parts : kMergeChunks, bs, draft_tokens,
+                         confidence, top2_margin, s));
   }
   return DFLASH_OK;
 }

@@ -32,27 +32,54 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(int ntiles,
   }
 }
 
-// One wave per sequence; lane i is block index i.  A masked lane merges the
-// chunk records of its LM-head row (rank among masked positions by index),
-// then ranks itself by confidence (ties -> lower index) and commits if within
-// the pass's quota.
-__global__ __launch_bounds__(64) void commit_kernel(
-    int K, int n_cap, int quota, int last, const Top2* part2, BlockState st,
-    int32_t* draft, float* conf_out, float* margin_out) {
-  const int b = blockIdx.x, i = threadIdx.x;
-  const bool masked = i < K && !st.committed[b * K + i];
-  const unsigned long long ball = __ballot(masked);
-  const unsigned long long below = (i == 0) ? 0ull : (ball & ((1ull << i) - 1ull));
-  const int rank_idx = __popcll(below);
-  Top2 r = top2_empty();
-  if (masked) {
-    const Top2* src = part2 + (int64_t)(b * n_cap + rank_idx) * kMergeChunks;
-    Top2 c[kMergeChunks];
-#pragma unroll
-    for (int k = 0; k < kMergeChunks; ++k) c[k] = src[k];
-#pragma unroll
-    for (int k = 0; k < kMergeChunks; ++k) r = top2_merge(r, c[k]);
+// One workgroup per sequence.  Wave w merges the records of the LM-head
+// rows of block positions w, w + 16, ... (a masked position's row is its
+// rank among the masked positions): nrec records per row, lane k taking
+// records k, k + 64, ... in order (loaded four at a time), then a
+// butterfly.  Wave 0 then ranks the
+// masked positions by confidence (ties -> lower index) and commits those
+// within the pass's quota.
+constexpr int kCommitWaves = 16;
+
+__global__ __launch_bounds__(64 * kCommitWaves) void commit_kernel(
+    int K, int n_cap, int quota, int last, const Top2* part, int nrec,
+    BlockState st, int32_t* draft, float* conf_out, float* margin_out) {
+  __shared__ Top2 res[64];
+  __shared__ unsigned long long ball_s;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    const bool m = lane < K && !st.committed[b * K + lane];
+    const unsigned long long ball = __ballot(m);
+    if (lane == 0) ball_s = ball;
   }
+  __syncthreads();
+  const unsigned long long ball = ball_s;
+  for (int i = wave; i < K; i += kCommitWaves) {
+    if (!((ball >> i) & 1ull)) continue;  // uniform per wave
+    const int rank_idx = __popcll(ball & ((1ull << i) - 1ull));
+    const Top2* src = part + (int64_t)(b * n_cap + rank_idx) * nrec;
+    // lane records issued in batches of kCommitBatch, merged in order
+    constexpr int kCommitBatch = 4;
+    Top2 r = top2_empty();
+    for (int k0 = 0; k0 < nrec; k0 += 64 * kCommitBatch) {
+      Top2 t[kCommitBatch];
+#pragma unroll
+      for (int u = 0; u < kCommitBatch; ++u) {
+        const int k = k0 + u * 64 + lane;
+        t[u] = k < nrec ? src[k] : top2_empty();
+      }
+#pragma unroll
+      for (int u = 0; u < kCommitBatch; ++u) r = top2_merge(r, t[u]);
+    }
+    r = top2_wave(r);
+    if (lane == 0) res[i] = r;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int i = lane;
+  const bool masked = (ball >> i) & 1ull;
+  const Top2 r = masked ? res[i] : top2_empty();
   const float cf = masked ? 1.f / r.s : -1.f;  // exp(max - logsumexp)
   int better = 0;
   for (int j = 0; j < K; ++j) {
@@ -98,10 +125,13 @@ hipError_t launch_lm_merge(int rows, int ntiles, const Top2* part, Top2* part2,
 }
 
 hipError_t launch_commit(int B, int K, int n_cap, int commit, bool last,
-                         const Top2* part2, BlockState st, int32_t* draft,
-                         float* conf, float* margin, hipStream_t s) {
-  hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(64), 0, s, K, n_cap, commit,
-                     last ? 1 : 0, part2, st, draft, conf, margin);
+                         const Top2* part, int nrec, BlockState st,
+                         int32_t* draft, float* conf, float* margin,
+                         hipStream_t s) {
+  if (K > 64 || nrec < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(64 * kCommitWaves), 0, s, K,
+                     n_cap, commit, last ? 1 : 0, part, nrec, st, draft, conf,
+                     margin);
   return hipGetLastError();
 }
 

@@ -179,9 +179,12 @@ constexpr int kMergeChunks = 16;
 // part [rows][ntiles] -> part2 [rows][kMergeChunks], merged in tile order
 hipError_t launch_lm_merge(int rows, int ntiles, const Top2* part, Top2* part2,
                            hipStream_t s);
+// Merges each LM-head row's nrec records (part [rows][nrec]: lm_merge's
+// chunks, or the persistent LM head's per-workgroup records) and commits.
 hipError_t launch_commit(int B, int K, int n_cap, int commit, bool last,
-                         const Top2* part2, BlockState st, int32_t* draft,
-                         float* conf, float* margin, hipStream_t s);
+                         const Top2* part, int nrec, BlockState st,
+                         int32_t* draft, float* conf, float* margin,
+                         hipStream_t s);
 hipError_t launch_verify(int B, int K, const int32_t* draft,
                          const int32_t* target, int32_t* accept,
                          int32_t* next_anchor, hipStream_t s);
