@@ -86,34 +86,22 @@ struct Tiled {
   static_assert(NF % NW == 0, "fragments must split evenly over the waves");
 };
 
-// One LDS stage = SK contraction steps: wait for this stage's staged
-// fragments (loaded PD stages ago: the PD - 1 later stages' loads may still
-// be in flight), publish them in LDS, refill the same registers PD stages
-// ahead, then multiply from LDS.  The refill is unconditional (clamped to
-// the last stage), so the loop is straight-line code.
-
+// One LDS stage = SK contraction steps, multiplied from LDS buffer `cur`
+// (published during the previous stage).  After the first half-step's MFMAs
+// the staged registers of the next stage (loaded PD stages ago: the PD - 1
+// later stages' loads may still be in flight) are waited for and published
+// into the other buffer `nxt` while the remaining MFMAs run; one barrier
+// then makes them visible and frees `cur`, and the same registers are
+// refilled PD stages ahead.  The refill is unconditional (clamped to the last
+// stage), so the loop is straight-line code.
 template <int TM, int TN, int WM, int WN, int SK, int PD>
 __device__ __forceinline__ void tiled_stage(
-    int next, u32x4 (&st)[Tiled<TM, TN, WM, WN>::LPW * SK],
-    const char* const (&src)[Tiled<TM, TN, WM, WN>::LPW], u32x4* buf,
-    int wave, int lane, int a_off, int w_off, f32x16 (&acc)[TM][TN]) {
+    int refill, u32x4 (&st)[Tiled<TM, TN, WM, WN>::LPW * SK],
+    const char* const (&src)[Tiled<TM, TN, WM, WN>::LPW], const u32x4* cur,
+    u32x4* nxt, int wave, int lane, int a_off, int w_off,
+    f32x16 (&acc)[TM][TN]) {
   using C = Tiled<TM, TN, WM, WN>;
   constexpr int NL = C::LPW * SK;  // loads per stage per lane
-  __builtin_amdgcn_sched_barrier(0);
-  stage_wait<0, NL, (PD - 1) * NL>(st);
-#pragma unroll
-  for (int k = 0; k < SK; ++k)
-#pragma unroll
-    for (int i = 0; i < C::LPW; ++i)
-      buf[(k * C::NF + wave + i * C::NW) * 64 + lane] = st[k * C::LPW + i];
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < SK; ++k)
-#pragma unroll
-    for (int i = 0; i < C::LPW; ++i)
-      st[k * C::LPW + i] =
-          stage_load(src[i] + ((int64_t)next * SK + k) * 1024);
-  __builtin_amdgcn_sched_barrier(0);
   // step k, half h: contraction 32k + 16h .. + 16
 #pragma unroll
   for (int k = 0; k < SK; ++k)
@@ -122,15 +110,32 @@ __device__ __forceinline__ void tiled_stage(
       u32x4 a[TM], w[TN];
 #pragma unroll
       for (int m = 0; m < TM; ++m)
-        a[m] = buf[k * C::NF * 64 + a_off + m * 128 + 32 * h];
+        a[m] = cur[k * C::NF * 64 + a_off + m * 128 + 32 * h];
 #pragma unroll
       for (int n = 0; n < TN; ++n)
-        w[n] = buf[k * C::NF * 64 + w_off + n * 128 + 32 * h];
+        w[n] = cur[k * C::NF * 64 + w_off + n * 128 + 32 * h];
 #pragma unroll
       for (int m = 0; m < TM; ++m)
 #pragma unroll
         for (int n = 0; n < TN; ++n) mma32(acc[m][n], a[m], w[n]);
+      if (k == 0 && h == 0) {
+        stage_wait<0, NL, (PD - 1) * NL>(st);
+#pragma unroll
+        for (int kk = 0; kk < SK; ++kk)
+#pragma unroll
+          for (int i = 0; i < C::LPW; ++i)
+            nxt[(kk * C::NF + wave + i * C::NW) * 64 + lane] =
+                st[kk * C::LPW + i];
+      }
     }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < SK; ++k)
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i)
+      st[k * C::LPW + i] =
+          stage_load(src[i] + ((int64_t)refill * SK + k) * 1024);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int TM, int TN, int WM, int WN, int SK, int PD>
@@ -179,7 +184,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(GemmArgs p,
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[m][n][j] = 0.f;
 
-  u32x4 st[PD][C::LPW * SK];
+  constexpr int NL = C::LPW * SK;
+  u32x4 st[PD][NL];
 #pragma unroll
   for (int j = 0; j < PD; ++j)
 #pragma unroll
@@ -188,20 +194,36 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(GemmArgs p,
       for (int i = 0; i < C::LPW; ++i)
         st[j][kk * C::LPW + i] = stage_load(
             src[i] + ((int64_t)min(j, nstages - 1) * SK + kk) * 1024);
-  // nstages is a multiple of PD; LDS buffers alternate by stage parity
+  // stage 0 into buffer 0; its registers then take stage PD
+  stage_wait<0, NL, (PD - 1) * NL>(st[0]);
+#pragma unroll
+  for (int kk = 0; kk < SK; ++kk)
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i)
+      lds[(kk * C::NF + wave + i * C::NW) * 64 + lane] = st[0][kk * C::LPW + i];
+  __syncthreads();
+#pragma unroll
+  for (int kk = 0; kk < SK; ++kk)
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i)
+      st[0][kk * C::LPW + i] = stage_load(
+          src[i] + ((int64_t)min(PD, nstages - 1) * SK + kk) * 1024);
+  // stage s is multiplied from buffer s % 2 while stage s + 1 (register set
+  // (s + 1) % PD) is published into the other; nstages is a multiple of PD
   for (int s = 0; s < nstages; s += PD) {
 #pragma unroll
     for (int j = 0; j < PD; ++j)
       tiled_stage<TM, TN, WM, WN, SK, PD>(
-          min(s + j + PD, nstages - 1), st[j], src,
-          lds + ((s + j) & 1) * SK * C::NF * 64, wave, lane, a_off, w_off,
+          min(s + j + 1 + PD, nstages - 1), st[(j + 1) % PD], src,
+          lds + ((s + j) & 1) * SK * C::NF * 64,
+          lds + ((s + j + 1) & 1) * SK * C::NF * 64, wave, lane, a_off, w_off,
           acc);
   }
   // the last PD stages' refills (clamped repeats) are still in flight
 #pragma unroll
   for (int j = 0; j < PD; ++j)
 #pragma unroll
-    for (int i = 0; i < C::LPW * SK; ++i) vm_wait<0>(st[j][i]);
+    for (int i = 0; i < NL; ++i) vm_wait<0>(st[j][i]);
 
   // One copy of the epilogue code in a rolled loop; each tile is selected
   // out of the accumulators with compile-time indices (a dynamic index would
