@@ -2,7 +2,8 @@
 
 A plain, slow, float64 numpy statement of what one drafting step computes:
 feature fusion and KV injection, the single-pass (or S-pass) block draft, the
-LM-head reduction, confidence-ordered commit and greedy verification, plus the
+LM-head reduction, confidence-ordered commit, greedy verification and the
+speculative-sampling verification for temperature > 0, plus the
 accounting formulas the pages give (latency per token, the toy drafting race).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -25,7 +26,8 @@ from .numerics import (round_bf16, identity_round, rms_norm, silu, rope,
 from .drafter import (OracleModel, fuse_features, inject_kv, inject_rows,
                       block_attention, decoder_layer, lm_head_reduce,
                       confidence_commit, draft_sequence, draft_batch)
-from .verify import (verify_greedy, synthetic_target, expected_accept_len,
+from .verify import (verify_greedy, verify_sampling, sample_inverse_cdf,
+                     synthetic_target, expected_accept_len,
                      latency_per_token, simulate_rounds, toy_race_ratio,
                      simulate_toy_race)
 

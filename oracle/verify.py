@@ -1,4 +1,5 @@
-"""Greedy verification, the synthetic target, and the pages' accounting.
+"""Greedy and sampling verification, the synthetic target, and the pages'
+accounting.
 
 Oracle / test infrastructure.  Sources:
   * acceptance of the longest matching prefix plus one token from the target,
@@ -34,6 +35,62 @@ def verify_greedy(draft, target):
     while tau < len(draft) and draft[tau] == target[tau]:
         tau += 1
     return tau + 1, int(target[tau])
+
+
+def sample_inverse_cdf(w, u):
+    """Index drawn from the weights ``w`` (>= 0, not all zero) by inverse CDF
+    at the uniform ``u`` in [0, 1): the smallest x whose running sum, taken in
+    index order in float64, exceeds u times the total.  An index of weight 0
+    is never returned."""
+    w = np.asarray(w, dtype=np.float64)
+    c = np.cumsum(w)
+    x = int(np.searchsorted(c, float(u) * c[-1], side="right"))
+    return min(x, len(w) - 1)
+
+
+def verify_sampling(draft, q, p, u_accept, u_sample):
+    """Lossless speculative-sampling verification of one drafted block.
+
+    The pages say the target accepts the longest valid prefix by rejection
+    sampling, position by position, and that the output distribution stays
+    the target's exactly ("DFlash Guide", section "The Cost Breakdown of
+    Speculative Rounds"; stable-lab, "Common misconception").  They give no
+    formula; this is the published rule of speculative sampling (Leviathan,
+    Kalman and Matias 2023; Chen et al. 2023):
+
+      * drafted index j (1..K-1, row j-1 here) with token x is accepted when
+        u_j * q_j(x) < p_j(x), i.e. with probability min(1, p_j(x) / q_j(x));
+        the product of the two float32 inputs is exact in float64;
+      * at the first rejection the replacement token is drawn from the
+        normalised residual max(0, p_j - q_j) (float64 differences); when that
+        is zero everywhere, from p_j;
+      * when every draft is accepted the bonus token is drawn from p_K.
+
+    draft: [K-1] ids; q: [K-1, V] draft probabilities; p: [K, V] target
+    probabilities (row K-1 is the position after the block); u_accept: [K-1]
+    and u_sample: uniforms in [0, 1).  A drafted id outside [0, V) is
+    rejected.  Returns (accept_len = tau + 1, next token).
+    """
+    draft = np.asarray(draft)
+    q = np.asarray(q, dtype=np.float32)
+    p = np.asarray(p, dtype=np.float32)
+    k1, V = q.shape
+    tau = 0
+    while tau < k1:
+        x = int(draft[tau])
+        if not (0 <= x < V):
+            break
+        if float(np.float32(u_accept[tau])) * float(q[tau, x]) < float(p[tau, x]):
+            tau += 1
+        else:
+            break
+    if tau < k1:
+        w = np.maximum(p[tau].astype(np.float64) - q[tau].astype(np.float64), 0.0)
+        if not np.any(w > 0):
+            w = p[tau].astype(np.float64)
+    else:
+        w = p[k1].astype(np.float64)
+    return tau + 1, sample_inverse_cdf(w, np.float32(u_sample))
 
 
 def synthetic_target(draft, u, r, tail, p, vocab):
