@@ -27,8 +27,8 @@ DTYPE = {"f32": 0, "bf16": 1}
 LIB_SYMBOLS = ["dflash_create", "dflash_destroy", "dflash_kv_cache_bytes",
                "dflash_last_error", "dflash_check_device_errors",
                "dflash_inject_kv", "dflash_draft_block",
-               "dflash_verify_greedy", "dflash_set_kernel_timing",
-               "dflash_get_kernel_timing"]
+               "dflash_verify_greedy", "dflash_verify_sampling",
+               "dflash_set_kernel_timing", "dflash_get_kernel_timing"]
 TIME_KIND = {"off": 0, "lmhead": 1, "attention": 2, "gemm": 3}
 HARNESS_SYMBOLS = ["dflash_harness_synth_target"]
 
@@ -94,6 +94,9 @@ def load_library():
     lib.dflash_draft_block.restype = ctypes.c_int
     lib.dflash_verify_greedy.argtypes = [vp, i32, i32, vp, vp, vp, vp]
     lib.dflash_verify_greedy.restype = ctypes.c_int
+    lib.dflash_verify_sampling.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp,
+                                           vp, vp, vp]
+    lib.dflash_verify_sampling.restype = ctypes.c_int
     lib.dflash_set_kernel_timing.argtypes = [vp, i32]
     lib.dflash_set_kernel_timing.restype = ctypes.c_int
     lib.dflash_get_kernel_timing.argtypes = [vp, ctypes.POINTER(i32),
@@ -258,6 +261,31 @@ class DFlash:
         if st not in (DFLASH_OK, -4):
             _check(st)
         return bits.value
+
+
+def verify_sampling(draft: torch.Tensor, draft_probs: torch.Tensor,
+                    target_probs: torch.Tensor, u_accept: torch.Tensor,
+                    u_sample: torch.Tensor,
+                    accept: Optional[torch.Tensor] = None,
+                    next_token: Optional[torch.Tensor] = None, stream=None):
+    """Speculative-sampling verification (dflash_verify_sampling): draft
+    [B, K-1] int32, draft_probs [B, K-1, V] and target_probs [B, K, V] fp32,
+    u_accept [B, K-1] and u_sample [B] fp32, all contiguous on the device."""
+    lib = load_library()
+    B, K, V = target_probs.shape
+    for t in (draft, draft_probs, target_probs, u_accept, u_sample):
+        if not t.is_contiguous():
+            raise ValueError("verify_sampling needs contiguous tensors")
+    if accept is None:
+        accept = torch.empty(B, dtype=torch.int32, device=target_probs.device)
+    if next_token is None:
+        next_token = torch.empty(B, dtype=torch.int32,
+                                 device=target_probs.device)
+    _check(lib.dflash_verify_sampling(_stream(stream), B, K, V, _ptr(draft),
+                                      _ptr(draft_probs), _ptr(target_probs),
+                                      _ptr(u_accept), _ptr(u_sample),
+                                      _ptr(accept), _ptr(next_token)))
+    return accept, next_token
 
 
 def verify_greedy(draft: torch.Tensor, target: torch.Tensor,

@@ -753,4 +753,29 @@ dflash_status dflash_verify_greedy(void* stream, int32_t batch,
   return DFLASH_OK;
 }
 
+dflash_status dflash_verify_sampling(void* stream, int32_t batch,
+                                     int32_t block_size, int32_t vocab,
+                                     const int32_t* draft_tokens,
+                                     const float* draft_probs,
+                                     const float* target_probs,
+                                     const float* u_accept,
+                                     const float* u_sample,
+                                     int32_t* accept_len,
+                                     int32_t* next_token) {
+  g_last_error.clear();
+  if (batch < 1) return fail(DFLASH_E_SHAPE, "batch %d < 1", batch);
+  if (block_size < 2 || block_size > 64)
+    return fail(DFLASH_E_SHAPE, "block_size %d outside [2, 64]", block_size);
+  if (vocab < 1 || vocab > 262144)
+    return fail(DFLASH_E_SHAPE, "vocab %d outside [1, 262144]", vocab);
+  if (!draft_tokens || !draft_probs || !target_probs || !u_accept ||
+      !u_sample || !accept_len || !next_token)
+    return fail(DFLASH_E_INVALID, "NULL argument");
+  DF_HIP(launch_verify_sampling(batch, block_size, vocab, draft_tokens,
+                                draft_probs, target_probs, u_accept, u_sample,
+                                accept_len, next_token,
+                                static_cast<hipStream_t>(stream)));
+  return DFLASH_OK;
+}
+
 }  // extern "C"

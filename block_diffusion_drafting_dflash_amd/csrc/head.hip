@@ -115,6 +115,133 @@ __global__ void verify_kernel(int B, int K, const int32_t* draft,
   next_anchor[b] = t[tau];
 }
 
+// Speculative-sampling verification, one workgroup of 16 waves per sequence.
+// Wave 0 decides the acceptances.  The draw's weights are summed in
+// 64-element tiles (coalesced loads, a fixed butterfly per tile), the tiles
+// in index order within segments of 64 tiles, the segments in order; the draw
+// walks segments, tiles and the tile's elements in that order and takes the
+// first whose running sum exceeds u times the total (if rounding leaves the
+// target at the very end, the last entry of positive weight).
+constexpr int kSampWaves = 16;
+constexpr int kSampMaxTiles = 4096;  // vocab <= 262144
+
+__global__ __launch_bounds__(64 * kSampWaves) void verify_sampling_kernel(
+    int K, int V, const int32_t* draft, const float* q, const float* p,
+    const float* ua, const float* us, int32_t* accept, int32_t* next) {
+  __shared__ double ts[kSampMaxTiles];        // tile sums
+  __shared__ double seg[kSampMaxTiles / 64];  // segment sums
+  __shared__ int tau_s, tile_s, mode_s;
+  __shared__ double base_s, target_s;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int K1 = K - 1;
+  if (wave == 0) {
+    bool rej = false;
+    if (lane < K1) {
+      const int64_t o = (int64_t)b * K1 + lane;
+      const int x = draft[o];
+      if (x < 0 || x >= V) {
+        rej = true;
+      } else {
+        // u * q(x) < p(x): the product of two float32 values is exact in
+        // float64
+        const double qx = q[o * V + x];
+        const double px = p[((int64_t)b * K + lane) * V + x];
+        rej = !((double)ua[o] * qx < px);
+      }
+    }
+    const unsigned long long m = __ballot(rej);
+    if (lane == 0) tau_s = m ? __ffsll((long long)m) - 1 : K1;
+  }
+  __syncthreads();
+  const int tau = tau_s;
+  const float* prow = p + ((int64_t)b * K + min(tau, K1)) * V;
+  const float* qrow = q + ((int64_t)b * K1 + min(tau, K1 - 1)) * V;
+  const int ntiles = (V + 63) / 64, nseg = (ntiles + 63) / 64;
+  // mode 1: residual max(0, p - q) after a rejection; mode 0: p itself (all
+  // accepted, or a residual that is zero everywhere)
+  auto weight = [&](int mode, int i) -> double {
+    if (i >= V) return 0.0;
+    const double pv = prow[i];
+    return mode ? fmax(pv - (double)qrow[i], 0.0) : pv;
+  };
+  for (int mode = tau < K1 ? 1 : 0; mode >= 0; --mode) {
+    for (int t = wave; t < ntiles; t += kSampWaves) {
+      double v = weight(mode, t * 64 + lane);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+      if (lane == 0) ts[t] = v;
+    }
+    __syncthreads();
+    if (tid < nseg) {
+      const int t1 = min(ntiles, tid * 64 + 64);
+      double v = 0.0;
+      for (int t = tid * 64; t < t1; ++t) v += ts[t];
+      seg[tid] = v;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double total = 0.0;
+      for (int g = 0; g < nseg; ++g) total += seg[g];
+      tile_s = -1;
+      if (total > 0.0) {
+        const double t = (double)us[b] * total;
+        double run = 0.0, base = 0.0;
+        int gs = -1;
+        for (int g = 0; g < nseg; ++g) {
+          if (seg[g] > 0.0) {
+            gs = g;
+            base = run;
+            if (run + seg[g] > t) break;
+          }
+          run += seg[g];
+        }
+        run = base;
+        int ks = -1;
+        const int t1 = min(ntiles, gs * 64 + 64);
+        for (int k = gs * 64; k < t1; ++k) {
+          if (ts[k] > 0.0) {
+            ks = k;
+            base = run;
+            if (run + ts[k] > t) break;
+          }
+          run += ts[k];
+        }
+        tile_s = ks;
+        mode_s = mode;
+        base_s = base;
+        target_s = t;
+      }
+    }
+    __syncthreads();
+    if (tile_s >= 0) break;  // uniform
+  }
+  if (wave != 0) return;
+  if (tile_s < 0) {  // nothing to draw from
+    if (lane == 0) {
+      accept[b] = tau + 1;
+      next[b] = -1;
+    }
+    return;
+  }
+  const double w = weight(mode_s, tile_s * 64 + lane);
+  const double t = target_s;
+  double run = base_s;
+  int pick = -1, last = -1;
+  for (int k = 0; k < 64; ++k) {
+    const double wk = __shfl(w, k, 64);
+    if (wk > 0.0) {
+      last = k;
+      if (pick < 0 && run + wk > t) pick = k;
+    }
+    run += wk;
+  }
+  if (lane == 0) {
+    accept[b] = tau + 1;
+    next[b] = tile_s * 64 + (pick >= 0 ? pick : last);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_lm_merge(int rows, int ntiles, const Top2* part, Top2* part2,
@@ -132,6 +259,19 @@ hipError_t launch_commit(int B, int K, int n_cap, int commit, bool last,
   hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(64 * kCommitWaves), 0, s, K,
                      n_cap, commit, last ? 1 : 0, part, nrec, st, draft, conf,
                      margin);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_sampling(int B, int K, int V, const int32_t* draft,
+                                  const float* q, const float* p,
+                                  const float* u_accept, const float* u_sample,
+                                  int32_t* accept, int32_t* next,
+                                  hipStream_t s) {
+  if (K < 2 || K > 64 || V < 1 || (V + 63) / 64 > kSampMaxTiles)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(verify_sampling_kernel, dim3(B), dim3(64 * kSampWaves),
+                     0, s, K, V, draft, q, p, u_accept, u_sample, accept,
+                     next);
   return hipGetLastError();
 }
 

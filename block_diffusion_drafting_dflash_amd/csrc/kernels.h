@@ -185,6 +185,12 @@ hipError_t launch_commit(int B, int K, int n_cap, int commit, bool last,
                          const Top2* part, int nrec, BlockState st,
                          int32_t* draft, float* conf, float* margin,
                          hipStream_t s);
+// Speculative-sampling verification (see dflash_verify_sampling).
+hipError_t launch_verify_sampling(int B, int K, int V, const int32_t* draft,
+                                  const float* q, const float* p,
+                                  const float* u_accept, const float* u_sample,
+                                  int32_t* accept, int32_t* next,
+                                  hipStream_t s);
 hipError_t launch_verify(int B, int K, const int32_t* draft,
                          const int32_t* target, int32_t* accept,
                          int32_t* next_anchor, hipStream_t s);

@@ -14,7 +14,11 @@
  *                        passes);
  *   dflash_verify_greedy the accepted length is the longest prefix of the
  *                        draft that matches the target's greedy tokens, plus
- *                        one token from the target.
+ *                        one token from the target;
+ *   dflash_verify_sampling
+ *                        the same for sampled decoding (temperature > 0):
+ *                        lossless speculative-sampling acceptance against the
+ *                        draft's and the target's probabilities.
  *
  * Sources: "DFlash Guide: Block Diffusion for Speculative Decoding"
  * (aifetchly blog), "DFlash: Block Diffusion for Flash Speculative Decoding"
@@ -263,6 +267,54 @@ dflash_status dflash_verify_greedy(void* stream, int32_t batch,
                                    const int32_t* draft_tokens,
                                    const int32_t* target_argmax,
                                    int32_t* accept_len, int32_t* next_anchor);
+
+/* Speculative-sampling verification (sampled decoding, temperature > 0).
+ *
+ * Passage: "DFlash Guide", section "The Cost Breakdown of Speculative Rounds"
+ * (the target keeps the longest valid prefix of the draft by rejection
+ * sampling); stable-lab "Common misconception" (every drafted position must
+ * clear the target's acceptance rule, so the output distribution is exactly
+ * the target's).  The pages give no formula; this is the published rule of
+ * speculative sampling (Leviathan, Kalman and Matias 2023; Chen et al. 2023):
+ *   - drafted index j+1 with token x = draft_tokens[b][j] is accepted when
+ *     u_accept[b][j] * q[b][j][x] < p[b][j][x], the product of the two
+ *     float32 values taken exactly in float64; tau = the number of leading
+ *     accepted positions;
+ *   - if tau < K-1 the next token is drawn from the residual
+ *     max(0, p[b][tau] - q[b][tau]) (float64 differences; from p[b][tau]
+ *     itself when that residual is zero everywhere), else from p[b][K-1];
+ *   - a draw takes the smallest index whose running float64 sum exceeds
+ *     u_sample[b] times the total (never an index of weight zero).  The
+ *     running sum adds 64-element tiles (each summed by a fixed pairwise
+ *     tree) in index order, in segments of 64 tiles; at a boundary closer
+ *     than rounding it can differ from a single sequential sum, and either
+ *     index is a correct draw.  A distribution that is zero everywhere draws
+ *     -1.
+ * The drafter's own sampling (temperature, the draws that produced
+ * draft_tokens) is the caller's: this call only judges a block.
+ *
+ * draft_tokens: [batch, K-1] int32; an id outside [0, vocab) is rejected.
+ * draft_probs:  [batch, K-1, vocab] fp32 q, the draft distribution of each
+ *               drafted index (rows need not be normalised exactly).
+ * target_probs: [batch, K, vocab] fp32 p; row K-1 is the position after the
+ *               block (the bonus token).  Entries must be finite and >= 0.
+ * u_accept:     [batch, K-1] fp32 uniforms in [0, 1).
+ * u_sample:     [batch] fp32 uniform in [0, 1).
+ * accept_len:   [batch] int32 out, tau + 1 (1 <= accept_len <= K).
+ * next_token:   [batch] int32 out, the drawn replacement or bonus token.
+ * Needs no context; 2 <= block_size <= 64, 1 <= vocab <= 262144.  Reads at
+ * most two vocabulary rows per sequence beyond the K-1 gathered
+ * probabilities.
+ */
+dflash_status dflash_verify_sampling(void* stream, int32_t batch,
+                                     int32_t block_size, int32_t vocab,
+                                     const int32_t* draft_tokens,
+                                     const float* draft_probs,
+                                     const float* target_probs,
+                                     const float* u_accept,
+                                     const float* u_sample,
+                                     int32_t* accept_len,
+                                     int32_t* next_token);
 
 #ifdef __cplusplus
 }

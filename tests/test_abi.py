@@ -192,3 +192,18 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
             src = open(os.path.join(pkg, f)).read()
             assert not re.search(r"^\s*(from|import)\s+oracle", src, re.M), f
     assert "raise RuntimeError" in open(binding.__file__).read()
+
+
+@pytest.mark.parametrize("batch,block,vocab,null,status", [
+    (0, 16, 100, False, "DFLASH_E_SHAPE"),
+    (4, 1, 100, False, "DFLASH_E_SHAPE"),
+    (4, 65, 100, False, "DFLASH_E_SHAPE"),
+    (4, 16, 0, False, "DFLASH_E_SHAPE"),
+    (4, 16, 262145, False, "DFLASH_E_SHAPE"),
+    (4, 16, 100, True, "DFLASH_E_INVALID"),
+])
+def test_verify_sampling_validation(batch, block, vocab, null, status):
+    p = ctypes.c_void_p(16)
+    args = [None if null else p] + [p] * 6
+    st = lib().dflash_verify_sampling(None, batch, block, vocab, *args)
+    assert binding.STATUS[st] == status
