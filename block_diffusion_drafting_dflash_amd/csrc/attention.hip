@@ -381,12 +381,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
 
 template <typename T, int D, int G>
 hipError_t attn_t(int B, const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_partial_kernel<T, D, G>), dim3(a.nch, a.Hkv, B),
+  launch_k((attn_partial_kernel<T, D, G>), dim3(a.nch, a.Hkv, B),
                      dim3(64 * G), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = B * a.Hq * a.K;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3((rows + 3) / 4),
+  launch_k((attn_merge_kernel<T, D>), dim3((rows + 3) / 4),
                      dim3(256), 0, s, a, rows);
   return hipGetLastError();
 }

@@ -43,8 +43,18 @@ bool aligned16(const void* p) {
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr size_t kTimingSlots = 8192;
+// Timing events are bound to kernel dispatches and need no system-scope
+// fence.
+constexpr unsigned kTimingEventFlags = hipEventDisableSystemFence;
 
 }  // namespace
+
+namespace dflash {
+DispatchTiming& dispatch_timing() {
+  static thread_local DispatchTiming t;
+  return t;
+}
+}  // namespace dflash
 
 struct dflash_ctx {
   dflash_config cfg;
@@ -104,22 +114,20 @@ void free_events(dflash_ctx* c) {
   c->ev_next = c->ev_count = 0;
 }
 
-// Brackets one launch of the timed kernel class with an event pair.
+// Arms one event pair for the launches of the timed kernel class made in
+// its scope; the kernels bind the events to their dispatches (launch_k).
 struct TimedLaunch {
   dflash_ctx* c;
-  hipStream_t s;
-  size_t slot = 0;
   bool on = false;
-  TimedLaunch(dflash_ctx* ctx, int kind, hipStream_t st) : c(ctx), s(st) {
+  TimedLaunch(dflash_ctx* ctx, int kind, hipStream_t) : c(ctx) {
     if (c->time_kind == kind && !c->ev_start.empty()) {
       on = true;
-      slot = c->ev_next;
-      hipEventRecord(c->ev_start[slot], s);
+      dispatch_timing() = {c->ev_start[c->ev_next], c->ev_stop[c->ev_next]};
     }
   }
   ~TimedLaunch() {
     if (!on) return;
-    hipEventRecord(c->ev_stop[slot], s);
+    dispatch_timing() = {};
     c->ev_next = (c->ev_next + 1) % c->ev_start.size();
     if (c->ev_count < c->ev_start.size()) c->ev_count++;
   }
@@ -473,8 +481,8 @@ dflash_status dflash_set_kernel_timing(dflash_ctx* ctx, int32_t kind) {
   ctx->ev_start.resize(kTimingSlots);
   ctx->ev_stop.resize(kTimingSlots);
   for (size_t i = 0; i < kTimingSlots; ++i) {
-    if (hipEventCreate(&ctx->ev_start[i]) != hipSuccess ||
-        hipEventCreate(&ctx->ev_stop[i]) != hipSuccess) {
+    if (hipEventCreateWithFlags(&ctx->ev_start[i], kTimingEventFlags) != hipSuccess ||
+        hipEventCreateWithFlags(&ctx->ev_stop[i], kTimingEventFlags) != hipSuccess) {
       ctx->ev_start.resize(i);
       ctx->ev_stop.resize(i);
       free_events(ctx);

@@ -96,10 +96,12 @@ __global__ __launch_bounds__(256) void embed_kernel(
     const u32x4 gv = load16(g0 + c * EL);
     const T* vt = reinterpret_cast<const T*>(&v);
     const T* gt = reinterpret_cast<const T*>(&gv);
-    T* dst = reinterpret_cast<T*>(ob + packed_offset<T>(row, c * EL, D));
+    u32x4 o;  // the 16-byte chunk is built in registers, stored once
+    T* ot = reinterpret_cast<T*>(&o);
 #pragma unroll
     for (int e = 0; e < EL; ++e)
-      store_elem(dst, e, (double)load_elem(vt, e) * inv * (double)load_elem(gt, e));
+      store_elem(ot, e, (double)load_elem(vt, e) * inv * (double)load_elem(gt, e));
+    *reinterpret_cast<u32x4*>(ob + packed_offset<T>(row, c * EL, D)) = o;
   }
 }
 
@@ -152,11 +154,14 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(int rows, int D,
   for (int ci = 0; ci < kNormChunks; ++ci) {
     const int c = tid + ci * 256;
     if (c < nch) {
-      T* dst = reinterpret_cast<T*>(ob + packed_offset<T>(row, c * E, D));
+      const u32x4 gv = load16(g + c * E);
+      const T* gt = reinterpret_cast<const T*>(&gv);
+      u32x4 o;  // the 16-byte chunk is built in registers, stored once
+      T* ot = reinterpret_cast<T*>(&o);
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        store_elem(dst, e,
-                   (double)v[ci][e] * inv * (double)load_elem(g, c * E + e));
+        store_elem(ot, e, (double)v[ci][e] * inv * (double)load_elem(gt, e));
+      *reinterpret_cast<u32x4*>(ob + packed_offset<T>(row, c * E, D)) = o;
     }
   }
 }
@@ -245,7 +250,7 @@ hipError_t embed_t(int B, int K, int D, int V, int mask_id, int pass,
                    BlockState st, const void* embed, float* x,
                    int32_t* draft, const void* g0, float eps, void* h0,
                    hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel<T>, dim3(B * K), dim3(256), 0, s, K, D, V,
+  launch_k(embed_kernel<T>, dim3(B * K), dim3(256), 0, s, K, D, V,
                      mask_id, pass, n_cap, anchor, block_tokens, st,
                      static_cast<const T*>(embed), x, draft,
                      static_cast<const T*>(g0), eps, static_cast<T*>(h0));
@@ -273,23 +278,23 @@ hipError_t launch_rmsnorm(bool bf16, int rows, int D, const float* x,
   const int tiles = (rows + 15) / 16;
   if (tiles < 32 && D <= 256 * 4 * (bf16 ? 8 : 4)) {
     if (bf16)
-      hipLaunchKernelGGL(rmsnorm_row_kernel<bf16_t>, dim3(tiles * 16), dim3(256),
+      launch_k(rmsnorm_row_kernel<bf16_t>, dim3(tiles * 16), dim3(256),
                          0, s, rows, D, x, rowmap,
                          static_cast<const bf16_t*>(gain), eps,
                          static_cast<bf16_t*>(out));
     else
-      hipLaunchKernelGGL(rmsnorm_row_kernel<float>, dim3(tiles * 16), dim3(256),
+      launch_k(rmsnorm_row_kernel<float>, dim3(tiles * 16), dim3(256),
                          0, s, rows, D, x, rowmap,
                          static_cast<const float*>(gain), eps,
                          static_cast<float*>(out));
     return hipGetLastError();
   }
   if (bf16)
-    hipLaunchKernelGGL(rmsnorm_tile_kernel<bf16_t>, dim3(tiles), dim3(1024), 0,
+    launch_k(rmsnorm_tile_kernel<bf16_t>, dim3(tiles), dim3(1024), 0,
                        s, rows, D, x, rowmap, static_cast<const bf16_t*>(gain),
                        eps, static_cast<bf16_t*>(out));
   else
-    hipLaunchKernelGGL(rmsnorm_tile_kernel<float>, dim3(tiles), dim3(1024), 0,
+    launch_k(rmsnorm_tile_kernel<float>, dim3(tiles), dim3(1024), 0,
                        s, rows, D, x, rowmap, static_cast<const float*>(gain),
                        eps, static_cast<float*>(out));
   return hipGetLastError();

@@ -446,18 +446,18 @@ template <typename T, int AP>
 hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream_t s) {
   dim3 grid(pl.gx, pl.gy, 1), block(pl.waves * 64);
   if (pl.MT == 1 && a.ep == EP_TOP2)
-    hipLaunchKernelGGL(
+    launch_k(
         (gemm_kernel<T, 1, AP, DFLASH_LM_W, DFLASH_LM_U, false, false>), grid,
         block, 0, s, a);
   else if (pl.MT == 1)
-    hipLaunchKernelGGL((gemm_kernel<T, 1, AP, DFLASH_GEMM_W, DFLASH_GEMM_U,
+    launch_k((gemm_kernel<T, 1, AP, DFLASH_GEMM_W, DFLASH_GEMM_U,
                                     true, AP == 1>),
                        grid, block, 0, s, a);
   else if (pl.MT == 2)
-    hipLaunchKernelGGL((gemm_kernel<T, 2, AP, 4, 8, true, false>), grid, block,
+    launch_k((gemm_kernel<T, 2, AP, 4, 8, true, false>), grid, block,
                        0, s, a);
   else if (pl.MT == 4)
-    hipLaunchKernelGGL((gemm_kernel<T, 4, AP, 16, 2, true, false>), grid,
+    launch_k((gemm_kernel<T, 4, AP, 16, 2, true, false>), grid,
                        block, 0, s, a);
   else
     return hipErrorInvalidValue;
@@ -497,10 +497,10 @@ hipError_t launch_lm_head(bool bf16, int parts, const GemmArgs& a,
                           hipStream_t s) {
   if (parts <= 0 || !a.a_packed) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL((lm_head_kernel<bf16_t, kLmW, kLmNS>), dim3(parts),
+    launch_k((lm_head_kernel<bf16_t, kLmW, kLmNS>), dim3(parts),
                        dim3(64 * kLmW), 0, s, a);
   else
-    hipLaunchKernelGGL((lm_head_kernel<float, kLmW, kLmNS>), dim3(parts),
+    launch_k((lm_head_kernel<float, kLmW, kLmNS>), dim3(parts),
                        dim3(64 * kLmW), 0, s, a);
   return hipGetLastError();
 }
@@ -511,10 +511,10 @@ hipError_t launch_pack(bool bf16, const PackArgs& a, hipStream_t s) {
   int64_t blocks = (chunks + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (bf16)
-    hipLaunchKernelGGL(pack_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0,
+    launch_k(pack_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0,
                        s, a);
   else
-    hipLaunchKernelGGL(pack_kernel<float>, dim3((unsigned)blocks), dim3(256), 0,
+    launch_k(pack_kernel<float>, dim3((unsigned)blocks), dim3(256), 0,
                        s, a);
   return hipGetLastError();
 }

@@ -278,10 +278,10 @@ hipError_t tiled_t(const GemmArgs& a, hipStream_t s) {
   const int grid = (nbn + 7) / 8 * 8 * gm;
   const int nsteps = a.Kd / Storage<bf16_t>::KC;
   if (nsteps % (SK * PD) == 0)
-    hipLaunchKernelGGL((gemm_tiled_kernel<TM, TN, WM, WN, SK, PD>), dim3(grid),
+    launch_k((gemm_tiled_kernel<TM, TN, WM, WN, SK, PD>), dim3(grid),
                        dim3(64 * C::NW), 0, s, a, gm, nbn);
   else
-    hipLaunchKernelGGL((gemm_tiled_kernel<TM, TN, WM, WN, 1, 2>), dim3(grid),
+    launch_k((gemm_tiled_kernel<TM, TN, WM, WN, 1, 2>), dim3(grid),
                        dim3(64 * C::NW), 0, s, a, gm, nbn);
   return hipGetLastError();
 }
@@ -340,10 +340,10 @@ hipError_t launch_pack_act(bool bf16, const GemmArgs& a, void* dst,
   int64_t blocks = (chunks + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (bf16)
-    hipLaunchKernelGGL(pack_act_kernel<bf16_t>, dim3((unsigned)blocks),
+    launch_k(pack_act_kernel<bf16_t>, dim3((unsigned)blocks),
                        dim3(256), 0, s, a, dst);
   else
-    hipLaunchKernelGGL(pack_act_kernel<float>, dim3((unsigned)blocks),
+    launch_k(pack_act_kernel<float>, dim3((unsigned)blocks),
                        dim3(256), 0, s, a, dst);
   return hipGetLastError();
 }

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(64 * kSampWaves) void verify_sampling_kernel(
 
 hipError_t launch_lm_merge(int rows, int ntiles, const Top2* part, Top2* part2,
                            hipStream_t s) {
-  hipLaunchKernelGGL(lm_merge_kernel, dim3(rows * kMergeChunks), dim3(256), 0,
+  launch_k(lm_merge_kernel, dim3(rows * kMergeChunks), dim3(256), 0,
                      s, ntiles, part, part2);
   return hipGetLastError();
 }
@@ -256,7 +256,7 @@ hipError_t launch_commit(int B, int K, int n_cap, int commit, bool last,
                          int32_t* draft, float* conf, float* margin,
                          hipStream_t s) {
   if (K > 64 || nrec < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(64 * kCommitWaves), 0, s, K,
+  launch_k(commit_kernel, dim3(B), dim3(64 * kCommitWaves), 0, s, K,
                      n_cap, commit, last ? 1 : 0, part, nrec, st, draft, conf,
                      margin);
   return hipGetLastError();
@@ -269,7 +269,7 @@ hipError_t launch_verify_sampling(int B, int K, int V, const int32_t* draft,
                                   hipStream_t s) {
   if (K < 2 || K > 64 || V < 1 || (V + 63) / 64 > kSampMaxTiles)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(verify_sampling_kernel, dim3(B), dim3(64 * kSampWaves),
+  launch_k(verify_sampling_kernel, dim3(B), dim3(64 * kSampWaves),
                      0, s, K, V, draft, q, p, u_accept, u_sample, accept,
                      next);
   return hipGetLastError();
@@ -278,7 +278,7 @@ hipError_t launch_verify_sampling(int B, int K, int V, const int32_t* draft,
 hipError_t launch_verify(int B, int K, const int32_t* draft,
                          const int32_t* target, int32_t* accept,
                          int32_t* next_anchor, hipStream_t s) {
-  hipLaunchKernelGGL(verify_kernel, dim3((B + 63) / 64), dim3(64), 0, s, B, K,
+  launch_k(verify_kernel, dim3((B + 63) / 64), dim3(64), 0, s, B, K,
                      draft, target, accept, next_anchor);
   return hipGetLastError();
 }

@@ -1,12 +1,33 @@
 // Internal launch interface between the host library and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "common.h"
 
 namespace dflash {
+
+// Benchmark timing of one kernel class.  While a pair of events is armed,
+// every launch made through launch_k binds them to its own dispatch: the
+// first launch of the span takes the start event, each launch takes the stop
+// event (the last one wins), so the pair brackets the class's kernels without
+// any event packet of its own entering the stream.
+struct DispatchTiming {
+  hipEvent_t start = nullptr;  // taken by the next launch
+  hipEvent_t stop = nullptr;
+};
+DispatchTiming& dispatch_timing();  // per host thread
+
+template <typename F, typename... Args>
+inline void launch_k(F kernel, dim3 grid, dim3 block, uint32_t shm,
+                     hipStream_t s, Args... args) {
+  DispatchTiming& t = dispatch_timing();
+  hipExtLaunchKernelGGL(kernel, grid, block, shm, s, t.start, t.stop, 0u,
+                        args...);
+  t.start = nullptr;
+}
 
 constexpr int kMaxASeg = 8;
 constexpr int kMaxBSeg = 16;
