@@ -243,6 +243,150 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(GemmArgs p,
   }
 }
 
+// Direct-to-LDS form.  Each wave's fragment loads go from global memory
+// straight into a ring of NBUF contraction steps in LDS (no staging
+// registers, no LDS stores), so NBUF - 1 steps are in flight per workgroup.
+// The load is inline assembly: the compiler's wait insertion would drain
+// every in-flight load before each LDS read.  m0 carries the fragment's LDS
+// byte address and lane l's 16 bytes land at m0 + 16 l, which is the packed
+// fragment layout itself; nothing else in these kernels uses m0.
+__device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// The ring holds steps s + 1 .. s + NBUF while step s is multiplied: step s
+// is multiplied from registers read out of the ring one step earlier, so the
+// LDS reads of step s + 1 overlap the MFMAs of step s.  Iteration s waits
+// until this wave's loads of step s + 1 have landed (later steps may still
+// be in flight), one barrier (every wave's part of step s + 1 is visible and
+// every wave has read step s), refills step s's slot with step s + NBUF,
+// reads step s + 1 and multiplies step s.
+template <int TM, int TN, int WM, int WN, int NBUF>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
+                                                                int gm,
+                                                                int nbn) {
+  using C = Tiled<TM, TN, WM, WN>;
+  constexpr int STAGE = C::NF * 64;  // u32x4 per contraction step
+  __shared__ u32x4 lds[NBUF * STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.x, xcd = b & 7, k = b >> 3;
+  const int mb = k % gm, nb = (k / gm) * 8 + xcd;
+  if (nb >= nbn) return;  // whole workgroup: padding of the XCD mapping
+  const int nsteps = p.Kd / Storage<bf16_t>::KC;
+  const int mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // fragment f = wave + i NW of a step, as in gemm_tiled_kernel
+  const char* src[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int f = wave + i * C::NW;
+    int t;
+    const char* base;
+    if (f < C::BMT) {
+      t = min(mb * C::BMT + f, mtiles - 1);
+      base = static_cast<const char*>(p.a_ptr[0]);
+    } else {
+      t = min(nb * C::BNT + f - C::BMT, ntiles - 1);
+      base = static_cast<const char*>(p.w);
+    }
+    src[i] = base + ((int64_t)t * nsteps * 64 + lane) * 16;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(
+      __attribute__((address_space(3))) void*)lds;
+  // step `step` (clamped: repeats past the end are never multiplied) into
+  // ring slot `slot`
+  auto issue = [&](int step, int slot) {
+    const int64_t off = (int64_t)min(step, nsteps - 1) * 1024;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i)
+      lds_load16(src[i] + off,
+                 lds0 + (uint32_t)((slot * C::NF + wave + i * C::NW) * 1024));
+  };
+  const int lo = ((lane >> 4) & 1) * 64 + (lane >> 5) * 16 + (lane & 15);
+  const int a_off = wm * TM * 128 + lo;
+  const int w_off = (C::BMT + wn * TN * 2) * 64 + lo;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int m = 0; m < TM; ++m)
+#pragma unroll
+    for (int n = 0; n < TN; ++n)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[m][n][j] = 0.f;
+
+  // operands of one step: A then W fragments of both half-steps
+  using Ops = u32x4[2 * (TM + TN)];
+  auto read = [&](Ops& r, int slot) {
+    const u32x4* cur = lds + slot * STAGE;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int m = 0; m < TM; ++m)
+        r[h * (TM + TN) + m] = cur[a_off + m * 128 + 32 * h];
+#pragma unroll
+      for (int n = 0; n < TN; ++n)
+        r[h * (TM + TN) + TM + n] = cur[w_off + n * 128 + 32 * h];
+    }
+  };
+  auto mul = [&](const Ops& r) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < TN; ++n)
+          mma32(acc[m][n], r[h * (TM + TN) + m], r[h * (TM + TN) + TM + n]);
+  };
+  // one iteration; r_now holds step s, r_next receives step s + 1
+  auto iter = [&](int s, const Ops& r_now, Ops& r_next) {
+    vm_wait_n<(NBUF - 2) * C::LPW>();
+    __syncthreads();
+    issue(s + NBUF, s % NBUF);
+    read(r_next, (s + 1) % NBUF);
+    // keep the reads of step s + 1 ahead of the MFMAs of step s
+    __builtin_amdgcn_sched_barrier(0);
+    mul(r_now);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+#pragma unroll
+  for (int j = 0; j < NBUF; ++j) issue(j, j);
+  Ops r0, r1;
+  vm_wait_n<(NBUF - 1) * C::LPW>();
+  __syncthreads();
+  read(r0, 0);
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    iter(s, r0, r1);
+    iter(s + 1, r1, r0);
+  }
+  if (s < nsteps) mul(r0);  // odd step count: the last step
+  vm_wait_n<0>();  // the clamped refills past the last step
+
+#pragma unroll 1
+  for (int t = 0; t < TM * TN; ++t) {
+    const int m = t / TN, n = t % TN;
+    const int row0 = (mb * C::BMT + (wm * TM + m) * 2) * 16;
+    const int ctile = nb * C::BNT + (wn * TN + n) * 2;
+    f32x16 v = acc[0][0];
+#pragma unroll
+    for (int mm = 0; mm < TM; ++mm)
+#pragma unroll
+      for (int nn = 0; nn < TN; ++nn)
+        if (t == mm * TN + nn) v = acc[mm][nn];
+    if (ctile < ntiles && row0 < p.M) tile_epilogue(p, row0, ctile, v, lane);
+  }
+}
+
 // Row-major activation segments (the concatenated target layers) -> packed
 // rows; rows from M up to the next multiple of 16 are zero.
 template <typename T>
@@ -298,16 +442,46 @@ hipError_t tiled_t(const GemmArgs& a, hipStream_t s) {
 #ifndef DFLASH_T128_PD
 #define DFLASH_T128_PD 2
 #endif
+template <int TM, int TN, int WM, int WN, int NBUF>
+hipError_t dma_t(const GemmArgs& a, hipStream_t s) {
+  using C = Tiled<TM, TN, WM, WN>;
+  const int gm = (a.M + 16 * C::BMT - 1) / (16 * C::BMT);
+  const int nbn = (a.N / 16 + C::BNT - 1) / C::BNT;
+  const int grid = (nbn + 7) / 8 * 8 * gm;
+  launch_k((gemm_dma_kernel<TM, TN, WM, WN, NBUF>), dim3(grid),
+           dim3(64 * C::NW), 0, s, a, gm, nbn);
+  return hipGetLastError();
+}
+
+#ifndef DFLASH_TILED_DMA
+#define DFLASH_TILED_DMA 1
+#endif
+#ifndef DFLASH_D64_NBUF
+#define DFLASH_D64_NBUF 8
+#endif
+#ifndef DFLASH_D128_NBUF
+#define DFLASH_D128_NBUF 4
+#endif
 hipError_t tiled_cfg(int cfg, const GemmArgs& a, hipStream_t s) {
   switch (cfg) {
     case TILE_64x64:
+      if (DFLASH_TILED_DMA) return dma_t<1, 1, 2, 2, DFLASH_D64_NBUF>(a, s);
       return tiled_t<1, 1, 2, 2, DFLASH_T64_SK, DFLASH_T64_PD>(a, s);
     case TILE_128x128:
+      if (DFLASH_TILED_DMA) return dma_t<2, 2, 2, 2, DFLASH_D128_NBUF>(a, s);
       return tiled_t<2, 2, 2, 2, DFLASH_T128_SK, DFLASH_T128_PD>(a, s);
-    case TILE_256x64: return tiled_t<4, 1, 2, 2, 2, 2>(a, s);
-    case TILE_256x128: return tiled_t<4, 2, 2, 2, 2, 1>(a, s);
-    case TILE_128x256: return tiled_t<2, 4, 2, 2, 2, 1>(a, s);
-    case TILE_256x256: return tiled_t<4, 2, 2, 4, 2, 2>(a, s);
+    case TILE_256x64:
+      if (DFLASH_TILED_DMA) return dma_t<4, 1, 2, 2, 4>(a, s);
+      return tiled_t<4, 1, 2, 2, 2, 2>(a, s);
+    case TILE_256x128:
+      if (DFLASH_TILED_DMA) return dma_t<4, 2, 2, 2, 4>(a, s);
+      return tiled_t<4, 2, 2, 2, 2, 1>(a, s);
+    case TILE_128x256:
+      if (DFLASH_TILED_DMA) return dma_t<2, 4, 2, 2, 4>(a, s);
+      return tiled_t<2, 4, 2, 2, 2, 1>(a, s);
+    case TILE_256x256:
+      if (DFLASH_TILED_DMA) return dma_t<4, 2, 2, 4, 4>(a, s);
+      return tiled_t<4, 2, 2, 4, 2, 2>(a, s);
   }
   return hipErrorInvalidValue;
 }
