@@ -293,6 +293,32 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
 
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
+  if (p.nch == 1) {
+    // One chunk holds the whole softmax: normalise here with the merge's
+    // arithmetic (float64 quotient, one rounding to the storage type, the
+    // same bits) and write the packed output; no merge runs.
+    const double inv = 1.0 / (double)l_tot;
+    const int row = b * p.K + r, Kd = p.Hq * D;
+    char* ob = static_cast<char*>(p.o);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      char* dst = ob + packed_offset<T>(row, hq * D + 16 * dt + 4 * g, Kd);
+      if constexpr (SZ == 2) {
+        u32x2 w;
+        T* wt = reinterpret_cast<T*>(&w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_elem(wt, e, (double)o[dt][e] * inv);
+        *reinterpret_cast<u32x2*>(dst) = w;
+      } else {
+        u32x4 w;
+        T* wt = reinterpret_cast<T*>(&w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_elem(wt, e, (double)o[dt][e] * inv);
+        *reinterpret_cast<u32x4*>(dst) = w;
+      }
+    }
+    return;
+  }
   // partials are chunk-major within (sequence, query head, query):
   // part_o[((b*Hq + hq)*K + i)*nch + c][D], part_ml[... same index][2]
   const int64_t base = (((int64_t)b * p.Hq + hq) * p.K + r) * p.nch + c;
@@ -385,6 +411,7 @@ hipError_t attn_t(int B, const AttnArgs& a, hipStream_t s) {
                      dim3(64 * G), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.nch == 1) return hipSuccess;  // the partial kernel normalised
   const int rows = B * a.Hq * a.K;
   launch_k((attn_merge_kernel<T, D>), dim3((rows + 3) / 4),
                      dim3(256), 0, s, a, rows);

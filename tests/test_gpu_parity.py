@@ -162,7 +162,8 @@ def _seeded_cache(wl, ctx, lens):
     return kv, per_seq
 
 
-def _gpu_draft(ctx, wl, lens, kv, anchors=None, block=None, S=1, c=0):
+def _gpu_draft(ctx, wl, lens, kv, anchors=None, block=None, S=1, c=0,
+               max_len=None):
     B = len(lens)
     K1 = wl.block_size - 1
     draft = torch.full((B, K1), -7, dtype=torch.int32, device=DEV)
@@ -171,7 +172,7 @@ def _gpu_draft(ctx, wl, lens, kv, anchors=None, block=None, S=1, c=0):
     logits = torch.full((S, B, K1, wl.vocab), float("nan"), device=DEV)
     ctx.draft_block(
         torch.from_numpy(np.asarray(lens, np.int32)).to(DEV), kv,
-        int(max(lens)),
+        int(max(lens)) if max_len is None else int(max_len),
         anchor=None if anchors is None else torch.from_numpy(
             np.asarray(anchors, np.int32)).to(DEV),
         block_tokens=None if block is None else torch.from_numpy(
@@ -294,6 +295,31 @@ def test_draft_edge_context_lengths():
     comp, excl, dl = compare_draft(wl, g, ref)
     say(f"  tokens compared {comp}, excluded {excl}, max |dlogit| {dl:.2e}")
     assert comp > 0
+
+
+def test_draft_single_chunk_attention():
+    """Contexts of at most 112 keys: with the 16 block keys every sequence
+    fits one attention chunk, so the partial kernel normalises and writes the
+    output itself and no merge runs.  Checked against the oracle, and
+    bit for bit against the merge path (a larger length bound gives several
+    chunks, of which each of these sequences fills only the first)."""
+    wl = W.small_bf16(batch=4, name="small-bf16-1chunk")
+    lens = np.array([0, 5, 64, 112], dtype=np.int32)
+    say(f"[draft one chunk] lens {lens.tolist()}")
+    w_cpu, w_dev, ctx = _setup(wl, random_gains=True)
+    model = OracleModel(wl, w_cpu)
+    kv, per_seq = _seeded_cache(wl, ctx, lens)
+    anchors = W.gen_anchors(wl)
+    g = _gpu_draft(ctx, wl, lens, kv, anchors=anchors)
+    ref = draft_batch(model, per_seq, lens, anchors=anchors, keep_logits=True)
+    g["logits"] = g["logits_all"][0]
+    comp, excl, dl = compare_draft(wl, g, ref)
+    say(f"  tokens compared {comp}, excluded {excl}, max |dlogit| {dl:.2e}")
+    assert comp > 0
+    merged = _gpu_draft(ctx, wl, lens, kv, anchors=anchors,
+                        max_len=wl.ctx_max)
+    for k in ("draft", "conf", "margin", "logits_all"):
+        np.testing.assert_array_equal(g[k], merged[k])
 
 
 def test_draft_is_deterministic():
