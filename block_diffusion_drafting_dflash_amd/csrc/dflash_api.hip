@@ -203,11 +203,15 @@ int attn_chunk(int B, int Hkv, int max_keys, int num_cu) {
 #ifndef DFLASH_PACK_ROWMAJOR
 #define DFLASH_PACK_ROWMAJOR 1
 #endif
+bool gemm_is_tiled(const dflash_ctx* c, const GemmArgs& a) {
+  return c->bf16 && (a.M > 64 || (a.ep == EP_TOP2 && a.M > 16));
+}
+
 dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
                        int kind = DFLASH_TIME_GEMM) {
   a.err = c->err;
   const bool lm = a.ep == EP_TOP2;
-  const bool tiled = c->bf16 && (a.M > 64 || (lm && a.M > 16));
+  const bool tiled = gemm_is_tiled(c, a);
   if (!a.a_packed && (tiled || DFLASH_PACK_ROWMAJOR)) {
     // row-major activations (the target hidden states): pack once, so every
     // workgroup's operand loads are whole 1 KiB fragments
@@ -725,21 +729,29 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
     hd.logits_ld = V;
     hd.err = ctx->err;
     const int parts = lm_head_parts(bf, Mh, V, D, ctx->num_cu);
+    // records per row for the commit kernel: one per workgroup of the
+    // persistent head, one per column block of the tiled head (both merged
+    // by the commit kernel itself); the per-tile records of the streaming
+    // form are merged to kMergeChunks per row first
+    const Top2* recs = ctx->lm_part;
+    int nrec = 0;
     if (parts > 0) {
       TimedLaunch tl(ctx, DFLASH_TIME_LMHEAD, s);
       DF_HIP(launch_lm_head(bf, parts, hd, s));
+      nrec = parts;
     } else {
       dflash_status st = run_gemm(ctx, hd, s, DFLASH_TIME_LMHEAD);
       if (st != DFLASH_OK) return st;
+      if (gemm_is_tiled(ctx, hd)) {
+        nrec = tiled_top2_records(plan_tiled(Mh, V), V);
+      } else {
+        DF_HIP(launch_lm_merge(Mh, V / 16, ctx->lm_part, ctx->lm_part2, s));
+        recs = ctx->lm_part2;
+        nrec = kMergeChunks;
+      }
     }
-    // the persistent head leaves one record per row and workgroup, which
-    // the commit kernel merges itself; per-tile records are merged first
-    if (parts == 0)
-      DF_HIP(launch_lm_merge(Mh, V / 16, ctx->lm_part, ctx->lm_part2, s));
-    DF_HIP(launch_commit(batch, K, n_cap, commit_per_pass, last,
-                         parts > 0 ? ctx->lm_part : ctx->lm_part2,
-                         parts > 0 ? parts : kMergeChunks, bs, draft_tokens,
-                         confidence, top2_margin, s));
+    DF_HIP(launch_commit(batch, K, n_cap, commit_per_pass, last, recs, nrec,
+                         bs, draft_tokens, confidence, top2_margin, s));
   }
   return DFLASH_OK;
 }

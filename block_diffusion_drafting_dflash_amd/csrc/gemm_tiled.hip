@@ -6,14 +6,12 @@
 // over the whole contraction; each wave owns TM x TN tiles of 32 x 32 and
 // runs the 32x32x16 MFMA (on gfx950 it has twice the throughput of the
 // 16x16x32 form).  Operands are packed fragment-major (1 KiB per 16 rows x
-// one 32-wide contraction step), so staging a step into LDS is one
-// contiguous 1 KiB load per fragment; a 32-row MFMA operand is read back as
-// 16 bytes per lane from two fragments.  PD steps are kept in flight in
-// registers ahead of the double-buffered LDS stage the MFMAs read, with one
-// barrier per step.  Each wave applies the epilogue to its own tiles
-// straight from the accumulators (partner columns for RoPE and SwiGLU come
-// from the lane 8 apart), so the block never round-trips its output through
-// LDS.
+// one 32-wide contraction step), and each fragment goes from global memory
+// straight into a ring of contraction steps in LDS (see gemm_dma_kernel).
+// The projection epilogues run per wave on its own tiles straight from the
+// accumulators (partner columns for RoPE and SwiGLU come from the lane 8
+// apart); the LM head's top-2 reduction parks the block's logits in LDS and
+// scans each row.
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the mapping below
 // gives the row blocks of one column block workgroup ids 8 apart, so they
@@ -46,25 +44,6 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, int row0,
     }
     return;
   }
-  if (p.ep == EP_TOP2) {
-    const int col = tile * 16 + c;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int row = rbase + 8 * (j >> 2) + (j & 3);
-      Top2 v = top2_empty();
-      if (row < p.M && tile_ok) {
-        v.m1 = acc[j];
-        v.i1 = col;
-        v.s = 1.f;
-        if (p.logits != nullptr) store_debug_logit(p, row, col, acc[j]);
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) v = top2_merge(v, top2_shfl_xor(v, o));
-      if (c == 0 && row < p.M && tile_ok)
-        p.top2[(int64_t)row * (p.N / 16) + tile] = v;
-    }
-    return;
-  }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const float partner = __shfl_xor(acc[j], 8, 64);
@@ -86,160 +65,55 @@ struct Tiled {
   static_assert(NF % NW == 0, "fragments must split evenly over the waves");
 };
 
-// One LDS stage = SK contraction steps, multiplied from LDS buffer `cur`
-// (published during the previous stage).  After the first half-step's MFMAs
-// the staged registers of the next stage (loaded PD stages ago: the PD - 1
-// later stages' loads may still be in flight) are waited for and published
-// into the other buffer `nxt` while the remaining MFMAs run; one barrier
-// then makes them visible and frees `cur`, and the same registers are
-// refilled PD stages ahead.  The refill is unconditional (clamped to the last
-// stage), so the loop is straight-line code.
-template <int TM, int TN, int WM, int WN, int SK, int PD>
-__device__ __forceinline__ void tiled_stage(
-    int refill, u32x4 (&st)[Tiled<TM, TN, WM, WN>::LPW * SK],
-    const char* const (&src)[Tiled<TM, TN, WM, WN>::LPW], const u32x4* cur,
-    u32x4* nxt, int wave, int lane, int a_off, int w_off,
-    f32x16 (&acc)[TM][TN]) {
-  using C = Tiled<TM, TN, WM, WN>;
-  constexpr int NL = C::LPW * SK;  // loads per stage per lane
-  // step k, half h: contraction 32k + 16h .. + 16
-#pragma unroll
-  for (int k = 0; k < SK; ++k)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 a[TM], w[TN];
-#pragma unroll
-      for (int m = 0; m < TM; ++m)
-        a[m] = cur[k * C::NF * 64 + a_off + m * 128 + 32 * h];
-#pragma unroll
-      for (int n = 0; n < TN; ++n)
-        w[n] = cur[k * C::NF * 64 + w_off + n * 128 + 32 * h];
-#pragma unroll
-      for (int m = 0; m < TM; ++m)
-#pragma unroll
-        for (int n = 0; n < TN; ++n) mma32(acc[m][n], a[m], w[n]);
-      if (k == 0 && h == 0) {
-        stage_wait<0, NL, (PD - 1) * NL>(st);
-#pragma unroll
-        for (int kk = 0; kk < SK; ++kk)
-#pragma unroll
-          for (int i = 0; i < C::LPW; ++i)
-            nxt[(kk * C::NF + wave + i * C::NW) * 64 + lane] =
-                st[kk * C::LPW + i];
-      }
-    }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < SK; ++k)
-#pragma unroll
-    for (int i = 0; i < C::LPW; ++i)
-      st[k * C::LPW + i] =
-          stage_load(src[i] + ((int64_t)refill * SK + k) * 1024);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-template <int TM, int TN, int WM, int WN, int SK, int PD>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(GemmArgs p,
-                                                                  int gm,
-                                                                  int nbn) {
-  using C = Tiled<TM, TN, WM, WN>;
-  __shared__ u32x4 lds[2 * SK * C::NF * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.x, xcd = b & 7, k = b >> 3;
-  const int mb = k % gm, nb = (k / gm) * 8 + xcd;
-  if (nb >= nbn) return;  // whole workgroup: padding of the XCD mapping
-  const int nsteps = p.Kd / Storage<bf16_t>::KC;
-  const int nstages = nsteps / SK;
-  const int mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
-  const int wm = wave / WN, wn = wave % WN;
-
-  // fragment f of a step: row tile mb*BMT + f of A, else column tile
-  // nb*BNT + f - BMT of W (clamped; clamped tiles are never stored)
-  const char* src[C::LPW];
-#pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    const int f = wave + i * C::NW;
-    int t;
-    const char* base;
-    if (f < C::BMT) {
-      t = min(mb * C::BMT + f, mtiles - 1);
-      base = static_cast<const char*>(p.a_ptr[0]);
+// LM-head reduction of one block of logits parked in LDS (L: BM rows of
+// BN + 1 floats; the odd row stride makes a wave's column reads hit 64
+// different banks).  NT threads, NT / BM per row: thread t scans row t % BM,
+// its part t / BM of the columns, in increasing column order keeping (max,
+// its lowest index, second max, sum of exp(z - max)); the parts are then
+// merged in order and the row's record for this column block written:
+// top2[row * nrec + rec].  Columns past N (the ragged last block) are
+// skipped, rows past M are not written.
+template <int BM, int BN, int NT>
+__device__ __forceinline__ void top2_block(const GemmArgs& p, const float* L,
+                                           int row0, int col0, int rec,
+                                           int nrec) {
+  static_assert(NT % BM == 0, "whole rows per thread group");
+  constexpr int TPR = NT / BM, CPT = BN / TPR;
+  __shared__ Top2 part[NT];
+  const int t = threadIdx.x, r = t % BM, q = t / BM;
+  const int row = row0 + r;
+  const bool row_ok = row < p.M;
+  float m1 = -INFINITY, m2 = -INFINITY, sum = 0.f;
+  int i1 = 0x7fffffff;
+  const float* lr = L + r * (BN + 1) + q * CPT;
+  const int cbase = col0 + q * CPT;
+#pragma unroll 8
+  for (int i = 0; i < CPT; ++i) {
+    const int col = cbase + i;
+    if (col >= p.N) break;
+    const float z = lr[i];
+    if (z > m1) {
+      sum = sum * __expf(m1 - z) + 1.f;
+      m2 = m1;
+      m1 = z;
+      i1 = col;
     } else {
-      t = min(nb * C::BNT + f - C::BMT, ntiles - 1);
-      base = static_cast<const char*>(p.w);
+      m2 = fmaxf(m2, z);
+      sum += __expf(z - m1);
     }
-    src[i] = base + ((int64_t)t * nsteps * 64 + lane) * 16;
+    if (p.logits != nullptr && row_ok) store_debug_logit(p, row, col, z);
   }
-  // this lane's 16 bytes of a 32-row operand: fragment (lane / 16) % 2 of
-  // the pair, contraction group 2h + lane / 32, row lane % 16
-  const int lo = ((lane >> 4) & 1) * 64 + (lane >> 5) * 16 + (lane & 15);
-  const int a_off = wm * TM * 128 + lo;
-  const int w_off = (C::BMT + wn * TN * 2) * 64 + lo;
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int m = 0; m < TM; ++m)
-#pragma unroll
-    for (int n = 0; n < TN; ++n)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[m][n][j] = 0.f;
-
-  constexpr int NL = C::LPW * SK;
-  u32x4 st[PD][NL];
-#pragma unroll
-  for (int j = 0; j < PD; ++j)
-#pragma unroll
-    for (int kk = 0; kk < SK; ++kk)
-#pragma unroll
-      for (int i = 0; i < C::LPW; ++i)
-        st[j][kk * C::LPW + i] = stage_load(
-            src[i] + ((int64_t)min(j, nstages - 1) * SK + kk) * 1024);
-  // stage 0 into buffer 0; its registers then take stage PD
-  stage_wait<0, NL, (PD - 1) * NL>(st[0]);
-#pragma unroll
-  for (int kk = 0; kk < SK; ++kk)
-#pragma unroll
-    for (int i = 0; i < C::LPW; ++i)
-      lds[(kk * C::NF + wave + i * C::NW) * 64 + lane] = st[0][kk * C::LPW + i];
+  Top2 v;
+  v.m1 = m1;
+  v.i1 = i1;
+  v.m2 = m2;
+  v.s = sum;
+  part[t] = v;
   __syncthreads();
+  if (q == 0 && row_ok) {
 #pragma unroll
-  for (int kk = 0; kk < SK; ++kk)
-#pragma unroll
-    for (int i = 0; i < C::LPW; ++i)
-      st[0][kk * C::LPW + i] = stage_load(
-          src[i] + ((int64_t)min(PD, nstages - 1) * SK + kk) * 1024);
-  // stage s is multiplied from buffer s % 2 while stage s + 1 (register set
-  // (s + 1) % PD) is published into the other; nstages is a multiple of PD
-  for (int s = 0; s < nstages; s += PD) {
-#pragma unroll
-    for (int j = 0; j < PD; ++j)
-      tiled_stage<TM, TN, WM, WN, SK, PD>(
-          min(s + j + 1 + PD, nstages - 1), st[(j + 1) % PD], src,
-          lds + ((s + j) & 1) * SK * C::NF * 64,
-          lds + ((s + j + 1) & 1) * SK * C::NF * 64, wave, lane, a_off, w_off,
-          acc);
-  }
-  // the last PD stages' refills (clamped repeats) are still in flight
-#pragma unroll
-  for (int j = 0; j < PD; ++j)
-#pragma unroll
-    for (int i = 0; i < NL; ++i) vm_wait<0>(st[j][i]);
-
-  // One copy of the epilogue code in a rolled loop; each tile is selected
-  // out of the accumulators with compile-time indices (a dynamic index would
-  // move the whole accumulator array to scratch memory).
-#pragma unroll 1
-  for (int t = 0; t < TM * TN; ++t) {
-    const int m = t / TN, n = t % TN;
-    const int row0 = (mb * C::BMT + (wm * TM + m) * 2) * 16;
-    const int ctile = nb * C::BNT + (wn * TN + n) * 2;
-    f32x16 v = acc[0][0];
-#pragma unroll
-    for (int mm = 0; mm < TM; ++mm)
-#pragma unroll
-      for (int nn = 0; nn < TN; ++nn)
-        if (t == mm * TN + nn) v = acc[mm][nn];
-    if (ctile < ntiles && row0 < p.M) tile_epilogue(p, row0, ctile, v, lane);
+    for (int k = 1; k < TPR; ++k) v = top2_merge(v, part[t + k * BM]);
+    p.top2[(int64_t)row * nrec + rec] = v;
   }
 }
 
@@ -274,7 +148,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
                                                                 int nbn) {
   using C = Tiled<TM, TN, WM, WN>;
   constexpr int STAGE = C::NF * 64;  // u32x4 per contraction step
-  __shared__ u32x4 lds[NBUF * STAGE];
+  // the ring, reused after the contraction for the LM head's logit block
+  constexpr int BM = 32 * WM * TM, BN = 32 * WN * TN;
+  constexpr int RING = NBUF * STAGE, LOGITS = (BM * (BN + 1) + 3) / 4;
+  __shared__ u32x4 lds[RING > LOGITS ? RING : LOGITS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x, xcd = b & 7, k = b >> 3;
@@ -372,6 +249,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
   if (s < nsteps) mul(r0);  // odd step count: the last step
   vm_wait_n<0>();  // the clamped refills past the last step
 
+  if (p.ep == EP_TOP2) {
+    // Every wave has drained its loads and finished reading the ring.
+    __syncthreads();
+    float* L = reinterpret_cast<float*>(lds);  // [BM][BN + 1]
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+      for (int n = 0; n < TN; ++n)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = (wm * TM + m) * 32 + 4 * (lane >> 5) + 8 * (j >> 2) +
+                        (j & 3);
+          const int c = (wn * TN + n) * 32 + (lane & 31);
+          L[r * (BN + 1) + c] = acc[m][n][j];
+        }
+    __syncthreads();
+    top2_block<BM, BN, 64 * C::NW>(p, L, mb * BM, nb * BN, nb, nbn);
+    return;
+  }
+
 #pragma unroll 1
   for (int t = 0; t < TM * TN; ++t) {
     const int m = t / TN, n = t % TN;
@@ -412,36 +309,6 @@ __global__ void pack_act_kernel(GemmArgs a, void* dst) {
   }
 }
 
-// SK steps per LDS stage and PD stages in flight when the step count
-// allows, else one step per stage and two in flight (steps are always even).
-template <int TM, int TN, int WM, int WN, int SK, int PD>
-hipError_t tiled_t(const GemmArgs& a, hipStream_t s) {
-  using C = Tiled<TM, TN, WM, WN>;
-  const int gm = (a.M + 16 * C::BMT - 1) / (16 * C::BMT);
-  const int nbn = (a.N / 16 + C::BNT - 1) / C::BNT;
-  const int grid = (nbn + 7) / 8 * 8 * gm;
-  const int nsteps = a.Kd / Storage<bf16_t>::KC;
-  if (nsteps % (SK * PD) == 0)
-    launch_k((gemm_tiled_kernel<TM, TN, WM, WN, SK, PD>), dim3(grid),
-                       dim3(64 * C::NW), 0, s, a, gm, nbn);
-  else
-    launch_k((gemm_tiled_kernel<TM, TN, WM, WN, 1, 2>), dim3(grid),
-                       dim3(64 * C::NW), 0, s, a, gm, nbn);
-  return hipGetLastError();
-}
-
-#ifndef DFLASH_T64_SK
-#define DFLASH_T64_SK 2
-#endif
-#ifndef DFLASH_T64_PD
-#define DFLASH_T64_PD 4
-#endif
-#ifndef DFLASH_T128_SK
-#define DFLASH_T128_SK 2
-#endif
-#ifndef DFLASH_T128_PD
-#define DFLASH_T128_PD 2
-#endif
 template <int TM, int TN, int WM, int WN, int NBUF>
 hipError_t dma_t(const GemmArgs& a, hipStream_t s) {
   using C = Tiled<TM, TN, WM, WN>;
@@ -453,9 +320,6 @@ hipError_t dma_t(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-#ifndef DFLASH_TILED_DMA
-#define DFLASH_TILED_DMA 1
-#endif
 #ifndef DFLASH_D64_NBUF
 #define DFLASH_D64_NBUF 8
 #endif
@@ -464,26 +328,23 @@ hipError_t dma_t(const GemmArgs& a, hipStream_t s) {
 #endif
 hipError_t tiled_cfg(int cfg, const GemmArgs& a, hipStream_t s) {
   switch (cfg) {
-    case TILE_64x64:
-      if (DFLASH_TILED_DMA) return dma_t<1, 1, 2, 2, DFLASH_D64_NBUF>(a, s);
-      return tiled_t<1, 1, 2, 2, DFLASH_T64_SK, DFLASH_T64_PD>(a, s);
-    case TILE_128x128:
-      if (DFLASH_TILED_DMA) return dma_t<2, 2, 2, 2, DFLASH_D128_NBUF>(a, s);
-      return tiled_t<2, 2, 2, 2, DFLASH_T128_SK, DFLASH_T128_PD>(a, s);
-    case TILE_256x64:
-      if (DFLASH_TILED_DMA) return dma_t<4, 1, 2, 2, 4>(a, s);
-      return tiled_t<4, 1, 2, 2, 2, 2>(a, s);
-    case TILE_256x128:
-      if (DFLASH_TILED_DMA) return dma_t<4, 2, 2, 2, 4>(a, s);
-      return tiled_t<4, 2, 2, 2, 2, 1>(a, s);
-    case TILE_128x256:
-      if (DFLASH_TILED_DMA) return dma_t<2, 4, 2, 2, 4>(a, s);
-      return tiled_t<2, 4, 2, 2, 2, 1>(a, s);
-    case TILE_256x256:
-      if (DFLASH_TILED_DMA) return dma_t<4, 2, 2, 4, 4>(a, s);
-      return tiled_t<4, 2, 2, 4, 2, 2>(a, s);
+    case TILE_64x64: return dma_t<1, 1, 2, 2, DFLASH_D64_NBUF>(a, s);
+    case TILE_128x128: return dma_t<2, 2, 2, 2, DFLASH_D128_NBUF>(a, s);
+    case TILE_256x64: return dma_t<4, 1, 2, 2, 4>(a, s);
+    case TILE_256x128: return dma_t<4, 2, 2, 2, 4>(a, s);
+    case TILE_128x256: return dma_t<2, 4, 2, 2, 4>(a, s);
   }
-  return hipErrorInvalidValue;
+  return hipErrorInvalidValue;  // 256 x 256: its logit block exceeds LDS
+}
+
+// output columns per block of each shape
+int tiled_block_cols(int cfg) {
+  switch (cfg) {
+    case TILE_64x64: case TILE_256x64: return 64;
+    case TILE_128x128: case TILE_256x128: return 128;
+    case TILE_128x256: return 256;
+  }
+  return 0;
 }
 
 }  // namespace
@@ -499,6 +360,11 @@ int plan_tiled(int M, int N) {
   if (M > 512) return TILE_128x128;
   if (M > 64 && N >= 16384) return TILE_128x128;
   return TILE_64x64;
+}
+
+int tiled_top2_records(int cfg, int N) {
+  const int bc = tiled_block_cols(cfg);
+  return bc > 0 ? (N + bc - 1) / bc : 0;
 }
 
 hipError_t launch_gemm_tiled(bool bf16, int cfg, const GemmArgs& a,

@@ -136,6 +136,9 @@ enum TileCfg : int {
   TILE_NCFG = 6,
 };
 int plan_tiled(int M, int N);
+// Top-2 records per row that the tiled LM head writes with block shape cfg
+// (one per column block: top2[row * records + block]).
+int tiled_top2_records(int cfg, int N);
 // bf16 only; a.a_packed must be set; a.M any size, a.N % 16 == 0,
 // a.Kd % 64 == 0
 hipError_t launch_gemm_tiled(bool bf16, int cfg, const GemmArgs& a,
