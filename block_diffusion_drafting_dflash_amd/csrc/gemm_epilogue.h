@@ -109,6 +109,80 @@ __device__ __forceinline__ void pair_epilogue(const GemmArgs& p, int row,
   store_elem(dst, i + half, rb);
 }
 
+// Eight consecutive finished output pairs of a bf16 MAP_PAIRS GEMM: a[k] is
+// low column col + k, b[k] its partner (col % 8 == 0, the eight never cross
+// a head or a 16-byte output chunk).  The arithmetic and the rounding of each
+// element are those of pair_epilogue; the stores are whole 16-byte chunks.
+__device__ __forceinline__ void pair_epilogue8(const GemmArgs& p, int row,
+                                               int col, const float (&a)[8],
+                                               const float (&b)[8]) {
+  if (p.ep == EP_SWIGLU) {
+    u32x4 w;
+    uint16_t* wt = reinterpret_cast<uint16_t*>(&w);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) wt[k] = (uint16_t)swiglu_bf16(a[k], b[k]);
+    *reinterpret_cast<u32x4*>(static_cast<char*>(p.out_t) +
+                              packed_offset<bf16_t>(row, col, p.pair_off)) = w;
+    return;
+  }
+  const int half = p.d / 2;
+  const int head = col / p.d, i = col % p.d;  // i + 7 < d/2
+  bool rot = true;
+  int pos;
+  bf16_t* dst;
+  if (p.ep == EP_QKV) {
+    const int bs = row / p.K;
+    int L = p.ctx_len[bs];
+    if (L < 0 || L > p.max_len) {
+      set_error(p.err, DFLASH_DEVERR_CTX_LEN);
+      L = min(max(L, 0), p.max_len);
+    }
+    pos = L + row % p.K;
+    if (head < p.Hq) {
+      dst = static_cast<bf16_t*>(p.out_t) + (int64_t)row * p.Hq * p.d +
+            head * p.d;
+    } else {
+      const bool is_k = head < p.Hq + p.Hkv;
+      const int h = is_k ? head - p.Hq : head - p.Hq - p.Hkv;
+      dst = static_cast<bf16_t*>(p.kv) +
+            (is_k ? 0 : (int64_t)p.max_batch * p.Hkv * p.P * p.d) +
+            (((int64_t)bs * p.Hkv + h) * p.P + pos) * p.d;
+      rot = is_k;
+    }
+  } else {  // EP_KV: injected context rows
+    const int seq = p.row_seq[row];
+    pos = p.row_pos[row];
+    if (seq < 0 || seq >= p.max_batch) {
+      set_error(p.err, DFLASH_DEVERR_SLOT);
+      return;
+    }
+    if (pos < 0 || pos >= p.max_ctx) {
+      set_error(p.err, DFLASH_DEVERR_POS);
+      return;
+    }
+    const int l = head / (2 * p.Hkv), w = head % (2 * p.Hkv);
+    const bool is_k = w < p.Hkv;
+    const int h = is_k ? w : w - p.Hkv;
+    const int64_t plane = (int64_t)p.max_batch * p.Hkv * p.P * p.d;
+    dst = static_cast<bf16_t*>(p.kv) + (2 * l + (is_k ? 0 : 1)) * plane +
+          (((int64_t)seq * p.Hkv + h) * p.P + pos) * p.d;
+    rot = is_k;
+  }
+  u32x4 wa, wb;
+  bf16_t* ta = reinterpret_cast<bf16_t*>(&wa);
+  bf16_t* tb = reinterpret_cast<bf16_t*>(&wb);
+  const double2* cs = p.rope + (int64_t)pos * half + i;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    double ra = a[k], rb = b[k];
+    if (rot) rope_pair(a[k], b[k], cs[k], ra, rb);
+    store_elem(ta, k, ra);
+    store_elem(tb, k, rb);
+  }
+  *reinterpret_cast<u32x4*>(dst + i) = wa;
+  *reinterpret_cast<u32x4*>(dst + i + half) = wb;
+}
+
 // Debug copy of one LM-head logit (row -> block row via the row map).
 __device__ __forceinline__ void store_debug_logit(const GemmArgs& p, int row,
                                                   int col, float z) {

@@ -22,39 +22,6 @@ namespace dflash {
 
 namespace {
 
-// Epilogue of one 32 x 32 accumulator tile: rows row0.., 16-column tiles
-// ctile and ctile + 1 (lanes 16-31 of each half-wave take the second).
-__device__ __forceinline__ void tile_epilogue(const GemmArgs& p, int row0,
-                                              int ctile, const f32x16& acc,
-                                              int lane) {
-  const int c = lane & 15;
-  const int tile = ctile + ((lane >> 4) & 1);
-  const bool tile_ok = tile < p.N / 16;
-  const int rbase = row0 + 4 * (lane >> 5);
-  if (p.ep == EP_STORE || p.ep == EP_RESID) {
-    if (!tile_ok) return;
-    const int col = map_col(p.cmap, p.pair_group, p.pair_off, tile, c);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int row = rbase + 8 * (j >> 2) + (j & 3);
-      if (row < p.M) {
-        float* o = p.out_f32 + (int64_t)row * p.ldo + col;
-        *o = p.ep == EP_RESID ? *o + acc[j] : acc[j];
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float partner = __shfl_xor(acc[j], 8, 64);
-    const int row = rbase + 8 * (j >> 2) + (j & 3);
-    if (c < 8 && row < p.M && tile_ok)
-      pair_epilogue<bf16_t>(
-          p, row, map_col(p.cmap, p.pair_group, p.pair_off, tile, c), acc[j],
-          partner);
-  }
-}
-
 template <int TM, int TN, int WM, int WN>
 struct Tiled {
   static constexpr int NW = WM * WN;
@@ -64,6 +31,63 @@ struct Tiled {
   static constexpr int LPW = NF / NW;      // fragment loads per wave per step
   static_assert(NF % NW == 0, "fragments must split evenly over the waves");
 };
+
+// Projection epilogue of one block of sums parked in LDS (L: BM rows of
+// BN + 1 floats; block column c is column c % 16 of 16-column tile
+// tile0 + c / 16).  Rows past M and tiles past N are skipped.
+//   EP_STORE / EP_RESID: a unit is 4 consecutive columns of a row (float4
+//   stores, 32 lanes along a row of 128 columns).
+//   Pair epilogues: a unit is one (row, tile): its 8 low columns and their
+//   partners, written as whole 16-byte chunks (pair_epilogue8); the lanes of
+//   a wave take consecutive rows.
+template <int BM, int BN, int NT>
+__device__ __forceinline__ void block_epilogue(const GemmArgs& p,
+                                               const float* L, int row0,
+                                               int tile0) {
+  const int ntiles = p.N / 16;
+  if (p.ep == EP_STORE || p.ep == EP_RESID) {
+    constexpr int UPR = BN / 4;
+    for (int u = threadIdx.x; u < BM * UPR; u += NT) {
+      const int r = u / UPR, c4 = (u % UPR) * 4;
+      const int row = row0 + r, tile = tile0 + c4 / 16;
+      if (row >= p.M || tile >= ntiles) continue;
+      const float* lr = L + r * (BN + 1) + c4;
+      if (p.cmap == MAP_LINEAR) {
+        float* o = p.out_f32 + (int64_t)row * p.ldo + tile * 16 + c4 % 16;
+        f32x4 v = {lr[0], lr[1], lr[2], lr[3]};
+        if (p.ep == EP_RESID) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(o);
+          v = f32x4{x[0] + v[0], x[1] + v[1], x[2] + v[2], x[3] + v[3]};
+        }
+        *reinterpret_cast<f32x4*>(o) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col =
+              map_col(p.cmap, p.pair_group, p.pair_off, tile, c4 % 16 + e);
+          float* o = p.out_f32 + (int64_t)row * p.ldo + col;
+          *o = p.ep == EP_RESID ? *o + lr[e] : lr[e];
+        }
+      }
+    }
+    return;
+  }
+  constexpr int TPB = BN / 16;
+  for (int u = threadIdx.x; u < BM * TPB; u += NT) {
+    const int r = u % BM, tb = u / BM;
+    const int row = row0 + r, tile = tile0 + tb;
+    if (row >= p.M || tile >= ntiles) continue;
+    const float* lr = L + r * (BN + 1) + tb * 16;
+    float a[8], b[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a[k] = lr[k];
+      b[k] = lr[k + 8];
+    }
+    pair_epilogue8(p, row,
+                   map_col(p.cmap, p.pair_group, p.pair_off, tile, 0), a, b);
+  }
+}
 
 // LM-head reduction of one block of logits parked in LDS (L: BM rows of
 // BN + 1 floats; the odd row stride makes a wave's column reads hit 64
@@ -249,39 +273,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
   if (s < nsteps) mul(r0);  // odd step count: the last step
   vm_wait_n<0>();  // the clamped refills past the last step
 
-  if (p.ep == EP_TOP2) {
-    // Every wave has drained its loads and finished reading the ring.
-    __syncthreads();
-    float* L = reinterpret_cast<float*>(lds);  // [BM][BN + 1]
+  // Every wave has drained its loads and finished reading the ring: park
+  // the block's sums there, then run the epilogue over whole rows.
+  __syncthreads();
+  float* L = reinterpret_cast<float*>(lds);  // [BM][BN + 1]
 #pragma unroll
-    for (int m = 0; m < TM; ++m)
+  for (int m = 0; m < TM; ++m)
 #pragma unroll
-      for (int n = 0; n < TN; ++n)
+    for (int n = 0; n < TN; ++n)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int r = (wm * TM + m) * 32 + 4 * (lane >> 5) + 8 * (j >> 2) +
-                        (j & 3);
-          const int c = (wn * TN + n) * 32 + (lane & 31);
-          L[r * (BN + 1) + c] = acc[m][n][j];
-        }
-    __syncthreads();
+      for (int j = 0; j < 16; ++j) {
+        const int r = (wm * TM + m) * 32 + 4 * (lane >> 5) + 8 * (j >> 2) +
+                      (j & 3);
+        const int c = (wn * TN + n) * 32 + (lane & 31);
+        L[r * (BN + 1) + c] = acc[m][n][j];
+      }
+  __syncthreads();
+  if (p.ep == EP_TOP2)
     top2_block<BM, BN, 64 * C::NW>(p, L, mb * BM, nb * BN, nb, nbn);
-    return;
-  }
-
-#pragma unroll 1
-  for (int t = 0; t < TM * TN; ++t) {
-    const int m = t / TN, n = t % TN;
-    const int row0 = (mb * C::BMT + (wm * TM + m) * 2) * 16;
-    const int ctile = nb * C::BNT + (wn * TN + n) * 2;
-    f32x16 v = acc[0][0];
-#pragma unroll
-    for (int mm = 0; mm < TM; ++mm)
-#pragma unroll
-      for (int nn = 0; nn < TN; ++nn)
-        if (t == mm * TN + nn) v = acc[mm][nn];
-    if (ctile < ntiles && row0 < p.M) tile_epilogue(p, row0, ctile, v, lane);
-  }
+  else
+    block_epilogue<BM, BN, 64 * C::NW>(p, L, mb * BM, nb * C::BNT);
 }
 
 // Row-major activation segments (the concatenated target layers) -> packed
