@@ -43,6 +43,7 @@ bool aligned16(const void* p) {
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr size_t kTimingSlots = 8192;
+constexpr int kCommitMaxRecords = 1536;
 // Timing events are bound to kernel dispatches and need no system-scope
 // fence.
 constexpr unsigned kTimingEventFlags = hipEventDisableSystemFence;
@@ -203,8 +204,18 @@ int attn_chunk(int B, int Hkv, int max_keys, int num_cu) {
 #ifndef DFLASH_PACK_ROWMAJOR
 #define DFLASH_PACK_ROWMAJOR 1
 #endif
+// bf16 GEMMs above 64 rows are tiled; from 17 rows so are the LM head and
+// wide outputs (at least DFLASH_TILED_MIN_COLS columns): there a 16-column
+// streaming workgroup would re-read every activation row for each weight
+// tile, while a 64-column block reads them once per 64 columns.  Narrower
+// outputs keep the streaming form, which has four times the workgroups.
+#ifndef DFLASH_TILED_MIN_COLS
+#define DFLASH_TILED_MIN_COLS 6144
+#endif
 bool gemm_is_tiled(const dflash_ctx* c, const GemmArgs& a) {
-  return c->bf16 && (a.M > 64 || (a.ep == EP_TOP2 && a.M > 16));
+  return c->bf16 &&
+         (a.M > 64 ||
+          (a.M > 16 && (a.ep == EP_TOP2 || a.N >= DFLASH_TILED_MIN_COLS)));
 }
 
 dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
@@ -729,10 +740,10 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
     hd.logits_ld = V;
     hd.err = ctx->err;
     const int parts = lm_head_parts(bf, Mh, V, D, ctx->num_cu);
-    // records per row for the commit kernel: one per workgroup of the
-    // persistent head, one per column block of the tiled head (both merged
-    // by the commit kernel itself); the per-tile records of the streaming
-    // form are merged to kMergeChunks per row first
+    // records per row: one per workgroup of the persistent head, one per
+    // column block of the tiled head, one per 16-column tile of the
+    // streaming form; the commit kernel merges up to kCommitMaxRecords
+    // itself
     const Top2* recs = ctx->lm_part;
     int nrec = 0;
     if (parts > 0) {
@@ -742,10 +753,12 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
     } else {
       dflash_status st = run_gemm(ctx, hd, s, DFLASH_TIME_LMHEAD);
       if (st != DFLASH_OK) return st;
-      if (gemm_is_tiled(ctx, hd)) {
-        nrec = tiled_top2_records(plan_tiled(Mh, V), V);
-      } else {
-        DF_HIP(launch_lm_merge(Mh, V / 16, ctx->lm_part, ctx->lm_part2, s));
+      nrec = gemm_is_tiled(ctx, hd) ? tiled_top2_records(plan_tiled(Mh, V), V)
+                                    : V / 16;
+      if (nrec > kCommitMaxRecords) {
+        // many records per row: merge them to kMergeChunks per row first,
+        // with a workgroup per (row, chunk), rather than serially per wave
+        DF_HIP(launch_lm_merge(Mh, nrec, ctx->lm_part, ctx->lm_part2, s));
         recs = ctx->lm_part2;
         nrec = kMergeChunks;
       }

@@ -99,11 +99,10 @@ __device__ __forceinline__ void block_epilogue(const GemmArgs& p,
 // skipped, rows past M are not written.
 template <int BM, int BN, int NT>
 __device__ __forceinline__ void top2_block(const GemmArgs& p, const float* L,
-                                           int row0, int col0, int rec,
-                                           int nrec) {
+                                           Top2* part, int row0, int col0,
+                                           int rec, int nrec) {
   static_assert(NT % BM == 0, "whole rows per thread group");
   constexpr int TPR = NT / BM, CPT = BN / TPR;
-  __shared__ Top2 part[NT];
   const int t = threadIdx.x, r = t % BM, q = t / BM;
   const int row = row0 + r;
   const bool row_ok = row < p.M;
@@ -174,8 +173,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
   constexpr int STAGE = C::NF * 64;  // u32x4 per contraction step
   // the ring, reused after the contraction for the LM head's logit block
   constexpr int BM = 32 * WM * TM, BN = 32 * WN * TN;
-  constexpr int RING = NBUF * STAGE, LOGITS = (BM * (BN + 1) + 3) / 4;
-  __shared__ u32x4 lds[RING > LOGITS ? RING : LOGITS];
+  // (u32x4 units) logit block, then the top-2 merge records of NT threads
+  constexpr int RING = NBUF * STAGE;
+  constexpr int LOGITS = (BM * (BN + 1) + 3) / 4, PARTS = 64 * C::NW;
+  constexpr int EPI = LOGITS + PARTS;
+  __shared__ u32x4 lds[RING > EPI ? RING : EPI];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x, xcd = b & 7, k = b >> 3;
@@ -290,7 +292,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
       }
   __syncthreads();
   if (p.ep == EP_TOP2)
-    top2_block<BM, BN, 64 * C::NW>(p, L, mb * BM, nb * BN, nb, nbn);
+    top2_block<BM, BN, 64 * C::NW>(p, L,
+                                   reinterpret_cast<Top2*>(lds + LOGITS),
+                                   mb * BM, nb * BN, nb, nbn);
   else
     block_epilogue<BM, BN, 64 * C::NW>(p, L, mb * BM, nb * C::BNT);
 }
