@@ -4,6 +4,7 @@
 // built once at create time.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -82,6 +83,8 @@ struct dflash_ctx {
   size_t attn_floats = 0, lm_part_count = 0;
   double2* rope = nullptr;   // cos, sin of pos * theta^(-2i/d) [P][d/2]
   float* u = nullptr;        // fused target features before RMSNorm [TI][D]
+  float* splitk = nullptr;   // split-K copies [S][rows][D]
+  size_t splitk_floats = 0;
   void* cond = nullptr;      // H_cond, packed [TI16][D]
   void* hpk = nullptr;       // target hidden states, packed [TI16][n_t * D_t]
   float* x = nullptr;        // residual rows [R][D]
@@ -212,10 +215,31 @@ int attn_chunk(int B, int Hkv, int max_keys, int num_cu) {
 #ifndef DFLASH_TILED_MIN_COLS
 #define DFLASH_TILED_MIN_COLS 6144
 #endif
+bool splittable(const GemmArgs& a) {
+  return (a.ep == EP_STORE || a.ep == EP_RESID) && a.cmap == MAP_LINEAR;
+}
 bool gemm_is_tiled(const dflash_ctx* c, const GemmArgs& a) {
   return c->bf16 &&
-         (a.M > 64 ||
-          (a.M > 16 && (a.ep == EP_TOP2 || a.N >= DFLASH_TILED_MIN_COLS)));
+         (a.M > 64 || (a.M > 16 && (a.ep == EP_TOP2 || splittable(a) ||
+                                    a.N >= DFLASH_TILED_MIN_COLS)));
+}
+
+// Contraction splits of a tiled store / residual GEMM whose block grid
+// leaves CUs idle: copies up to about one workgroup per CU (at most 4, at
+// least 8 contraction steps each, within the split workspace).  Measured:
+// at 64 rows (64 blocks, 4 copies) the split plus its reduction is 30-40%
+// faster than one pass; at 256 blocks two copies gain nothing.
+#ifndef DFLASH_MAX_KSPLIT
+#define DFLASH_MAX_KSPLIT 4
+#endif
+int plan_ksplit(const dflash_ctx* c, const GemmArgs& a, int cfg) {
+  if (!splittable(a)) return 1;
+  const int blocks = tiled_blocks(cfg, a.M, a.N);
+  int S = blocks > 0 ? c->num_cu / blocks : 1;
+  S = std::min(S, DFLASH_MAX_KSPLIT);
+  S = std::min(S, a.Kd / 32 / 8);
+  while (S > 1 && (size_t)S * a.M * a.N > c->splitk_floats) --S;
+  return std::max(S, 1);
 }
 
 dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
@@ -232,8 +256,22 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
     a.a_seg_k = a.Kd;
   }
   if (tiled) {
+    const int cfg = plan_tiled(a.M, a.N);
+    const int S = plan_ksplit(c, a, cfg);
     TimedLaunch tl(c, kind, s);
-    DF_HIP(launch_gemm_tiled(true, plan_tiled(a.M, a.N), a, s));
+    if (S > 1) {
+      // split copies into the workspace, then summed in order into the
+      // output (plain store or residual add)
+      GemmArgs b = a;
+      b.ep = EP_STORE;
+      b.out_f32 = c->splitk;
+      b.ldo = a.N;
+      DF_HIP(launch_gemm_tiled(true, cfg, b, S, s));
+      DF_HIP(launch_splitk_reduce(a.M, a.N, S, c->splitk, a.out_f32, a.ldo,
+                                  a.ep == EP_RESID, s));
+      return DFLASH_OK;
+    }
+    DF_HIP(launch_gemm_tiled(true, cfg, a, 1, s));
     return DFLASH_OK;
   }
   const GemmPlan pl = plan_gemm(a.M, a.N, lm);
@@ -428,6 +466,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
   const int G = c.num_q_heads / c.num_kv_heads;
   x->attn_floats =
       (size_t)G * (DFLASH_ATTN_WG_PER_CU * x->num_cu + c.max_batch * c.num_kv_heads) * K;
+  x->splitk_floats = (size_t)DFLASH_MAX_KSPLIT * std::max(R, TI16) * D;
   const int lm_rows = c.max_batch * (K - 1);
   x->lm_part_count = (size_t)lm_rows * (c.vocab / 16);
 
@@ -435,6 +474,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
   std::vector<Item> items = {
       {(void**)&x->rope, (size_t)x->P * (d / 2) * sizeof(double2)},
       {(void**)&x->u, (size_t)TI * D * sizeof(float)},
+      {(void**)&x->splitk, x->splitk_floats * sizeof(float)},
       {&x->cond, (size_t)TI16 * D * esz},
       {&x->hpk, (size_t)TI16 * c.num_target_layers * c.target_hidden * esz},
       {(void**)&x->x, (size_t)R * D * sizeof(float)},

@@ -166,9 +166,15 @@ __device__ __forceinline__ void vm_wait_n() {
 // every wave has read step s), refills step s's slot with step s + NBUF,
 // reads step s + 1 and multiplies step s.
 template <int TM, int TN, int WM, int WN, int NBUF>
+//
+// With ksplit > 1 the grid holds ksplit copies of the block grid; copy sp
+// takes contraction steps [sp n / ksplit, (sp + 1) n / ksplit) and stores its
+// fp32 block at out_f32 + sp M ldo (EP_STORE only; splitk_reduce_kernel sums
+// the copies).
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
                                                                 int gm,
-                                                                int nbn) {
+                                                                int nbn,
+                                                                int ksplit) {
   using C = Tiled<TM, TN, WM, WN>;
   constexpr int STAGE = C::NF * 64;  // u32x4 per contraction step
   // the ring, reused after the contraction for the LM head's logit block
@@ -180,14 +186,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
   __shared__ u32x4 lds[RING > EPI ? RING : EPI];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = blockIdx.x, xcd = b & 7, k = b >> 3;
+  // the block grid is a multiple of 8 ids, so b & 7 is still the XCD
+  const int grid1 = (nbn + 7) / 8 * 8 * gm;
+  const int sp = blockIdx.x / grid1, b = blockIdx.x % grid1;
+  const int xcd = b & 7, k = b >> 3;
   const int mb = k % gm, nb = (k / gm) * 8 + xcd;
   if (nb >= nbn) return;  // whole workgroup: padding of the XCD mapping
-  const int nsteps = p.Kd / Storage<bf16_t>::KC;
+  const int ksteps = p.Kd / Storage<bf16_t>::KC;
+  const int s_begin = (int)((int64_t)sp * ksteps / ksplit);
+  const int nsteps = (int)((int64_t)(sp + 1) * ksteps / ksplit) - s_begin;
   const int mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
   const int wm = wave / WN, wn = wave % WN;
+  if (ksplit > 1) p.out_f32 += (int64_t)sp * p.M * p.ldo;
 
-  // fragment f = wave + i NW of a step, as in gemm_tiled_kernel
+  // fragment f = wave + i NW of a step
   const char* src[C::LPW];
 #pragma unroll
   for (int i = 0; i < C::LPW; ++i) {
@@ -201,7 +213,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
       t = min(nb * C::BNT + f - C::BMT, ntiles - 1);
       base = static_cast<const char*>(p.w);
     }
-    src[i] = base + ((int64_t)t * nsteps * 64 + lane) * 16;
+    src[i] = base + (((int64_t)t * ksteps + s_begin) * 64 + lane) * 16;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(
       __attribute__((address_space(3))) void*)lds;
@@ -325,14 +337,37 @@ __global__ void pack_act_kernel(GemmArgs a, void* dst) {
 }
 
 template <int TM, int TN, int WM, int WN, int NBUF>
-hipError_t dma_t(const GemmArgs& a, hipStream_t s) {
+hipError_t dma_t(const GemmArgs& a, int ksplit, hipStream_t s) {
   using C = Tiled<TM, TN, WM, WN>;
   const int gm = (a.M + 16 * C::BMT - 1) / (16 * C::BMT);
   const int nbn = (a.N / 16 + C::BNT - 1) / C::BNT;
   const int grid = (nbn + 7) / 8 * 8 * gm;
-  launch_k((gemm_dma_kernel<TM, TN, WM, WN, NBUF>), dim3(grid),
-           dim3(64 * C::NW), 0, s, a, gm, nbn);
+  launch_k((gemm_dma_kernel<TM, TN, WM, WN, NBUF>), dim3(grid * ksplit),
+           dim3(64 * C::NW), 0, s, a, gm, nbn, ksplit);
   return hipGetLastError();
+}
+
+// out[row][col] (+)= sum over s of ws[s][row][col], s in order, fp32; one
+// float4 per thread (N % 4 == 0).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(
+    int M, int N, int S, const float* ws, float* out, int ldo, int resid) {
+  const int64_t n4 = (int64_t)M * N / 4, plane = (int64_t)M * N;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n4;
+       q += (int64_t)gridDim.x * 256) {
+    const int64_t e = q * 4;
+    const int row = (int)(e / N), col = (int)(e % N);
+    f32x4 v = *reinterpret_cast<const f32x4*>(ws + e);
+    for (int k = 1; k < S; ++k) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(ws + k * plane + e);
+      v = f32x4{v[0] + w[0], v[1] + w[1], v[2] + w[2], v[3] + w[3]};
+    }
+    float* o = out + (int64_t)row * ldo + col;
+    if (resid) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(o);
+      v = f32x4{x[0] + v[0], x[1] + v[1], x[2] + v[2], x[3] + v[3]};
+    }
+    *reinterpret_cast<f32x4*>(o) = v;
+  }
 }
 
 #ifndef DFLASH_D64_NBUF
@@ -341,13 +376,13 @@ hipError_t dma_t(const GemmArgs& a, hipStream_t s) {
 #ifndef DFLASH_D128_NBUF
 #define DFLASH_D128_NBUF 4
 #endif
-hipError_t tiled_cfg(int cfg, const GemmArgs& a, hipStream_t s) {
+hipError_t tiled_cfg(int cfg, const GemmArgs& a, int ks, hipStream_t s) {
   switch (cfg) {
-    case TILE_64x64: return dma_t<1, 1, 2, 2, DFLASH_D64_NBUF>(a, s);
-    case TILE_128x128: return dma_t<2, 2, 2, 2, DFLASH_D128_NBUF>(a, s);
-    case TILE_256x64: return dma_t<4, 1, 2, 2, 4>(a, s);
-    case TILE_256x128: return dma_t<4, 2, 2, 2, 4>(a, s);
-    case TILE_128x256: return dma_t<2, 4, 2, 2, 4>(a, s);
+    case TILE_64x64: return dma_t<1, 1, 2, 2, DFLASH_D64_NBUF>(a, ks, s);
+    case TILE_128x128: return dma_t<2, 2, 2, 2, DFLASH_D128_NBUF>(a, ks, s);
+    case TILE_256x64: return dma_t<4, 1, 2, 2, 4>(a, ks, s);
+    case TILE_256x128: return dma_t<4, 2, 2, 2, 4>(a, ks, s);
+    case TILE_128x256: return dma_t<2, 4, 2, 2, 4>(a, ks, s);
   }
   return hipErrorInvalidValue;  // 256 x 256: its logit block exceeds LDS
 }
@@ -382,10 +417,34 @@ int tiled_top2_records(int cfg, int N) {
   return bc > 0 ? (N + bc - 1) / bc : 0;
 }
 
+int tiled_blocks(int cfg, int M, int N) {
+  const int bc = tiled_block_cols(cfg);
+  const int br = cfg == TILE_64x64 ? 64 : (cfg == TILE_128x128 ||
+                                           cfg == TILE_128x256) ? 128 : 256;
+  return bc > 0 ? ((M + br - 1) / br) * ((N + bc - 1) / bc) : 0;
+}
+
 hipError_t launch_gemm_tiled(bool bf16, int cfg, const GemmArgs& a,
-                             hipStream_t s) {
+                             int ksplit, hipStream_t s) {
   if (!bf16) return hipErrorInvalidValue;  // fp32 drafters use gemm_kernel
-  return tiled_cfg(cfg, a, s);
+  // every split needs at least one contraction step
+  if (ksplit < 1 || ksplit > a.Kd / Storage<bf16_t>::KC ||
+      (ksplit > 1 && a.ep != EP_STORE))
+    return hipErrorInvalidValue;
+  return tiled_cfg(cfg, a, ksplit, s);
+}
+
+hipError_t launch_splitk_reduce(int M, int N, int S, const float* ws,
+                                float* out, int ldo, bool resid,
+                                hipStream_t s) {
+  if (N % 4 != 0 || ldo % 4 != 0) return hipErrorInvalidValue;
+  const int64_t n4 = (int64_t)M * N / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  launch_k(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, M,
+           N, S, ws, out, ldo, resid ? 1 : 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack_act(bool bf16, const GemmArgs& a, void* dst,

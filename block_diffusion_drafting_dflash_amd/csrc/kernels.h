@@ -139,10 +139,17 @@ int plan_tiled(int M, int N);
 // Top-2 records per row that the tiled LM head writes with block shape cfg
 // (one per column block: top2[row * records + block]).
 int tiled_top2_records(int cfg, int N);
+// Output blocks of shape cfg over an M x N result.
+int tiled_blocks(int cfg, int M, int N);
 // bf16 only; a.a_packed must be set; a.M any size, a.N % 16 == 0,
-// a.Kd % 64 == 0
+// a.Kd % 32 == 0.  ksplit > 1 splits the contraction (EP_STORE only): copy s
+// of the result goes to a.out_f32 + s * M * ldo.
 hipError_t launch_gemm_tiled(bool bf16, int cfg, const GemmArgs& a,
-                             hipStream_t s);
+                             int ksplit, hipStream_t s);
+// out[M][N] (row stride ldo) = (out +) sum of the S planes ws[S][M][N].
+hipError_t launch_splitk_reduce(int M, int N, int S, const float* ws,
+                                float* out, int ldo, bool resid,
+                                hipStream_t s);
 // dst = packed copy of a's row-major A segments (M rows, contraction a.Kd)
 hipError_t launch_pack_act(bool bf16, const GemmArgs& a, void* dst,
                            hipStream_t s);
