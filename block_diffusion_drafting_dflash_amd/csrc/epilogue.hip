@@ -5,6 +5,8 @@
 // Pass 0 also sets up the block: [anchor, mask, ..., mask] or the caller's
 // block, with index 0 and non-mask ids committed.  Every pass rebuilds the
 // map from LM-head rows to still-masked block rows (rank by block index).
+#include <algorithm>
+
 #include "../../include/dflash.h"
 #include "kernels.h"
 
@@ -174,6 +176,9 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(int rows, int D,
 // writes whole 1 KiB fragments of the packed tile (lane l: tile row l % 16,
 // contraction group l / 16), so every store is part of one contiguous
 // wave-wide write.
+// The tile's contraction steps are split over gridDim.y workgroups (each
+// recomputes the 16 rows' statistics, from L2), so that a few hundred rows
+// still fill the chip.
 template <typename T>
 __global__ __launch_bounds__(1024) void rmsnorm_tile_kernel(int rows, int D,
                                                        const float* x,
@@ -184,6 +189,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_tile_kernel(int rows, int D,
   __shared__ double inv_s[16];
   __shared__ int src_s[16];
   const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int part = blockIdx.y, nparts = gridDim.y;
   {
     const int row = t * 16 + wave;
     const int src = row < rows ? (rowmap ? rowmap[row] : row) : -1;
@@ -209,20 +215,23 @@ __global__ __launch_bounds__(1024) void rmsnorm_tile_kernel(int rows, int D,
   const int src = src_s[r];
   const double inv = inv_s[r];
   const int nsteps = D / KC;
+  // this workgroup's steps [s_lo, s_hi)
+  const int s_lo = (int)((int64_t)part * nsteps / nparts);
+  const int s_hi = (int)((int64_t)(part + 1) * nsteps / nparts);
   char* ob = reinterpret_cast<char*>(out) + ((int64_t)t * nsteps * 64 + lane) * 16;
   if (src < 0) {  // lanes of rows without a source write zeros
-    for (int s = wave; s < nsteps; s += 16)
+    for (int s = s_lo + wave; s < s_hi; s += 16)
       *reinterpret_cast<u32x4*>(ob + (int64_t)s * 1024) = u32x4{0u, 0u, 0u, 0u};
     return;
   }
   const float* xr = x + (int64_t)src * D + grp * E;
   const T* gk = g + grp * E;
   constexpr int U = 4;  // fragments whose loads are in flight together
-  for (int s0 = wave; s0 < nsteps; s0 += 16 * U) {
+  for (int s0 = s_lo + wave; s0 < s_hi; s0 += 16 * U) {
     u32x4 gv[U], q[U][E / 4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int s = min(s0 + 16 * u, nsteps - 1);
+      const int s = min(s0 + 16 * u, s_hi - 1);
       gv[u] = load16(gk + s * KC);
 #pragma unroll
       for (int e = 0; e < E / 4; ++e) q[u][e] = load16(xr + s * KC + 4 * e);
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_tile_kernel(int rows, int D,
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + 16 * u;
-      if (s >= nsteps) break;
+      if (s >= s_hi) break;
       const T* gt = reinterpret_cast<const T*>(&gv[u]);
       u32x4 v;
       T* vt = reinterpret_cast<T*>(&v);
@@ -289,12 +298,16 @@ hipError_t launch_rmsnorm(bool bf16, int rows, int D, const float* x,
                          static_cast<float*>(out));
     return hipGetLastError();
   }
+  // about 256 workgroups, each with at least 16 contraction steps
+  const int nsteps = D / (bf16 ? Storage<bf16_t>::KC : Storage<float>::KC);
+  const int parts = std::max(1, std::min((256 + tiles - 1) / tiles,
+                                         nsteps / 16));
   if (bf16)
-    launch_k(rmsnorm_tile_kernel<bf16_t>, dim3(tiles), dim3(1024), 0,
+    launch_k(rmsnorm_tile_kernel<bf16_t>, dim3(tiles, parts), dim3(1024), 0,
                        s, rows, D, x, rowmap, static_cast<const bf16_t*>(gain),
                        eps, static_cast<bf16_t*>(out));
   else
-    launch_k(rmsnorm_tile_kernel<float>, dim3(tiles), dim3(1024), 0,
+    launch_k(rmsnorm_tile_kernel<float>, dim3(tiles, parts), dim3(1024), 0,
                        s, rows, D, x, rowmap, static_cast<const float*>(gain),
                        eps, static_cast<float*>(out));
   return hipGetLastError();
