@@ -353,25 +353,26 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
   const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + base;
   const float* ob = p.part_o + base * D + lane * DPL;
 
-  // the first batch of partial outputs does not depend on the weights:
-  // issue its loads before the reductions
+  // The first batch of partial outputs does not depend on the weights:
+  // issue its loads before the reductions.  Every row has nch chunk slots,
+  // so the loads are made unconditionally (clamped to the slots, not to the
+  // row's own chunk count, which needs ctx_len first) and the values of
+  // chunks past nc are dropped below.
   float v[kMergeBatch][DPL];
   auto load_batch = [&](int c0) {
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u)
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int c = min(c0 + u, p.nch - 1);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e)
-        v[u][e] = c0 + u < nc ? ob[(int64_t)(c0 + u) * D + e] : 0.f;
+      for (int e = 0; e < DPL; ++e) v[u][e] = ob[(int64_t)c * D + e];
+    }
   };
   load_batch(0);
   // chunk weights 2^(m_c - M): lane c holds chunk c (c < 64); further
   // chunks, if any, are read again where needed
-  float m_l = -INFINITY, l_l = 0.f;
-  if (lane < nc) {
-    const float2 t = ml[lane];
-    m_l = t.x;
-    l_l = t.y;
-  }
+  const float2 t_l = ml[min(lane, p.nch - 1)];
+  const float m_l = lane < nc ? t_l.x : -INFINITY;
+  const float l_l = lane < nc ? t_l.y : 0.f;
   float M = m_l;
   for (int c = lane + 64; c < nc; c += 64) M = fmaxf(M, ml[c].x);
   M = warp_max(M);
