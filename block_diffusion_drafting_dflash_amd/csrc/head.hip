@@ -32,33 +32,24 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(int ntiles,
   }
 }
 
-// One workgroup per sequence.  Wave w merges the records of the LM-head
-// rows of block positions w, w + 16, ... (a masked position's row is its
-// rank among the masked positions): nrec records per row, lane k taking
-// records k, k + 64, ... in order (loaded four at a time), then a
-// butterfly.  Wave 0 then ranks the
-// masked positions by confidence (ties -> lower index) and commits those
-// within the pass's quota.
+// One workgroup per sequence.  Wave w merges the records of LM-head rows
+// w, w + 16, ... of the sequence (row = rank of a still-masked position):
+// nrec records per row, lane k taking records k, k + 64, ... in order
+// (loaded four at a time), then a butterfly.  The rows are taken by rank, so
+// the loads need no block state; ranks past the masked count hold records
+// of zeroed rows and are never read back.  Wave 0 then maps each masked
+// position to its rank, ranks the positions by confidence (ties -> lower
+// index) and commits those within the pass's quota.
 constexpr int kCommitWaves = 16;
 
 __global__ __launch_bounds__(64 * kCommitWaves) void commit_kernel(
     int K, int n_cap, int quota, int last, const Top2* part, int nrec,
     BlockState st, int32_t* draft, float* conf_out, float* margin_out) {
   __shared__ Top2 res[64];
-  __shared__ unsigned long long ball_s;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave == 0) {
-    const bool m = lane < K && !st.committed[b * K + lane];
-    const unsigned long long ball = __ballot(m);
-    if (lane == 0) ball_s = ball;
-  }
-  __syncthreads();
-  const unsigned long long ball = ball_s;
-  for (int i = wave; i < K; i += kCommitWaves) {
-    if (!((ball >> i) & 1ull)) continue;  // uniform per wave
-    const int rank_idx = __popcll(ball & ((1ull << i) - 1ull));
-    const Top2* src = part + (int64_t)(b * n_cap + rank_idx) * nrec;
+  for (int rk = wave; rk < n_cap; rk += kCommitWaves) {
+    const Top2* src = part + (int64_t)(b * n_cap + rk) * nrec;
     // lane records issued in batches of kCommitBatch, merged in order
     constexpr int kCommitBatch = 4;
     Top2 r = top2_empty();
@@ -73,13 +64,19 @@ __global__ __launch_bounds__(64 * kCommitWaves) void commit_kernel(
       for (int u = 0; u < kCommitBatch; ++u) r = top2_merge(r, t[u]);
     }
     r = top2_wave(r);
-    if (lane == 0) res[i] = r;
+    if (lane == 0) res[rk] = r;
+  }
+  unsigned long long ball = 0;
+  if (wave == 0) {
+    const bool m = lane < K && !st.committed[b * K + lane];
+    ball = __ballot(m);
   }
   __syncthreads();
   if (wave != 0) return;
   const int i = lane;
   const bool masked = (ball >> i) & 1ull;
-  const Top2 r = masked ? res[i] : top2_empty();
+  const int rank = __popcll(ball & ((1ull << i) - 1ull));
+  const Top2 r = masked && rank < n_cap ? res[rank] : top2_empty();
   const float cf = masked ? 1.f / r.s : -1.f;  // exp(max - logsumexp)
   int better = 0;
   for (int j = 0; j < K; ++j) {
