@@ -383,6 +383,7 @@ hipError_t tiled_cfg(int cfg, const GemmArgs& a, int ks, hipStream_t s) {
     case TILE_256x64: return dma_t<4, 1, 2, 2, 4>(a, ks, s);
     case TILE_256x128: return dma_t<4, 2, 2, 2, 4>(a, ks, s);
     case TILE_128x256: return dma_t<2, 4, 2, 2, 4>(a, ks, s);
+    case TILE_256x128_W8: return dma_t<2, 2, 4, 2, 4>(a, ks, s);
   }
   return hipErrorInvalidValue;  // 256 x 256: its logit block exceeds LDS
 }
@@ -391,7 +392,7 @@ hipError_t tiled_cfg(int cfg, const GemmArgs& a, int ks, hipStream_t s) {
 int tiled_block_cols(int cfg) {
   switch (cfg) {
     case TILE_64x64: case TILE_256x64: return 64;
-    case TILE_128x128: case TILE_256x128: return 128;
+    case TILE_128x128: case TILE_256x128: case TILE_256x128_W8: return 128;
     case TILE_128x256: return 256;
   }
   return 0;
@@ -407,7 +408,10 @@ int tiled_block_cols(int cfg) {
 // rows over the drafter's projection and LM-head shapes).
 int plan_tiled(int M, int N) {
   if (DFLASH_TILED_CFG >= 0) return DFLASH_TILED_CFG;
-  if (M > 512) return TILE_128x128;
+  // above 512 rows, outputs narrower than 16384 columns take 256 x 128
+  // blocks on eight waves (with split-K filling the CUs): 16% faster than
+  // 128 x 128 there at 1024 rows, slower for the wide gate/up and LM head
+  if (M > 512) return N >= 16384 ? TILE_128x128 : TILE_256x128_W8;
   if (M > 64 && N >= 16384) return TILE_128x128;
   return TILE_64x64;
 }

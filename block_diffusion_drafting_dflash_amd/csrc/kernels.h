@@ -133,7 +133,8 @@ enum TileCfg : int {
   TILE_256x128 = 3,
   TILE_128x256 = 4,
   TILE_256x256 = 5,
-  TILE_NCFG = 6,
+  TILE_256x128_W8 = 6,  // 256 x 128 on eight waves of 64 x 64
+  TILE_NCFG = 7,
 };
 int plan_tiled(int M, int N);
 // Top-2 records per row that the tiled LM head writes with block shape cfg
