@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured in a HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter scale)")
     return ap.parse_args()
@@ -323,13 +325,30 @@ def main():
     # Timed region: exactly K steps, bracketed by synchronisation, with no
     # instrumentation inside (an event bound to a kernel dispatch holds the
     # stream for a few microseconds on either side of that kernel).
+    run = step
+    if args.graph:
+        # the step's launches captured once (the calls enqueue kernels only);
+        # the step closure binds the stream that is current when it is made
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            make_step(ctx, kv, lens, inp, wl, torch, dfl)()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            make_step(ctx, kv, lens, inp, wl, torch, dfl)()
+        torch.cuda.synchronize()
+        run = graph.replay
+        for _ in range(args.warmup):
+            run()
     stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(
         enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(args.steps):
-        step()
+        run()
     t1.record(stream)
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
@@ -372,7 +391,8 @@ def main():
                    "block": wl.block_size, "draft_layers": wl.num_layers,
                    "passes": wl.num_passes,
                    "commit_per_pass": wl.commit_per_pass,
-                   "new_rows_per_seq": wl.new_rows},
+                   "new_rows_per_seq": wl.new_rows,
+                   "launch": "hip_graph" if args.graph else "stream"},
         "roofline": {"kernel": kind, "bound": bound, "achieved": round(ach, 1),
                      "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
                      "traffic": measured_traffic(wl, kind),
