@@ -47,6 +47,10 @@
  *     dflash_check_device_errors() reports.
  *   - Results are bitwise reproducible from run to run: no reduction depends
  *     on scheduling order.
+ *   - A context's workspace (activations, partial sums, split-contraction
+ *     copies, the block state between passes) is shared by all its calls, so
+ *     calls on one context must not overlap: issue them on one stream, or
+ *     order the streams.  Different contexts are independent.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
