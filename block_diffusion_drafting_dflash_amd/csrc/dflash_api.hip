@@ -256,7 +256,7 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
     a.a_seg_k = a.Kd;
   }
   if (tiled) {
-    const int cfg = plan_tiled(a.M, a.N);
+    const int cfg = plan_tiled(a.M, a.N, splittable(a));
     const int S = plan_ksplit(c, a, cfg);
     TimedLaunch tl(c, kind, s);
     if (S > 1) {

@@ -406,13 +406,16 @@ int tiled_block_cols(int cfg) {
 
 // Block shape by rows and columns (measured on MI355X at 64, 256 and 1024
 // rows over the drafter's projection and LM-head shapes).
-int plan_tiled(int M, int N) {
+int plan_tiled(int M, int N, bool splittable) {
   if (DFLASH_TILED_CFG >= 0) return DFLASH_TILED_CFG;
   // above 512 rows, outputs narrower than 16384 columns take 256 x 128
   // blocks on eight waves (with split-K filling the CUs): 16% faster than
   // 128 x 128 there at 1024 rows, slower for the wide gate/up and LM head
   if (M > 512) return N >= 16384 ? TILE_128x128 : TILE_256x128_W8;
-  if (M > 64 && N >= 16384) return TILE_128x128;
+  // from 65 rows: 128 x 128 for wide outputs, and for narrow ones whose
+  // contraction can be split over the grid (at 256 rows the residual and
+  // store GEMMs take 30 us plus the reduction, against 44 us in 64 x 64)
+  if (M > 64 && (N >= 16384 || splittable)) return TILE_128x128;
   return TILE_64x64;
 }
 

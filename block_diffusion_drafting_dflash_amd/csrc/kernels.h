@@ -136,7 +136,9 @@ enum TileCfg : int {
   TILE_256x128_W8 = 6,  // 256 x 128 on eight waves of 64 x 64
   TILE_NCFG = 7,
 };
-int plan_tiled(int M, int N);
+// Block shape of an M x N tiled GEMM; `splittable`: its contraction may be
+// split (plain-store and residual epilogues).
+int plan_tiled(int M, int N, bool splittable = false);
 // Top-2 records per row that the tiled LM head writes with block shape cfg
 // (one per column block: top2[row * records + block]).
 int tiled_top2_records(int cfg, int N);
