@@ -168,15 +168,18 @@ def setup(wl, torch, dfl, dev):
     ctx = dfl.DFlash(wl, weights, max_inject_rows=max(chunk, B * wl.new_rows))
     kv = ctx.new_kv_cache(dev)
     # untimed prefix: positions [0, L_b - 16) of every sequence
+    prefill = None
     for b, L in enumerate(lens):
         n_pre = int(L) - wl.new_rows
         for c0 in range(0, n_pre, chunk):
             n = min(chunk, n_pre - c0)
             H = W.gen_hiddens(wl, n, device=dev, index=b * 100000 + c0 // chunk,
                               tag="prefix")
-            ctx.inject_kv(H, torch.full((n,), b, dtype=torch.int32, device=dev),
-                          torch.arange(c0, c0 + n, dtype=torch.int32,
-                                       device=dev), kv)
+            args = (H, torch.full((n,), b, dtype=torch.int32, device=dev),
+                    torch.arange(c0, c0 + n, dtype=torch.int32, device=dev))
+            ctx.inject_kv(*args, kv)
+            if prefill is None:
+                prefill = args  # re-injected (same rows, same values) to time
     torch.cuda.synchronize()
     T = B * wl.new_rows
     inp = {
@@ -189,6 +192,7 @@ def setup(wl, torch, dfl, dev):
         "ctx_len": torch.from_numpy(lens.astype(np.int32)).to(dev),
         "anchor": torch.from_numpy(W.gen_anchors(wl)).to(dev),
     }
+    inp["prefill"] = prefill
     draws = W.gen_verify_draws(wl)
     for k, v in draws.items():
         inp[k] = torch.from_numpy(v).to(dev)
@@ -363,6 +367,29 @@ def main():
     ms_total_ev = t0.elapsed_time(t1)
     n_launch, k_ms = ctx.kernel_timing()
     ctx.set_kernel_timing("off")
+    # Step-time spread: the same steps with one event at each step boundary.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        run()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1])
+                         for i in range(args.steps)])
+    # Injection of a whole context chunk (the untimed set-up's first call,
+    # repeated with the same rows and values).
+    prefill = None
+    if inp["prefill"] is not None:
+        H, seq, pos = inp["prefill"]
+        ctx.inject_kv(H, seq, pos, kv)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        ctx.inject_kv(H, seq, pos, kv)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        pf_ms = t0.elapsed_time(t1)
+        prefill = {"rows": int(seq.numel()), "ms": round(pf_ms, 4),
+                   "rows_per_s": round(seq.numel() / (pf_ms / 1e3), 1)}
     if ctx.check_device_errors() != 0:
         raise RuntimeError("device error during the timed steps")
     ms_step = ms_total / args.steps
@@ -405,6 +432,9 @@ def main():
                          ms_total_ev / args.steps, 5),
                      "alg_bytes_per_launch": int(kb),
                      "alg_flops_per_launch": kf},
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 5)
+                                for q in (10, 50, 90)],
+        "prefill_inject": prefill,
         "step": {"alg_bytes": int(by), "alg_flops": fl,
                  "hbm_frac": round(by / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                  "mfma_frac": round(fl / (ms_step / 1e3) / 1e12 /
