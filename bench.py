@@ -121,9 +121,12 @@ def kernel_cost(wl, lens, kind):
 
 # ---------------------------------------------------------------------------
 
+# Sources that define each timed kernel class: the LM head is the persistent
+# kernel up to 16 rows and the tiled GEMM beyond; the projection GEMMs are
+# the streaming or the tiled form with their shared epilogues.
 KERNEL_SOURCES = {
-    "lmhead": ["gemm.hip"],
-    "gemm": ["gemm.hip"],
+    "lmhead": ["gemm.hip", "gemm_tiled.hip", "gemm_epilogue.h"],
+    "gemm": ["gemm.hip", "gemm_tiled.hip", "gemm_epilogue.h"],
     "attention": ["attention.hip"],
 }
 
