@@ -230,22 +230,25 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
       // P = p1 + p2 (+ p3) in bf16 parts of 8 significant bits each
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
+        // (each pair rounded to nearest even by one packed conversion)
         constexpr int NP3 = DFLASH_ATTN_PSPLIT;
-        uint32_t pp[NP3][8];
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        float rem[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float rem = s[2 * cc + e / 4][e % 4];
-#pragma unroll
-          for (int t = 0; t < NP3; ++t) {
-            pp[t][e] = f32_to_bf16(rem);
-            rem -= bf16_to_f32(pp[t][e]);
-          }
-        }
+        for (int e = 0; e < 8; ++e) rem[e] = s[2 * cc + e / 4][e % 4];
         u32x4 bp[NP3];
 #pragma unroll
-        for (int t = 0; t < NP3; ++t)
-          bp[t] = u32x4{pp[t][0] | (pp[t][1] << 16), pp[t][2] | (pp[t][3] << 16),
-                        pp[t][4] | (pp[t][5] << 16), pp[t][6] | (pp[t][7] << 16)};
+        for (int t = 0; t < NP3; ++t) {
+          uint32_t w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bf16x2_t h = {(__bf16)rem[2 * q], (__bf16)rem[2 * q + 1]};
+            w[q] = __builtin_bit_cast(uint32_t, h);
+            rem[2 * q] -= __uint_as_float(w[q] << 16);
+            rem[2 * q + 1] -= __uint_as_float(w[q] & 0xFFFF0000u);
+          }
+          bp[t] = u32x4{w[0], w[1], w[2], w[3]};
+        }
         // lane (r, g) reads key 32cc + 4g + r/4 (+16), channels
         // 16dt + 4(r%4) .. +3, and receives channel 16dt + r of keys
         // 32cc + 4g + 0..3 (lo) and 32cc + 16 + 4g + 0..3 (hi)
