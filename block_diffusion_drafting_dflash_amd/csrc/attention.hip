@@ -188,30 +188,43 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
       for (int dc = 0; dc < DC; ++dc)
         mma16(s[mt], load16(krow + dc * KC * SZ), qf[dc], T());
     }
-    // online softmax for query r (log2 domain); keys 16mt + 4g + j
+    // online softmax for query r (log2 domain); keys 16mt + 4g + j (only a
+    // chunk's last tile can hold keys past its end: a uniform branch)
     float tmax = -INFINITY;
+    if (n_valid == kKeyTile) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = 16 * mt + 4 * g + j;
-        const float v = key < n_valid ? s[mt][j] * p.scale_log2 : -INFINITY;
-        s[mt][j] = v;
-        tmax = fmaxf(tmax, v);
-      }
+        for (int j = 0; j < 4; ++j) {
+          s[mt][j] *= p.scale_log2;
+          tmax = fmaxf(tmax, s[mt][j]);
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = 16 * mt + 4 * g + j;
+          const float v = key < n_valid ? s[mt][j] * p.scale_log2 : -INFINITY;
+          s[mt][j] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
     // the same factor scales numerator and denominator, so its rounding
     // cancels in o = numerator / denominator; once the running maxima have
     // settled the factor is 1 for every query and the rescale is skipped
-    const float alpha = exp2f(m_run - m_new);
+    // The hardware exp2 (no rescaling for results below 2^-126, which it
+    // flushes: such weights add nothing a float32 sum of values near 1 keeps)
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float lt = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float pv = exp2f(s[mt][j] - m_new);
+        const float pv = __builtin_amdgcn_exp2f(s[mt][j] - m_new);
         s[mt][j] = pv;
         lt += pv;
       }
