@@ -207,3 +207,32 @@ def test_verify_sampling_validation(batch, block, vocab, null, status):
     args = [None if null else p] + [p] * 6
     st = lib().dflash_verify_sampling(None, batch, block, vocab, *args)
     assert binding.STATUS[st] == status
+
+
+def test_bench_profile_bookkeeping():
+    """The bench keys each committed HBM-traffic summary to the sources of
+    its kernel class: every named source exists, and every summary under
+    profiles/ names a known kernel class and workload and a well-formed
+    hash and byte count (whether it still matches is decided at run time)."""
+    import bench
+    import workloads as W
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    csrc = os.path.join(root, "block_diffusion_drafting_dflash_amd", "csrc")
+    for kind, files in bench.KERNEL_SOURCES.items():
+        for f in files + ["common.h", "kernels.h"]:
+            assert os.path.exists(os.path.join(csrc, f)), (kind, f)
+        assert re.fullmatch(r"[0-9a-f]{64}", bench.kernel_source_sha(kind))
+    prof = os.path.join(root, "profiles")
+    for f in os.listdir(prof):
+        if not f.endswith("_traffic.txt"):
+            continue
+        kv = {}
+        for line in open(os.path.join(prof, f)):
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        assert kv["kernel"] in bench.KERNEL_SOURCES, f
+        assert kv["workload"] in W.WORKLOADS, f
+        assert f == f"{kv['kernel']}_{kv['workload']}_traffic.txt"
+        assert re.fullmatch(r"[0-9a-f]{64}", kv["source_sha256"]), f
+        assert int(kv["traffic_bytes_per_launch"]) > 0, f
