@@ -42,6 +42,14 @@ WLS = {
                                   name="small-bf16-b8", seed=78),
     "small-bf16-b36": W.small_bf16(batch=36, ctx_min=16, ctx_max=80,
                                    name="small-bf16-b36", seed=79),
+    # the other two query-group sizes the attention kernel is specialised
+    # for: 2 (with head_dim 128, streaming GEMMs) and 8 (tiled GEMMs)
+    "small-bf16-g2-d128": W.small_bf16(num_q_heads=4, num_kv_heads=2,
+                                       head_dim=128, name="small-bf16-g2-d128",
+                                       seed=81),
+    "small-bf16-g8-b8": W.small_bf16(num_q_heads=16, num_kv_heads=2, batch=8,
+                                     ctx_min=30, ctx_max=260,
+                                     name="small-bf16-g8-b8", seed=82),
 }
 
 
