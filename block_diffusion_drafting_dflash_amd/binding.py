@@ -28,7 +28,8 @@ LIB_SYMBOLS = ["dflash_create", "dflash_destroy", "dflash_kv_cache_bytes",
                "dflash_last_error", "dflash_check_device_errors",
                "dflash_inject_kv", "dflash_draft_block",
                "dflash_verify_greedy", "dflash_verify_sampling",
-               "dflash_set_kernel_timing", "dflash_get_kernel_timing"]
+               "dflash_set_kernel_timing", "dflash_get_kernel_timing",
+               "dflash_set_kv_pages", "dflash_kv_cache_paged_bytes"]
 TIME_KIND = {"off": 0, "lmhead": 1, "attention": 2, "gemm": 3}
 HARNESS_SYMBOLS = ["dflash_harness_synth_target"]
 
@@ -102,6 +103,11 @@ def load_library():
     lib.dflash_get_kernel_timing.argtypes = [vp, ctypes.POINTER(i32),
                                              ctypes.POINTER(ctypes.c_double)]
     lib.dflash_get_kernel_timing.restype = ctypes.c_int
+    lib.dflash_set_kv_pages.argtypes = [vp, i32, i32, vp, i32]
+    lib.dflash_set_kv_pages.restype = ctypes.c_int
+    lib.dflash_kv_cache_paged_bytes.argtypes = [ctypes.POINTER(Config), i32,
+                                                i32]
+    lib.dflash_kv_cache_paged_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -154,6 +160,11 @@ def make_config(wl, max_batch=None, max_ctx=None,
 
 def kv_cache_bytes(cfg: Config) -> int:
     return int(load_library().dflash_kv_cache_bytes(ctypes.byref(cfg)))
+
+
+def kv_cache_paged_bytes(cfg: Config, page_size: int, num_pages: int) -> int:
+    return int(load_library().dflash_kv_cache_paged_bytes(
+        ctypes.byref(cfg), page_size, num_pages))
 
 
 class DFlash:
@@ -212,6 +223,31 @@ class DFlash:
         return torch.zeros(c.num_layers, 2, c.max_batch, c.num_kv_heads,
                            c.max_ctx + c.block_size, c.head_dim,
                            dtype=self.torch_dtype, device=device)
+
+    def set_kv_pages(self, page_size: int, num_pages: int = 0,
+                     block_table: Optional[torch.Tensor] = None):
+        """Paged cache addressing for the following calls (page_size 0:
+        contiguous).  block_table: [max_batch, pages per slot] int32 on the
+        device, kept alive by this object while in use."""
+        if page_size == 0:
+            _check(self.lib.dflash_set_kv_pages(self.ctx, 0, 0, None, 0))
+            self._block_table = None
+            return
+        if (block_table.dtype != torch.int32 or block_table.dim() != 2
+                or not block_table.is_contiguous()):
+            raise ValueError("block_table: contiguous int32 [max_batch, ld]")
+        _check(self.lib.dflash_set_kv_pages(
+            self.ctx, page_size, num_pages, _ptr(block_table),
+            block_table.shape[1]))
+        self._block_table = block_table
+
+    def new_kv_cache_paged(self, page_size: int, num_pages: int,
+                           device="cuda") -> torch.Tensor:
+        """[N_l, 2, num_pages, Hkv, page_size, d] in the drafter dtype."""
+        c = self.cfg
+        return torch.zeros(c.num_layers, 2, num_pages, c.num_kv_heads,
+                           page_size, c.head_dim, dtype=self.torch_dtype,
+                           device=device)
 
     # -- entry points -------------------------------------------------------
     def inject_kv(self, hiddens: Sequence[torch.Tensor], row_seq: torch.Tensor,

@@ -128,14 +128,22 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
   const int r = lane & 15, g = lane >> 4;
   const int hq = kvh * G + wave;
 
-  const int64_t head_off = ((int64_t)b * p.Hkv + kvh) * p.P * D;
-  const char* kbase = static_cast<const char*>(p.kc) + head_off * SZ;
-  const char* vbase = static_cast<const char*>(p.vc) + head_off * SZ;
+  // K/V of the 64-key tile at kt: load_tile adds key * D to these bases.
+  // A tile never straddles a page (pages hold a multiple of 64 positions);
+  // a tile past the chunk's end reads the chunk's last key, so its page is
+  // the last key's.
+  auto load_at = [&](TileRegs<T, D, G>& t, int kt) {
+    const int pk = min(kt, k1 - 1);
+    const int first = p.pages.log2 < 0 ? 0 : (pk >> p.pages.log2) << p.pages.log2;
+    const int64_t off =
+        (kv_row(p.pages, p.P, p.Hkv, b, kvh, first, p.err) - first) * D * SZ;
+    load_tile<T, D, G>(t, static_cast<const char*>(p.kc) + off,
+                       static_cast<const char*>(p.vc) + off, kt, k1 - 1, tid);
+  };
   TileRegs<T, D, G> regs0, regs1, regs2;
-  load_tile<T, D, G>(regs0, kbase, vbase, k0, k1 - 1, tid);
-  load_tile<T, D, G>(regs1, kbase, vbase, k0 + kKeyTile, k1 - 1, tid);
-  if constexpr (kSets == 3)
-    load_tile<T, D, G>(regs2, kbase, vbase, k0 + 2 * kKeyTile, k1 - 1, tid);
+  load_at(regs0, k0);
+  load_at(regs1, k0 + kKeyTile);
+  if constexpr (kSets == 3) load_at(regs2, k0 + 2 * kKeyTile);
 
   // Q fragments of this wave's head: lane (query r, group g)
   const char* qrow = static_cast<const char*>(p.q) +
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
       }
     }
     __syncthreads();
-    load_tile<T, D, G>(rg, kbase, vbase, kt + kSets * kKeyTile, k1 - 1, tid);
+    load_at(rg, kt + kSets * kKeyTile);
     if (kt >= k1) return;  // past the chunk's last tile: nothing to compute
     const int n_valid = min(kKeyTile, k1 - kt);
 

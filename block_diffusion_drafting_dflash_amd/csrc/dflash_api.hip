@@ -102,6 +102,8 @@ struct dflash_ctx {
   float* attn_ml = nullptr;
   int* err = nullptr;
 
+  KvPages pages;  // KV cache addressing (dflash_set_kv_pages)
+
   // benchmark timing of one kernel class (dflash_set_kernel_timing)
   int time_kind = 0;
   std::vector<hipEvent_t> ev_start, ev_stop;
@@ -308,6 +310,7 @@ void set_cache_geometry(GemmArgs& a, const dflash_ctx* c) {
   a.P = c->P;
   a.max_ctx = c->cfg.max_ctx;
   a.rope = c->rope;
+  a.pages = c->pages;
 }
 
 }  // namespace
@@ -321,6 +324,43 @@ size_t dflash_kv_cache_bytes(const dflash_config* c) {
   const size_t esz = c->dtype == DFLASH_F32 ? 4 : 2;
   return (size_t)c->num_layers * 2 * c->max_batch * c->num_kv_heads *
          (size_t)(c->max_ctx + c->block_size) * c->head_dim * esz;
+}
+
+size_t dflash_kv_cache_paged_bytes(const dflash_config* c, int32_t page_size,
+                                   int32_t num_pages) {
+  if (!c || c->num_layers < 1 || page_size < 1 || num_pages < 1) return 0;
+  const size_t esz = c->dtype == DFLASH_F32 ? 4 : 2;
+  return (size_t)c->num_layers * 2 * num_pages * c->num_kv_heads *
+         (size_t)page_size * c->head_dim * esz;
+}
+
+dflash_status dflash_set_kv_pages(dflash_ctx* ctx, int32_t page_size,
+                                  int32_t num_pages,
+                                  const int32_t* block_table,
+                                  int32_t table_ld) {
+  g_last_error.clear();
+  if (!ctx) return fail(DFLASH_E_INVALID, "ctx is NULL");
+  if (page_size == 0) {
+    ctx->pages = KvPages{};
+    return DFLASH_OK;
+  }
+  int log2 = 0;
+  while ((1 << log2) < page_size && log2 < 30) ++log2;
+  if (page_size < 64 || (1 << log2) != page_size)
+    return fail(DFLASH_E_SHAPE,
+                "page_size %d: a power of two of at least 64 (or 0)", page_size);
+  if (num_pages < 1) return fail(DFLASH_E_SHAPE, "num_pages %d < 1", num_pages);
+  if (!block_table) return fail(DFLASH_E_INVALID, "block_table is NULL");
+  const int64_t cap = (int64_t)table_ld * page_size;
+  if (table_ld < 1 || cap < ctx->P)
+    return fail(DFLASH_E_SHAPE,
+                "table_ld %d pages of %d positions < max_ctx + block_size %d",
+                table_ld, page_size, ctx->P);
+  ctx->pages.table = block_table;
+  ctx->pages.ld = table_ld;
+  ctx->pages.log2 = log2;
+  ctx->pages.npages = num_pages;
+  return DFLASH_OK;
 }
 
 void dflash_destroy(dflash_ctx* ctx) {
@@ -685,10 +725,14 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
             Hkv = c.num_kv_heads, I = c.intermediate, V = c.vocab;
   const int qd = Hq * d, kvd = Hkv * d;
   const int R = batch * K;
-  const size_t layer_elems = (size_t)2 * c.max_batch * Hkv * ctx->P * d;
+  const size_t plane_elems =
+      (size_t)kv_plane_rows(ctx->pages, c.max_batch, Hkv, ctx->P) * d;
+  const size_t layer_elems = 2 * plane_elems;
   BlockState bs{ctx->tokens, ctx->committed, ctx->rowmap, ctx->err};
 
   AttnArgs at{};
+  at.pages = ctx->pages;
+  at.err = ctx->err;
   at.q = ctx->qb;
   at.ctx_len = ctx_len;
   at.max_len = max_ctx_len;
@@ -735,7 +779,7 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
       dflash_status st = run_gemm(ctx, a, s);
       if (st != DFLASH_OK) return st;
       at.kc = kvl;
-      at.vc = kvl + (size_t)c.max_batch * Hkv * ctx->P * d * ctx->esz;
+      at.vc = kvl + plane_elems * ctx->esz;
       {
         TimedLaunch tl(ctx, DFLASH_TIME_ATTENTION, s);
         DF_HIP(launch_attention(bf, d, batch, at, s));

@@ -74,8 +74,8 @@ __device__ __forceinline__ void pair_epilogue(const GemmArgs& p, int row,
       const bool is_k = head < p.Hq + p.Hkv;
       const int h = is_k ? head - p.Hq : head - p.Hq - p.Hkv;
       dst = static_cast<T*>(p.kv) +
-            (is_k ? 0 : (int64_t)p.max_batch * p.Hkv * p.P * p.d) +
-            (((int64_t)bs * p.Hkv + h) * p.P + pos) * p.d;
+            (is_k ? 0 : kv_plane_rows(p.pages, p.max_batch, p.Hkv, p.P) * p.d) +
+            kv_row(p.pages, p.P, p.Hkv, bs, h, pos, p.err) * p.d;
       if (is_k) {
         rope_pair(a, b, cs, ra, rb);
       } else {
@@ -100,9 +100,10 @@ __device__ __forceinline__ void pair_epilogue(const GemmArgs& p, int row,
   const int l = head / (2 * p.Hkv), w = head % (2 * p.Hkv);
   const bool is_k = w < p.Hkv;
   const int h = is_k ? w : w - p.Hkv;
-  const int64_t plane = (int64_t)p.max_batch * p.Hkv * p.P * p.d;
+  const int64_t plane =
+      kv_plane_rows(p.pages, p.max_batch, p.Hkv, p.P) * p.d;
   T* dst = static_cast<T*>(p.kv) + (2 * l + (is_k ? 0 : 1)) * plane +
-           (((int64_t)seq * p.Hkv + h) * p.P + pos) * p.d;
+           kv_row(p.pages, p.P, p.Hkv, seq, h, pos, p.err) * p.d;
   double ra = a, rb = b;
   if (is_k) rope_pair(a, b, p.rope[(int64_t)pos * half + i], ra, rb);
   store_elem(dst, i, ra);
@@ -145,8 +146,8 @@ __device__ __forceinline__ void pair_epilogue8(const GemmArgs& p, int row,
       const bool is_k = head < p.Hq + p.Hkv;
       const int h = is_k ? head - p.Hq : head - p.Hq - p.Hkv;
       dst = static_cast<bf16_t*>(p.kv) +
-            (is_k ? 0 : (int64_t)p.max_batch * p.Hkv * p.P * p.d) +
-            (((int64_t)bs * p.Hkv + h) * p.P + pos) * p.d;
+            (is_k ? 0 : kv_plane_rows(p.pages, p.max_batch, p.Hkv, p.P) * p.d) +
+            kv_row(p.pages, p.P, p.Hkv, bs, h, pos, p.err) * p.d;
       rot = is_k;
     }
   } else {  // EP_KV: injected context rows
@@ -163,9 +164,10 @@ __device__ __forceinline__ void pair_epilogue8(const GemmArgs& p, int row,
     const int l = head / (2 * p.Hkv), w = head % (2 * p.Hkv);
     const bool is_k = w < p.Hkv;
     const int h = is_k ? w : w - p.Hkv;
-    const int64_t plane = (int64_t)p.max_batch * p.Hkv * p.P * p.d;
+    const int64_t plane =
+        kv_plane_rows(p.pages, p.max_batch, p.Hkv, p.P) * p.d;
     dst = static_cast<bf16_t*>(p.kv) + (2 * l + (is_k ? 0 : 1)) * plane +
-          (((int64_t)seq * p.Hkv + h) * p.P + pos) * p.d;
+          kv_row(p.pages, p.P, p.Hkv, seq, h, pos, p.err) * p.d;
     rot = is_k;
   }
   u32x4 wa, wb;

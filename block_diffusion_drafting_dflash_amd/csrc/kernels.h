@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/dflash.h"
 #include "common.h"
 
 namespace dflash {
@@ -79,6 +80,35 @@ enum Epilogue : int {
   EP_TOP2 = 5,    // LM head: per row (max, argmax, 2nd max, sum exp)
 };
 
+// KV cache addressing.  Contiguous (log2 < 0): a layer's K (or V) plane is
+// [max_batch][Hkv][P][d].  Paged: it is [npages][Hkv][1 << log2][d] and
+// position pos of sequence seq lives in page table[seq * ld + (pos >> log2)].
+struct KvPages {
+  const int32_t* table = nullptr;
+  int ld = 0;
+  int log2 = -1;
+  int npages = 0;
+};
+// Row (in units of d elements) of (seq, kv head h, pos) within one plane; a
+// page id out of range sets DFLASH_DEVERR_PAGE and addresses page 0.
+__device__ __forceinline__ int64_t kv_row(const KvPages& g, int P, int Hkv,
+                                          int seq, int h, int pos, int* err) {
+  if (g.log2 < 0) return ((int64_t)seq * Hkv + h) * P + pos;
+  int page = g.table[(int64_t)seq * g.ld + (pos >> g.log2)];
+  if (page < 0 || page >= g.npages) {
+    set_error(err, DFLASH_DEVERR_PAGE);
+    page = 0;
+  }
+  return (((int64_t)page * Hkv + h) << g.log2) + (pos & ((1 << g.log2) - 1));
+}
+// Rows of one plane.
+__host__ __device__ __forceinline__ int64_t kv_plane_rows(const KvPages& g,
+                                                          int max_batch,
+                                                          int Hkv, int P) {
+  return g.log2 < 0 ? (int64_t)max_batch * Hkv * P
+                    : ((int64_t)g.npages * Hkv) << g.log2;
+}
+
 // C[M, N] = A[M, Kd] . W[N, Kd]^T.  W is packed; A is packed (a_packed) or
 // row-major with up to kMaxASeg segments along the contraction (the
 // concatenated target layers).  A workgroup owns one 16-column tile and 16*MT
@@ -103,6 +133,7 @@ struct GemmArgs {
   const int32_t* row_seq;  // EP_KV
   const int32_t* row_pos;
   int Hq, Hkv, d, max_batch, P, max_ctx;
+  KvPages pages;           // EP_QKV / EP_KV cache addressing
   Top2* top2;              // EP_TOP2: [M][N / 16]
   float* logits;           // EP_TOP2 debug rows (via rowmap), may be null
   const int32_t* rowmap;   //   LM-head row -> block row b*K + i, or -1
@@ -194,11 +225,13 @@ hipError_t launch_rmsnorm(bool bf16, int rows, int D, const float* x,
 // ---- attention (attention.hip) -----------------------------------------
 struct AttnArgs {
   const void* q;        // [B*K][Hq*d] row-major
-  const void* kc;       // this layer's K cache [max_batch][Hkv][P][d]
+  const void* kc;       // this layer's K plane (see KvPages)
   const void* vc;       // this layer's V cache
   const int32_t* ctx_len;
   int max_len;          // host bound on ctx_len (grid sized for it)
   int P, Hq, Hkv, K;
+  KvPages pages;        // cache addressing (contiguous or paged)
+  int* err;             // device error word (page ids)
   int chunk, nch;       // keys per workgroup, chunks per (sequence, kv head)
   float scale_log2;     // log2(e) / sqrt(d)
   float* part_o;        // [B][Hq][nch][K][d]

@@ -78,6 +78,7 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 #define DFLASH_DEVERR_CTX_LEN  0x2  /* context length outside [0, max_ctx_len] */
 #define DFLASH_DEVERR_SLOT     0x4  /* inject row's sequence slot out of range */
 #define DFLASH_DEVERR_POS      0x8  /* inject row's position out of range */
+#define DFLASH_DEVERR_PAGE     0x10 /* KV page id outside [0, num_pages) */
 
 /* Drafter shape and capacities.  Supported: block_size == 16; head_dim 64 or
  * 128; num_q_heads equal to 2, 4 or 8 times num_kv_heads; hidden,
@@ -145,6 +146,37 @@ void dflash_destroy(dflash_ctx* ctx);
  * Layout kv[layer][0 = K | 1 = V][slot][kv_head][pos][head_dim].  Positions
  * [L, L + block_size) of a slot are scratch for the block being drafted. */
 size_t dflash_kv_cache_bytes(const dflash_config* cfg);
+
+/* Paged KV cache (serving-style storage of the context K/V; the pages'
+ * method is unchanged, only where each position's K/V lives).
+ *
+ * dflash_set_kv_pages switches the context's cache addressing for the calls
+ * that follow (inject, draft) from the contiguous layout above to pages:
+ *   kv[layer][0 = K | 1 = V][page][kv_head][page_size][head_dim],
+ * with position pos of slot s in page block_table[s * table_ld + pos /
+ * page_size].  The cache then takes dflash_kv_cache_paged_bytes(cfg,
+ * page_size, num_pages) bytes.
+ *
+ * page_size:   a power of two >= 64 (attention tiles of 64 keys never cross
+ *              a page), or 0 to return to the contiguous layout.
+ * num_pages:   pages per layer plane in the cache.
+ * block_table: DEVICE int32 [max_batch][table_ld], owned by the caller and
+ *              read by every later call (its contents may change between
+ *              calls on the same stream).  Entries must exist for positions
+ *              [0, L + block_size) of every slot drafted or injected; an id
+ *              outside [0, num_pages) reads and writes page 0 and sets
+ *              DFLASH_DEVERR_PAGE.
+ * table_ld:    pages per slot; table_ld * page_size >= max_ctx + block_size.
+ * Errors: DFLASH_E_INVALID (NULL ctx or table), DFLASH_E_SHAPE (sizes).
+ * Results are identical to the contiguous layout's. */
+dflash_status dflash_set_kv_pages(dflash_ctx* ctx, int32_t page_size,
+                                  int32_t num_pages,
+                                  const int32_t* block_table,
+                                  int32_t table_ld);
+/* num_layers * 2 * num_pages * num_kv_heads * page_size * head_dim
+ * * sizeof(dtype); 0 for invalid arguments. */
+size_t dflash_kv_cache_paged_bytes(const dflash_config* cfg, int32_t page_size,
+                                   int32_t num_pages);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* dflash_last_error(void);
