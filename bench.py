@@ -50,6 +50,9 @@ def parse():
                     help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured in a HIP graph")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="paged KV cache with pages of this many positions "
+                         "(handed out in a shuffled order); 0: contiguous")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter scale)")
     return ap.parse_args()
@@ -163,13 +166,28 @@ def measured_traffic(wl, kind):
         return None
 
 
-def setup(wl, torch, dfl, dev):
+def setup(wl, torch, dfl, dev, page_size=0):
     weights = W.gen_weights(wl, device=dev)
     lens = W.gen_ctx_lens(wl)
     B, K = wl.batch, wl.block_size
     chunk = 2048
     ctx = dfl.DFlash(wl, weights, max_inject_rows=max(chunk, B * wl.new_rows))
-    kv = ctx.new_kv_cache(dev)
+    if page_size:
+        # pages for positions [0, L_b + K) of every sequence, in a shuffled
+        # order; -1 (never read) past each sequence's last page
+        need = [(int(L) + K + page_size - 1) // page_size for L in lens]
+        ld = (ctx.cfg.max_ctx + K + page_size - 1) // page_size
+        perm = np.random.default_rng(1).permutation(sum(need))
+        table = np.full((ctx.cfg.max_batch, ld), -1, dtype=np.int32)
+        k = 0
+        for b, n in enumerate(need):
+            table[b, :n] = perm[k:k + n]
+            k += n
+        kv = ctx.new_kv_cache_paged(page_size, sum(need), dev)
+        ctx.set_kv_pages(page_size, sum(need),
+                         torch.from_numpy(table).to(dev))
+    else:
+        kv = ctx.new_kv_cache(dev)
     # untimed prefix: positions [0, L_b - 16) of every sequence
     prefill = None
     for b, L in enumerate(lens):
@@ -321,7 +339,7 @@ def main():
                 "qwen3-8b-3L-b64-ctx256-2k-S2": "gemm",
                 "qwen3-8b-5L-b16-ctx1k-4k": "gemm"}.get(wl.name, "lmhead")
 
-    ctx, kv, lens, inp, weights = setup(wl, torch, dfl, dev)
+    ctx, kv, lens, inp, weights = setup(wl, torch, dfl, dev, args.page_size)
     step = make_step(ctx, kv, lens, inp, wl, torch, dfl)
     for _ in range(args.warmup):
         step()
@@ -422,7 +440,9 @@ def main():
                    "passes": wl.num_passes,
                    "commit_per_pass": wl.commit_per_pass,
                    "new_rows_per_seq": wl.new_rows,
-                   "launch": "hip_graph" if args.graph else "stream"},
+                   "launch": "hip_graph" if args.graph else "stream",
+                   "kv_cache": (f"paged-{args.page_size}" if args.page_size
+                                else "contiguous")},
         "roofline": {"kernel": kind, "bound": bound, "achieved": round(ach, 1),
                      "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
                      "traffic": measured_traffic(wl, kind),
