@@ -120,15 +120,18 @@ void free_events(dflash_ctx* c) {
   c->ev_next = c->ev_count = 0;
 }
 
-// Arms one event pair for the launches of the timed kernel class made in
-// its scope; the kernels bind the events to their dispatches (launch_k).
+// Arms one event pair for the `kernels` launches of the timed kernel class
+// made in its scope: the first dispatch takes the start event, the last the
+// stop event (launch_k), so no event sits between them.
 struct TimedLaunch {
   dflash_ctx* c;
   bool on = false;
-  TimedLaunch(dflash_ctx* ctx, int kind, hipStream_t) : c(ctx) {
+  TimedLaunch(dflash_ctx* ctx, int kind, hipStream_t, int kernels = 1)
+      : c(ctx) {
     if (c->time_kind == kind && !c->ev_start.empty()) {
       on = true;
-      dispatch_timing() = {c->ev_start[c->ev_next], c->ev_stop[c->ev_next]};
+      dispatch_timing() = {c->ev_start[c->ev_next], c->ev_stop[c->ev_next],
+                           kernels};
     }
   }
   ~TimedLaunch() {
@@ -260,7 +263,7 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
   if (tiled) {
     const int cfg = plan_tiled(a.M, a.N, splittable(a));
     const int S = plan_ksplit(c, a, cfg);
-    TimedLaunch tl(c, kind, s);
+    TimedLaunch tl(c, kind, s, S > 1 ? 2 : 1);
     if (S > 1) {
       // split copies into the workspace, then summed in order into the
       // output (plain store or residual add)
@@ -781,7 +784,7 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
       at.kc = kvl;
       at.vc = kvl + plane_elems * ctx->esz;
       {
-        TimedLaunch tl(ctx, DFLASH_TIME_ATTENTION, s);
+        TimedLaunch tl(ctx, DFLASH_TIME_ATTENTION, s, at.nch > 1 ? 2 : 1);
         DF_HIP(launch_attention(bf, d, batch, at, s));
       }
       // x += o . Wo^T

@@ -17,7 +17,8 @@ namespace dflash {
 // any event packet of its own entering the stream.
 struct DispatchTiming {
   hipEvent_t start = nullptr;  // taken by the next launch
-  hipEvent_t stop = nullptr;
+  hipEvent_t stop = nullptr;   // taken by the last of `kernels` launches
+  int kernels = 1;
 };
 DispatchTiming& dispatch_timing();  // per host thread
 
@@ -25,9 +26,10 @@ template <typename F, typename... Args>
 inline void launch_k(F kernel, dim3 grid, dim3 block, uint32_t shm,
                      hipStream_t s, Args... args) {
   DispatchTiming& t = dispatch_timing();
-  hipExtLaunchKernelGGL(kernel, grid, block, shm, s, t.start, t.stop, 0u,
-                        args...);
+  hipExtLaunchKernelGGL(kernel, grid, block, shm, s, t.start,
+                        t.kernels <= 1 ? t.stop : nullptr, 0u, args...);
   t.start = nullptr;
+  if (t.kernels > 1) --t.kernels;
 }
 
 constexpr int kMaxASeg = 8;
