@@ -152,3 +152,83 @@ def test_set_kv_pages_rejects_bad_geometry():
     ctx.set_kv_pages(64, 4, table)
     ctx.set_kv_pages(0)
     say("[paged] geometry checks raise")
+
+
+def test_paged_step_in_a_hip_graph_follows_table_updates():
+    """Serving pattern: the step is captured once with a paged cache; the
+    block table is device memory read at run time, so moving a sequence's
+    pages (copy the page contents, rewrite the table in place) between
+    replays must give the same results."""
+    wl = W.small_bf16(batch=8, ctx_min=20, ctx_max=150, name="small-bf16-b8",
+                      seed=78)
+    ps = 64
+    say("[paged graph] small-bf16-b8, pages of 64")
+    ctx = dfl.DFlash(wl, to_dev(W.gen_weights(wl)))
+    K, B, n_new = wl.block_size, wl.batch, wl.new_rows
+    cfg = ctx.cfg
+    lens = W.gen_ctx_lens(wl)
+    ld = (cfg.max_ctx + K + ps - 1) // ps
+    table, num_pages = _page_table(lens, K, ps, ld, cfg.max_batch, 11)
+    table_d = torch.from_numpy(table).to(DEV)
+    kv = ctx.new_kv_cache_paged(ps, num_pages)
+    ctx.set_kv_pages(ps, num_pages, table_d)
+    for b, L in enumerate(lens):  # context before the step's new rows
+        n_pre = int(L) - n_new
+        if n_pre <= 0:
+            continue
+        H = W.gen_hiddens(wl, n_pre, index=b, tag="prefix")
+        ctx.inject_kv([h.to(DEV) for h in H],
+                      torch.full((n_pre,), b, dtype=torch.int32, device=DEV),
+                      torch.arange(n_pre, dtype=torch.int32, device=DEV), kv)
+    H = [h.to(DEV) for h in W.gen_hiddens(wl, B * n_new, index=0, tag="step")]
+    row_seq = torch.arange(B, dtype=torch.int32,
+                           device=DEV).repeat_interleave(n_new)
+    row_pos = torch.from_numpy(np.concatenate(
+        [np.arange(int(L) - n_new, int(L)) for L in lens]).astype(
+            np.int32)).to(DEV)
+    ctx_len = torch.from_numpy(lens.astype(np.int32)).to(DEV)
+    anchor = torch.from_numpy(W.gen_anchors(wl)).to(DEV)
+    draft = torch.empty(B, K - 1, dtype=torch.int32, device=DEV)
+    conf = torch.empty(B, K - 1, dtype=torch.float32, device=DEV)
+
+    def step():
+        ctx.inject_kv(H, row_seq, row_pos, kv)
+        ctx.draft_block(ctx_len, kv, int(lens.max()), anchor=anchor,
+                        draft=draft, conf=conf)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (draft.clone(), conf.clone())
+    assert ctx.check_device_errors() == 0
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(12)
+    for rep in range(3):
+        # move every used page to a new slot of the pool
+        used = table[table >= 0]
+        new_ids = rng.permutation(num_pages)
+        moved = kv.clone()
+        moved[:, :, torch.from_numpy(new_ids[used].astype(np.int64)).to(DEV)] = \
+            kv[:, :, torch.from_numpy(used.astype(np.int64)).to(DEV)]
+        kv.copy_(moved)
+        table = np.where(table >= 0, new_ids[np.maximum(table, 0)], -1).astype(
+            np.int32)
+        table_d.copy_(torch.from_numpy(table))
+        draft.fill_(-1)
+        conf.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(draft, ref[0]) and torch.equal(conf, ref[1]), \
+            f"replay {rep} after moving the pages differs from eager"
+        say(f"  replay {rep}: pages moved, draft and confidence equal eager")
+    assert ctx.check_device_errors() == 0
