@@ -57,6 +57,10 @@ __global__ __launch_bounds__(256) void embed_kernel(
         if (com && i > 0) draft[b * (K - 1) + i - 1] = tok;
       } else {
         tok = st.tokens[row];
+        if (tok < 0 || tok >= V) {  // a commit that found no finite logit
+          set_error(st.err, DFLASH_DEVERR_TOKEN);
+          tok = min(max(tok, 0), V - 1);
+        }
       }
       tok_s = tok;
     }

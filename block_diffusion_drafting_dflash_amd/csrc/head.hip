@@ -85,10 +85,15 @@ __global__ __launch_bounds__(64 * kCommitWaves) void commit_kernel(
     if (mj && (cj > cf || (cj == cf && j < i))) ++better;
   }
   if (masked && (last || better < quota)) {
-    st.tokens[b * K + i] = r.i1;
+    // a row whose maximum is not a finite logit (NaN activations leave the
+    // record empty): id -1, flagged
+    const bool ok = r.m1 > -INFINITY && r.m1 < INFINITY;
+    if (!ok) set_error(st.err, DFLASH_DEVERR_TOKEN);
+    const int tok = ok ? r.i1 : -1;
+    st.tokens[b * K + i] = tok;
     st.committed[b * K + i] = 1;
     const int64_t o = (int64_t)b * (K - 1) + (i - 1);
-    draft[o] = r.i1;
+    draft[o] = tok;
     if (conf_out) conf_out[o] = cf;
     if (margin_out) margin_out[o] = r.m1 - r.m2;
   }

@@ -74,7 +74,7 @@ typedef enum {
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
 /* Device error word bits (dflash_check_device_errors). */
-#define DFLASH_DEVERR_TOKEN    0x1  /* token id outside [0, vocab) */
+#define DFLASH_DEVERR_TOKEN    0x1  /* token id outside [0, vocab), or a drafted position whose logits had no finite maximum (id -1) */
 #define DFLASH_DEVERR_CTX_LEN  0x2  /* context length outside [0, max_ctx_len] */
 #define DFLASH_DEVERR_SLOT     0x4  /* inject row's sequence slot out of range */
 #define DFLASH_DEVERR_POS      0x8  /* inject row's position out of range */

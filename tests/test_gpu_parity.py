@@ -342,6 +342,30 @@ def test_draft_is_deterministic():
         np.testing.assert_array_equal(a[k], b[k])
 
 
+def test_draft_rows_without_finite_logits_are_flagged():
+    """Regression: an LM head whose logits are all NaN leaves a row with no
+    argmax (id -1).  The commit flags it (token error bit) and the next
+    refinement pass, which embeds every committed id, clamps it into the
+    vocabulary instead of reading outside the embedding."""
+    wl = WLS["small-bf16"]
+    w_cpu, w_dev, _ = _setup(wl)
+    w_dev = dict(w_dev)
+    w_dev["lm_head"] = torch.full_like(w_dev["lm_head"], float("nan"))
+    ctx = dfl.DFlash(wl, w_dev)
+    lens = W.gen_ctx_lens(wl)
+    kv, _ = _seeded_cache(wl, ctx, lens)
+    B, K1 = len(lens), wl.block_size - 1
+    draft = torch.full((B, K1), -7, dtype=torch.int32, device=DEV)
+    ctx.draft_block(torch.from_numpy(np.asarray(lens, np.int32)).to(DEV), kv,
+                    int(max(lens)),
+                    anchor=torch.from_numpy(W.gen_anchors(wl)).to(DEV),
+                    num_passes=2, commit_per_pass=8, draft=draft)
+    torch.cuda.synchronize()
+    assert ctx.check_device_errors() & 0x1
+    assert (draft.cpu().numpy() == -1).all()
+    assert ctx.check_device_errors() == 0
+
+
 # -------------------------------------------------------- whole step ------
 
 @pytest.mark.parametrize("name", list(WLS))
