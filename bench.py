@@ -397,6 +397,16 @@ def main():
     torch.cuda.synchronize()
     per_step = np.array([evs[i].elapsed_time(evs[i + 1])
                          for i in range(args.steps)])
+    # Host cost of issuing one step (the calls only enqueue work): each step
+    # is issued onto an idle stream, timed on the host clock until the calls
+    # return, then synchronised.
+    host_us = []
+    for _ in range(min(args.steps, 20)):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        run()
+        host_us.append((time.perf_counter() - h0) * 1e6)
+    torch.cuda.synchronize()
     # Injection of a whole context chunk (the untimed set-up's first call,
     # repeated with the same rows and values).
     prefill = None
@@ -458,6 +468,7 @@ def main():
         "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 5)
                                 for q in (10, 50, 90)],
         "prefill_inject": prefill,
+        "host_enqueue_us_per_step": round(float(np.median(host_us)), 1),
         "step": {"alg_bytes": int(by), "alg_flops": fl,
                  "hbm_frac": round(by / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                  "mfma_frac": round(fl / (ms_step / 1e3) / 1e12 /
