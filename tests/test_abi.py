@@ -147,6 +147,17 @@ def test_kv_cache_bytes_layout():
     assert lib().dflash_kv_cache_bytes(ctypes.byref(cfg)) == 0
 
 
+def test_kv_cache_paged_bytes_layout():
+    wl = W.small_bf16()
+    cfg = binding.make_config(wl, max_batch=5, max_ctx=1000)
+    want = wl.num_layers * 2 * 37 * wl.num_kv_heads * 64 * wl.head_dim * 2
+    assert lib().dflash_kv_cache_paged_bytes(ctypes.byref(cfg), 64, 37) == want
+    assert binding.kv_cache_paged_bytes(cfg, 64, 37) == want
+    assert lib().dflash_kv_cache_paged_bytes(ctypes.byref(cfg), 0, 37) == 0
+    assert lib().dflash_kv_cache_paged_bytes(ctypes.byref(cfg), 64, 0) == 0
+    assert lib().dflash_kv_cache_paged_bytes(None, 64, 37) == 0
+
+
 def test_calls_with_null_context_are_rejected():
     L = lib()
     p = ctypes.c_void_p(16)
@@ -158,6 +169,8 @@ def test_calls_with_null_context_are_rejected():
     assert binding.STATUS[L.dflash_set_kernel_timing(None, 1)] == \
         "DFLASH_E_INVALID"
     assert binding.STATUS[L.dflash_check_device_errors(None, None, None)] == \
+        "DFLASH_E_INVALID"
+    assert binding.STATUS[L.dflash_set_kv_pages(None, 64, 4, p, 8)] == \
         "DFLASH_E_INVALID"
 
 
