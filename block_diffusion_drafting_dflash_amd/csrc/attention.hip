@@ -359,10 +359,11 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
 // One wave per (sequence, query head, block query): lane c reads chunk c's
 // (m, l) so the weights come from wave reductions (fixed butterfly order);
 // the partial outputs are then summed in chunk order, lane owning D/64
-// consecutive channels, with kMergeBatch chunks' loads in flight.
-constexpr int kMergeBatch = 32;
-
-template <typename T, int D>
+// consecutive channels, with MB chunks' loads in flight (the smallest of 4,
+// 8, 16 and 32 that covers the grid's chunk count, so few chunks do not
+// issue loads that repeat the last one).  The sums run in chunk order
+// whatever MB is.
+template <typename T, int D, int MB>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
   constexpr int DPL = D / 64;
   const int wrow = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -382,10 +383,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
   // so the loads are made unconditionally (clamped to the slots, not to the
   // row's own chunk count, which needs ctx_len first) and the values of
   // chunks past nc are dropped below.
-  float v[kMergeBatch][DPL];
+  float v[MB][DPL];
   auto load_batch = [&](int c0) {
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
+    for (int u = 0; u < MB; ++u) {
       const int c = min(c0 + u, p.nch - 1);
 #pragma unroll
       for (int e = 0; e < DPL; ++e) v[u][e] = ob[(int64_t)c * D + e];
@@ -410,10 +411,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
   double acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0;
-  for (int c0 = 0; c0 < nc; c0 += kMergeBatch) {
+  for (int c0 = 0; c0 < nc; c0 += MB) {
     if (c0 > 0) load_batch(c0);
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
+    for (int u = 0; u < MB; ++u) {
       const int c = c0 + u;  // uniform across the wave
       if (c < nc) {
         const float w = c < 64 ? __shfl(w_l, c, 64) : exp2f(ml[c].x - M);
@@ -438,8 +439,15 @@ hipError_t attn_t(int B, const AttnArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (a.nch == 1) return hipSuccess;  // the partial kernel normalised
   const int rows = B * a.Hq * a.K;
-  launch_k((attn_merge_kernel<T, D>), dim3((rows + 3) / 4),
-                     dim3(256), 0, s, a, rows);
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (a.nch <= 4)
+    launch_k((attn_merge_kernel<T, D, 4>), grid, block, 0, s, a, rows);
+  else if (a.nch <= 8)
+    launch_k((attn_merge_kernel<T, D, 8>), grid, block, 0, s, a, rows);
+  else if (a.nch <= 16)
+    launch_k((attn_merge_kernel<T, D, 16>), grid, block, 0, s, a, rows);
+  else
+    launch_k((attn_merge_kernel<T, D, 32>), grid, block, 0, s, a, rows);
   return hipGetLastError();
 }
 
