@@ -359,8 +359,8 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
 // One wave per (sequence, query head, block query): lane c reads chunk c's
 // (m, l) so the weights come from wave reductions (fixed butterfly order);
 // the partial outputs are then summed in chunk order, lane owning D/64
-// consecutive channels, with MB chunks' loads in flight (the smallest of 4,
-// 8, 16 and 32 that covers the grid's chunk count, so few chunks do not
+// consecutive channels, with MB chunks' loads in flight (the grid's chunk
+// count rounded up to a multiple of 4, at most 32, so few chunks do not
 // issue loads that repeat the last one).  The sums run in chunk order
 // whatever MB is.
 template <typename T, int D, int MB>
@@ -440,14 +440,16 @@ hipError_t attn_t(int B, const AttnArgs& a, hipStream_t s) {
   if (a.nch == 1) return hipSuccess;  // the partial kernel normalised
   const int rows = B * a.Hq * a.K;
   const dim3 grid((rows + 3) / 4), block(256);
-  if (a.nch <= 4)
-    launch_k((attn_merge_kernel<T, D, 4>), grid, block, 0, s, a, rows);
-  else if (a.nch <= 8)
-    launch_k((attn_merge_kernel<T, D, 8>), grid, block, 0, s, a, rows);
-  else if (a.nch <= 16)
-    launch_k((attn_merge_kernel<T, D, 16>), grid, block, 0, s, a, rows);
-  else
-    launch_k((attn_merge_kernel<T, D, 32>), grid, block, 0, s, a, rows);
+  switch (a.nch <= 32 ? (a.nch + 3) / 4 : 8) {
+    case 1: launch_k((attn_merge_kernel<T, D, 4>), grid, block, 0, s, a, rows); break;
+    case 2: launch_k((attn_merge_kernel<T, D, 8>), grid, block, 0, s, a, rows); break;
+    case 3: launch_k((attn_merge_kernel<T, D, 12>), grid, block, 0, s, a, rows); break;
+    case 4: launch_k((attn_merge_kernel<T, D, 16>), grid, block, 0, s, a, rows); break;
+    case 5: launch_k((attn_merge_kernel<T, D, 20>), grid, block, 0, s, a, rows); break;
+    case 6: launch_k((attn_merge_kernel<T, D, 24>), grid, block, 0, s, a, rows); break;
+    case 7: launch_k((attn_merge_kernel<T, D, 28>), grid, block, 0, s, a, rows); break;
+    default: launch_k((attn_merge_kernel<T, D, 32>), grid, block, 0, s, a, rows); break;
+  }
   return hipGetLastError();
 }
 
