@@ -29,7 +29,8 @@ LIB_SYMBOLS = ["dflash_create", "dflash_destroy", "dflash_kv_cache_bytes",
                "dflash_inject_kv", "dflash_draft_block",
                "dflash_verify_greedy", "dflash_verify_sampling",
                "dflash_set_kernel_timing", "dflash_get_kernel_timing",
-               "dflash_set_kv_pages", "dflash_kv_cache_paged_bytes"]
+               "dflash_set_kv_pages", "dflash_kv_cache_paged_bytes",
+               "dflash_draft_block_noalloc"]
 TIME_KIND = {"off": 0, "lmhead": 1, "attention": 2, "gemm": 3}
 HARNESS_SYMBOLS = ["dflash_harness_synth_target"]
 
@@ -93,6 +94,8 @@ def load_library():
     lib.dflash_draft_block.argtypes = [vp, vp, i32, vp, vp, vp, i32, vp, i32,
                                        i32, vp, vp, vp, vp]
     lib.dflash_draft_block.restype = ctypes.c_int
+    lib.dflash_draft_block_noalloc.argtypes = lib.dflash_draft_block.argtypes
+    lib.dflash_draft_block_noalloc.restype = ctypes.c_int
     lib.dflash_verify_greedy.argtypes = [vp, i32, i32, vp, vp, vp, vp]
     lib.dflash_verify_greedy.restype = ctypes.c_int
     lib.dflash_verify_sampling.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp,
@@ -266,13 +269,18 @@ class DFlash:
                     draft: Optional[torch.Tensor] = None,
                     conf: Optional[torch.Tensor] = None,
                     margin: Optional[torch.Tensor] = None,
-                    logits: Optional[torch.Tensor] = None, stream=None):
+                    logits: Optional[torch.Tensor] = None, stream=None,
+                    noalloc: bool = False):
+        """dflash_draft_block, or dflash_draft_block_noalloc (scratch in
+        the library's static device buffer) with noalloc=True."""
         B = ctx_len.shape[0]
         K = self.cfg.block_size
         dev = ctx_len.device
         if draft is None:
             draft = torch.empty(B, K - 1, dtype=torch.int32, device=dev)
-        _check(self.lib.dflash_draft_block(
+        fn = (self.lib.dflash_draft_block_noalloc if noalloc
+              else self.lib.dflash_draft_block)
+        _check(fn(
             self.ctx, _stream(stream), B, _ptr(anchor), _ptr(block_tokens),
             _ptr(ctx_len), int(max_ctx_len), _ptr(kv), num_passes,
             commit_per_pass, _ptr(draft), _ptr(conf), _ptr(margin),

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -63,6 +64,8 @@ struct dflash_ctx {
   bool bf16 = true;
   size_t esz = 2;
   int num_cu = 256;
+  int device = 0;
+  void* static_scratch = nullptr;  // this device's static scratch (noalloc)
   int P = 0;  // positions per cache slot (max_ctx + block_size)
 
   // read in place after create: the embedding table and the norm gains
@@ -237,18 +240,25 @@ bool gemm_is_tiled(const dflash_ctx* c, const GemmArgs& a) {
 #ifndef DFLASH_MAX_KSPLIT
 #define DFLASH_MAX_KSPLIT 4
 #endif
-int plan_ksplit(const dflash_ctx* c, const GemmArgs& a, int cfg) {
+// Where a split GEMM stores its copies: floats of room at p.
+struct SplitWs {
+  float* p = nullptr;
+  size_t floats = 0;
+};
+
+int plan_ksplit(const dflash_ctx* c, const GemmArgs& a, int cfg,
+                const SplitWs& ws) {
   if (!splittable(a)) return 1;
   const int blocks = tiled_blocks(cfg, a.M, a.N);
   int S = blocks > 0 ? c->num_cu / blocks : 1;
   S = std::min(S, DFLASH_MAX_KSPLIT);
   S = std::min(S, a.Kd / 32 / 8);
-  while (S > 1 && (size_t)S * a.M * a.N > c->splitk_floats) --S;
+  while (S > 1 && (size_t)S * a.M * a.N > ws.floats) --S;
   return std::max(S, 1);
 }
 
 dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
-                       int kind = DFLASH_TIME_GEMM) {
+                       const SplitWs& sw, int kind = DFLASH_TIME_GEMM) {
   a.err = c->err;
   const bool lm = a.ep == EP_TOP2;
   const bool tiled = gemm_is_tiled(c, a);
@@ -262,17 +272,17 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
   }
   if (tiled) {
     const int cfg = plan_tiled(a.M, a.N, splittable(a));
-    const int S = plan_ksplit(c, a, cfg);
+    const int S = plan_ksplit(c, a, cfg, sw);
     TimedLaunch tl(c, kind, s, S > 1 ? 2 : 1);
     if (S > 1) {
       // split copies into the workspace, then summed in order into the
       // output (plain store or residual add)
       GemmArgs b = a;
       b.ep = EP_STORE;
-      b.out_f32 = c->splitk;
+      b.out_f32 = sw.p;
       b.ldo = a.N;
       DF_HIP(launch_gemm_tiled(true, cfg, b, S, s));
-      DF_HIP(launch_splitk_reduce(a.M, a.N, S, c->splitk, a.out_f32, a.ldo,
+      DF_HIP(launch_splitk_reduce(a.M, a.N, S, sw.p, a.out_f32, a.ldo,
                                   a.ep == EP_RESID, s));
       return DFLASH_OK;
     }
@@ -314,6 +324,284 @@ void set_cache_geometry(GemmArgs& a, const dflash_ctx* c) {
   a.max_ctx = c->cfg.max_ctx;
   a.rope = c->rope;
   a.pages = c->pages;
+}
+
+// Per-call scratch of the drafting pass: activations, attention and LM-head
+// partials, the block state between passes and the split-contraction
+// copies.  The context's workspace (dflash_draft_block) or the static buffer
+// (dflash_draft_block_noalloc) provides it.
+struct DraftWs {
+  float* x = nullptr;       // residual rows [R][D]
+  void* h = nullptr;        // RMSNorm(x) * g, packed [R][D]
+  void* hf = nullptr;       // final-norm rows of still-masked positions, packed
+  void* qb = nullptr;       // q after RoPE [R][Hq*d]
+  void* ob = nullptr;       // attention output, packed [R][Hq*d]
+  void* act = nullptr;      // SwiGLU output, packed [R][I]
+  int32_t* tokens = nullptr;
+  int32_t* committed = nullptr;
+  int32_t* rowmap = nullptr;
+  Top2* lm_part = nullptr;   // [rows][V/16]
+  Top2* lm_part2 = nullptr;  // [rows][kMergeChunks]
+  float* attn_o = nullptr;   // [attn_rows][d]
+  float* attn_ml = nullptr;  // [attn_rows][2]
+  size_t attn_rows = 0;
+  SplitWs split;
+};
+
+// Static scratch of the allocation-free drafting call: one copy per GPU,
+// kept until the process ends.  Host code uses only the per-device address
+// resolved by hipGetSymbolAddress (static_scratch_ptr), never this name.
+constexpr size_t kStaticScratchBytes = DFLASH_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of `scratch` on device dev, resolved once with dev current (the
+// caller has made it current); nullptr on failure.
+void* static_scratch_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// Keys per attention workgroup and chunks per (sequence, kv head) for a
+// call with this batch and context bound.
+void attn_geometry(const dflash_ctx* c, int batch, int max_ctx_len,
+                   int* chunk, int* nch) {
+  const int K = c->cfg.block_size;
+  *chunk = attn_chunk(batch, c->cfg.num_kv_heads, max_ctx_len + K, c->num_cu);
+  *nch = (max_ctx_len + K + *chunk - 1) / *chunk;
+}
+
+// Scratch of one drafting call with `batch` sequences and context bound
+// max_ctx_len, carved from base (256-byte aligned pieces) when base is not
+// null.  Returns the bytes used.
+size_t static_layout(const dflash_ctx* c, int batch, int max_ctx_len,
+                     char* base, DraftWs* ws) {
+  const dflash_config& g = c->cfg;
+  const int K = g.block_size, D = g.hidden, d = g.head_dim;
+  const int R = batch * K, qd = g.num_q_heads * d;
+  const size_t esz = c->esz;
+  int chunk = 0, nch = 0;
+  attn_geometry(c, batch, max_ctx_len, &chunk, &nch);
+  const size_t attn_rows = (size_t)batch * g.num_q_heads * nch * K;
+  const size_t lm_rows = (size_t)batch * (K - 1);
+  const size_t split_floats = (size_t)DFLASH_MAX_KSPLIT * R * D;
+  struct Item { void** p; size_t bytes; };
+  const Item items[] = {
+      {(void**)&ws->x, (size_t)R * D * sizeof(float)},
+      {&ws->h, (size_t)R * D * esz},
+      {&ws->hf, (size_t)R * D * esz},
+      {&ws->qb, (size_t)R * qd * esz},
+      {&ws->ob, (size_t)R * qd * esz},
+      {&ws->act, (size_t)R * g.intermediate * esz},
+      {(void**)&ws->tokens, (size_t)R * sizeof(int32_t)},
+      {(void**)&ws->committed, (size_t)R * sizeof(int32_t)},
+      {(void**)&ws->rowmap, (size_t)R * sizeof(int32_t)},
+      {(void**)&ws->lm_part, lm_rows * (g.vocab / 16) * sizeof(Top2)},
+      {(void**)&ws->lm_part2, lm_rows * kMergeChunks * sizeof(Top2)},
+      {(void**)&ws->attn_o, attn_rows * d * sizeof(float)},
+      {(void**)&ws->attn_ml, attn_rows * 2 * sizeof(float)},
+      {(void**)&ws->split.p, split_floats * sizeof(float)},
+  };
+  size_t off = 0;
+  for (const Item& it : items) {
+    if (base) *it.p = base + off;
+    off += align_up(it.bytes, 256);
+  }
+  ws->attn_rows = attn_rows;
+  ws->split.floats = split_floats;
+  return off;
+}
+
+dflash_status check_draft_args(const dflash_ctx* ctx, int32_t batch,
+                               const int32_t* anchor,
+                               const int32_t* block_tokens,
+                               const int32_t* ctx_len, int32_t max_ctx_len,
+                               const void* kv_cache, int32_t num_passes,
+                               int32_t commit_per_pass,
+                               const int32_t* draft_tokens) {
+  const dflash_config& c = ctx->cfg;
+  const int K = c.block_size;
+  if (batch < 1) return fail(DFLASH_E_SHAPE, "batch %d < 1", batch);
+  if (batch > c.max_batch)
+    return fail(DFLASH_E_CAPACITY, "batch %d > max_batch %d", batch,
+                c.max_batch);
+  if (!anchor && !block_tokens)
+    return fail(DFLASH_E_INVALID, "need anchor or block_tokens");
+  if (!ctx_len || !kv_cache || !draft_tokens)
+    return fail(DFLASH_E_INVALID, "NULL argument");
+  if (max_ctx_len < 0 || max_ctx_len > c.max_ctx)
+    return fail(DFLASH_E_CAPACITY, "max_ctx_len %d outside [0, %d]",
+                max_ctx_len, c.max_ctx);
+  if (num_passes < 1) return fail(DFLASH_E_INVALID, "num_passes %d < 1", num_passes);
+  if (num_passes > 1 &&
+      (commit_per_pass < 1 || commit_per_pass * (num_passes - 1) >= K - 1))
+    return fail(DFLASH_E_INVALID,
+                "commit_per_pass %d invalid for %d passes (need 1 <= c and "
+                "c*(S-1) < K-1)",
+                commit_per_pass, num_passes);
+  if (!aligned16(kv_cache))
+    return fail(DFLASH_E_INVALID, "kv_cache not 16-byte aligned");
+  return DFLASH_OK;
+}
+
+// The launch sequence of one drafting call on the scratch ws.
+dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
+                         int32_t batch, const int32_t* anchor,
+                         const int32_t* block_tokens, const int32_t* ctx_len,
+                         int32_t max_ctx_len, void* kv_cache,
+                         int32_t num_passes, int32_t commit_per_pass,
+                         int32_t* draft_tokens, float* confidence,
+                         float* top2_margin, float* logits_debug) {
+  dflash_status st0 = check_draft_args(ctx, batch, anchor, block_tokens,
+                                       ctx_len, max_ctx_len, kv_cache,
+                                       num_passes, commit_per_pass,
+                                       draft_tokens);
+  if (st0 != DFLASH_OK) return st0;
+  const dflash_config& c = ctx->cfg;
+  const int K = c.block_size;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = ctx->bf16;
+  const int D = c.hidden, d = c.head_dim, Hq = c.num_q_heads,
+            Hkv = c.num_kv_heads, I = c.intermediate, V = c.vocab;
+  const int qd = Hq * d, kvd = Hkv * d;
+  const int R = batch * K;
+  const size_t plane_elems =
+      (size_t)kv_plane_rows(ctx->pages, c.max_batch, Hkv, ctx->P) * d;
+  const size_t layer_elems = 2 * plane_elems;
+  BlockState bs{ws.tokens, ws.committed, ws.rowmap, ctx->err};
+
+  AttnArgs at{};
+  at.pages = ctx->pages;
+  at.err = ctx->err;
+  at.q = ws.qb;
+  at.ctx_len = ctx_len;
+  at.max_len = max_ctx_len;
+  at.P = ctx->P;
+  at.Hq = Hq;
+  at.Hkv = Hkv;
+  at.K = K;
+  attn_geometry(ctx, batch, max_ctx_len, &at.chunk, &at.nch);
+  at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  at.part_o = ws.attn_o;
+  at.part_ml = ws.attn_ml;
+  at.o = ws.ob;
+  const size_t need = (size_t)batch * Hq * at.nch * K;
+  if (need > ws.attn_rows)
+    return fail(DFLASH_E_CAPACITY, "attention workspace too small");
+
+  for (int pass = 0; pass < num_passes; ++pass) {
+    const int n_cap = (K - 1) - pass * commit_per_pass;
+    const bool last = pass == num_passes - 1;
+    // up to 512 rows the embedding kernel also writes the first layer's
+    // normalised input (one row per workgroup is the faster form there)
+    const bool fuse_norm = R <= 512;
+    DF_HIP(launch_embed(bf, batch, K, D, V, c.mask_token_id, pass, n_cap,
+                        anchor, block_tokens, bs, ctx->embed, ws.x,
+                        draft_tokens, fuse_norm ? ctx->attn_norm[0] : nullptr,
+                        c.rms_eps, ws.h, s));
+    for (int l = 0; l < c.num_layers; ++l) {
+      char* kvl = static_cast<char*>(kv_cache) + l * layer_elems * ctx->esz;
+      // q, k, v of RMSNorm(x); RoPE; q -> q buffer, block k, v -> cache
+      // positions L_b + i
+      if (l > 0 || !fuse_norm)
+        DF_HIP(launch_rmsnorm(bf, R, D, ws.x, nullptr, ctx->attn_norm[l],
+                              c.rms_eps, ws.h, s));
+      GemmArgs a = packed_args(ws.h, ctx->pk_qkv[l], R, qd + 2 * kvd, D);
+      set_pairs(a, d, d / 2);
+      set_cache_geometry(a, ctx);
+      a.ep = EP_QKV;
+      a.out_t = ws.qb;
+      a.kv = kvl;
+      a.ctx_len = ctx_len;
+      a.max_len = max_ctx_len;
+      a.K = K;
+      dflash_status st = run_gemm(ctx, a, s, ws.split);
+      if (st != DFLASH_OK) return st;
+      at.kc = kvl;
+      at.vc = kvl + plane_elems * ctx->esz;
+      {
+        TimedLaunch tl(ctx, DFLASH_TIME_ATTENTION, s, at.nch > 1 ? 2 : 1);
+        DF_HIP(launch_attention(bf, d, batch, at, s));
+      }
+      // x += o . Wo^T
+      GemmArgs o = packed_args(ws.ob, ctx->pk_o[l], R, D, qd);
+      o.ep = EP_RESID;
+      o.out_f32 = ws.x;
+      o.ldo = D;
+      st = run_gemm(ctx, o, s, ws.split);
+      if (st != DFLASH_OK) return st;
+      // act = silu(h Wg^T) * (h Wu^T), h = RMSNorm(x)
+      DF_HIP(launch_rmsnorm(bf, R, D, ws.x, nullptr, ctx->mlp_norm[l],
+                            c.rms_eps, ws.h, s));
+      GemmArgs gu = packed_args(ws.h, ctx->pk_gu[l], R, 2 * I, D);
+      set_pairs(gu, 2 * I, I);
+      gu.ep = EP_SWIGLU;
+      gu.out_t = ws.act;
+      st = run_gemm(ctx, gu, s, ws.split);
+      if (st != DFLASH_OK) return st;
+      // x += act . Wd^T
+      GemmArgs dn = packed_args(ws.act, ctx->pk_down[l], R, D, I);
+      dn.ep = EP_RESID;
+      dn.out_f32 = ws.x;
+      dn.ldo = D;
+      st = run_gemm(ctx, dn, s, ws.split);
+      if (st != DFLASH_OK) return st;
+    }
+    // final norm of the still-masked rows (compacted), then the LM head with
+    // the fused argmax / top-2 / log-sum-exp per 16-column vocabulary tile
+    const int Mh = batch * n_cap;
+    DF_HIP(launch_rmsnorm(bf, Mh, D, ws.x, ws.rowmap, ctx->final_norm,
+                          c.rms_eps, ws.hf, s));
+    GemmArgs hd = packed_args(ws.hf, ctx->pk_lm, Mh, V, D);
+    hd.ep = EP_TOP2;
+    hd.top2 = ws.lm_part;
+    hd.rowmap = ws.rowmap;
+    hd.K = K;
+    hd.logits = logits_debug
+                    ? logits_debug + (size_t)pass * batch * (K - 1) * V
+                    : nullptr;
+    hd.logits_ld = V;
+    hd.err = ctx->err;
+    const int parts = lm_head_parts(bf, Mh, V, D, ctx->num_cu);
+    // records per row: one per workgroup of the persistent head, one per
+    // column block of the tiled head, one per 16-column tile of the
+    // streaming form; the commit kernel merges up to kCommitMaxRecords
+    // itself
+    const Top2* recs = ws.lm_part;
+    int nrec = 0;
+    if (parts > 0) {
+      TimedLaunch tl(ctx, DFLASH_TIME_LMHEAD, s);
+      DF_HIP(launch_lm_head(bf, parts, hd, s));
+      nrec = parts;
+    } else {
+      dflash_status st = run_gemm(ctx, hd, s, ws.split, DFLASH_TIME_LMHEAD);
+      if (st != DFLASH_OK) return st;
+      nrec = gemm_is_tiled(ctx, hd) ? tiled_top2_records(plan_tiled(Mh, V), V)
+                                    : V / 16;
+      if (nrec > kCommitMaxRecords) {
+        // many records per row: merge them to kMergeChunks per row first,
+        // with a workgroup per (row, chunk), rather than serially per wave
+        DF_HIP(launch_lm_merge(Mh, nrec, ws.lm_part, ws.lm_part2, s));
+        recs = ws.lm_part2;
+        nrec = kMergeChunks;
+      }
+    }
+    DF_HIP(launch_commit(batch, K, n_cap, commit_per_pass, last, recs, nrec,
+                         bs, draft_tokens, confidence, top2_margin, s));
+  }
+  return DFLASH_OK;
 }
 
 }  // namespace
@@ -418,6 +706,15 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
                             dev) != hipSuccess) {
     delete x;
     return fail(DFLASH_E_DEVICE, "no HIP device available");
+  }
+  x->device = dev;
+  // the allocation-free drafting call's scratch on this device (resolved
+  // once per device, with the device current)
+  x->static_scratch = static_scratch_ptr(dev);
+  if (!x->static_scratch) {
+    delete x;
+    return fail(DFLASH_E_DEVICE, "hipGetSymbolAddress of the static scratch "
+                "failed on device %d", dev);
   }
   x->embed = w->embed;
   x->hidden_norm = w->hidden_norm;
@@ -672,7 +969,8 @@ dflash_status dflash_inject_kv(dflash_ctx* ctx, void* stream,
   a.ep = EP_STORE;
   a.out_f32 = ctx->u;
   a.ldo = D;
-  dflash_status st = run_gemm(ctx, a, s);
+  const SplitWs sw{ctx->splitk, ctx->splitk_floats};
+  dflash_status st = run_gemm(ctx, a, s, sw);
   if (st != DFLASH_OK) return st;
   // H_cond = RMSNorm(u) * g
   DF_HIP(launch_rmsnorm(ctx->bf16, T, D, ctx->u, nullptr, ctx->hidden_norm,
@@ -686,7 +984,7 @@ dflash_status dflash_inject_kv(dflash_ctx* ctx, void* stream,
   b.kv = kv_cache;
   b.row_seq = row_seq;
   b.row_pos = row_pos;
-  return run_gemm(ctx, b, s);
+  return run_gemm(ctx, b, s, sw);
 }
 
 dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
@@ -699,161 +997,55 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
                                  float* top2_margin, float* logits_debug) {
   g_last_error.clear();
   if (!ctx) return fail(DFLASH_E_INVALID, "ctx is NULL");
-  const dflash_config& c = ctx->cfg;
-  const int K = c.block_size;
-  if (batch < 1) return fail(DFLASH_E_SHAPE, "batch %d < 1", batch);
-  if (batch > c.max_batch)
-    return fail(DFLASH_E_CAPACITY, "batch %d > max_batch %d", batch,
-                c.max_batch);
-  if (!anchor && !block_tokens)
-    return fail(DFLASH_E_INVALID, "need anchor or block_tokens");
-  if (!ctx_len || !kv_cache || !draft_tokens)
-    return fail(DFLASH_E_INVALID, "NULL argument");
-  if (max_ctx_len < 0 || max_ctx_len > c.max_ctx)
-    return fail(DFLASH_E_CAPACITY, "max_ctx_len %d outside [0, %d]",
-                max_ctx_len, c.max_ctx);
-  if (num_passes < 1) return fail(DFLASH_E_INVALID, "num_passes %d < 1", num_passes);
-  if (num_passes > 1 &&
-      (commit_per_pass < 1 || commit_per_pass * (num_passes - 1) >= K - 1))
-    return fail(DFLASH_E_INVALID,
-                "commit_per_pass %d invalid for %d passes (need 1 <= c and "
-                "c*(S-1) < K-1)",
-                commit_per_pass, num_passes);
-  if (!aligned16(kv_cache))
-    return fail(DFLASH_E_INVALID, "kv_cache not 16-byte aligned");
+  DraftWs ws;
+  ws.x = ctx->x;
+  ws.h = ctx->h;
+  ws.hf = ctx->hf;
+  ws.qb = ctx->qb;
+  ws.ob = ctx->ob;
+  ws.act = ctx->act;
+  ws.tokens = ctx->tokens;
+  ws.committed = ctx->committed;
+  ws.rowmap = ctx->rowmap;
+  ws.lm_part = ctx->lm_part;
+  ws.lm_part2 = ctx->lm_part2;
+  ws.attn_o = ctx->attn_o;
+  ws.attn_ml = ctx->attn_ml;
+  ws.attn_rows = ctx->attn_floats;
+  ws.split = SplitWs{ctx->splitk, ctx->splitk_floats};
+  return draft_impl(ctx, ws, stream, batch, anchor, block_tokens, ctx_len,
+                    max_ctx_len, kv_cache, num_passes, commit_per_pass,
+                    draft_tokens, confidence, top2_margin, logits_debug);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf = ctx->bf16;
-  const int D = c.hidden, d = c.head_dim, Hq = c.num_q_heads,
-            Hkv = c.num_kv_heads, I = c.intermediate, V = c.vocab;
-  const int qd = Hq * d, kvd = Hkv * d;
-  const int R = batch * K;
-  const size_t plane_elems =
-      (size_t)kv_plane_rows(ctx->pages, c.max_batch, Hkv, ctx->P) * d;
-  const size_t layer_elems = 2 * plane_elems;
-  BlockState bs{ctx->tokens, ctx->committed, ctx->rowmap, ctx->err};
-
-  AttnArgs at{};
-  at.pages = ctx->pages;
-  at.err = ctx->err;
-  at.q = ctx->qb;
-  at.ctx_len = ctx_len;
-  at.max_len = max_ctx_len;
-  at.P = ctx->P;
-  at.Hq = Hq;
-  at.Hkv = Hkv;
-  at.K = K;
-  at.chunk = attn_chunk(batch, Hkv, max_ctx_len + K, ctx->num_cu);
-  at.nch = (max_ctx_len + K + at.chunk - 1) / at.chunk;
-  at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
-  at.part_o = ctx->attn_o;
-  at.part_ml = ctx->attn_ml;
-  at.o = ctx->ob;
-  const size_t need = (size_t)batch * Hq * at.nch * K;
-  if (need > ctx->attn_floats)
-    return fail(DFLASH_E_CAPACITY, "attention workspace too small");
-
-  for (int pass = 0; pass < num_passes; ++pass) {
-    const int n_cap = (K - 1) - pass * commit_per_pass;
-    const bool last = pass == num_passes - 1;
-    // up to 512 rows the embedding kernel also writes the first layer's
-    // normalised input (one row per workgroup is the faster form there)
-    const bool fuse_norm = R <= 512;
-    DF_HIP(launch_embed(bf, batch, K, D, V, c.mask_token_id, pass, n_cap,
-                        anchor, block_tokens, bs, ctx->embed, ctx->x,
-                        draft_tokens, fuse_norm ? ctx->attn_norm[0] : nullptr,
-                        c.rms_eps, ctx->h, s));
-    for (int l = 0; l < c.num_layers; ++l) {
-      char* kvl = static_cast<char*>(kv_cache) + l * layer_elems * ctx->esz;
-      // q, k, v of RMSNorm(x); RoPE; q -> q buffer, block k, v -> cache
-      // positions L_b + i
-      if (l > 0 || !fuse_norm)
-        DF_HIP(launch_rmsnorm(bf, R, D, ctx->x, nullptr, ctx->attn_norm[l],
-                              c.rms_eps, ctx->h, s));
-      GemmArgs a = packed_args(ctx->h, ctx->pk_qkv[l], R, qd + 2 * kvd, D);
-      set_pairs(a, d, d / 2);
-      set_cache_geometry(a, ctx);
-      a.ep = EP_QKV;
-      a.out_t = ctx->qb;
-      a.kv = kvl;
-      a.ctx_len = ctx_len;
-      a.max_len = max_ctx_len;
-      a.K = K;
-      dflash_status st = run_gemm(ctx, a, s);
-      if (st != DFLASH_OK) return st;
-      at.kc = kvl;
-      at.vc = kvl + plane_elems * ctx->esz;
-      {
-        TimedLaunch tl(ctx, DFLASH_TIME_ATTENTION, s, at.nch > 1 ? 2 : 1);
-        DF_HIP(launch_attention(bf, d, batch, at, s));
-      }
-      // x += o . Wo^T
-      GemmArgs o = packed_args(ctx->ob, ctx->pk_o[l], R, D, qd);
-      o.ep = EP_RESID;
-      o.out_f32 = ctx->x;
-      o.ldo = D;
-      st = run_gemm(ctx, o, s);
-      if (st != DFLASH_OK) return st;
-      // act = silu(h Wg^T) * (h Wu^T), h = RMSNorm(x)
-      DF_HIP(launch_rmsnorm(bf, R, D, ctx->x, nullptr, ctx->mlp_norm[l],
-                            c.rms_eps, ctx->h, s));
-      GemmArgs gu = packed_args(ctx->h, ctx->pk_gu[l], R, 2 * I, D);
-      set_pairs(gu, 2 * I, I);
-      gu.ep = EP_SWIGLU;
-      gu.out_t = ctx->act;
-      st = run_gemm(ctx, gu, s);
-      if (st != DFLASH_OK) return st;
-      // x += act . Wd^T
-      GemmArgs dn = packed_args(ctx->act, ctx->pk_down[l], R, D, I);
-      dn.ep = EP_RESID;
-      dn.out_f32 = ctx->x;
-      dn.ldo = D;
-      st = run_gemm(ctx, dn, s);
-      if (st != DFLASH_OK) return st;
-    }
-    // final norm of the still-masked rows (compacted), then the LM head with
-    // the fused argmax / top-2 / log-sum-exp per 16-column vocabulary tile
-    const int Mh = batch * n_cap;
-    DF_HIP(launch_rmsnorm(bf, Mh, D, ctx->x, ctx->rowmap, ctx->final_norm,
-                          c.rms_eps, ctx->hf, s));
-    GemmArgs hd = packed_args(ctx->hf, ctx->pk_lm, Mh, V, D);
-    hd.ep = EP_TOP2;
-    hd.top2 = ctx->lm_part;
-    hd.rowmap = ctx->rowmap;
-    hd.K = K;
-    hd.logits = logits_debug
-                    ? logits_debug + (size_t)pass * batch * (K - 1) * V
-                    : nullptr;
-    hd.logits_ld = V;
-    hd.err = ctx->err;
-    const int parts = lm_head_parts(bf, Mh, V, D, ctx->num_cu);
-    // records per row: one per workgroup of the persistent head, one per
-    // column block of the tiled head, one per 16-column tile of the
-    // streaming form; the commit kernel merges up to kCommitMaxRecords
-    // itself
-    const Top2* recs = ctx->lm_part;
-    int nrec = 0;
-    if (parts > 0) {
-      TimedLaunch tl(ctx, DFLASH_TIME_LMHEAD, s);
-      DF_HIP(launch_lm_head(bf, parts, hd, s));
-      nrec = parts;
-    } else {
-      dflash_status st = run_gemm(ctx, hd, s, DFLASH_TIME_LMHEAD);
-      if (st != DFLASH_OK) return st;
-      nrec = gemm_is_tiled(ctx, hd) ? tiled_top2_records(plan_tiled(Mh, V), V)
-                                    : V / 16;
-      if (nrec > kCommitMaxRecords) {
-        // many records per row: merge them to kMergeChunks per row first,
-        // with a workgroup per (row, chunk), rather than serially per wave
-        DF_HIP(launch_lm_merge(Mh, nrec, ctx->lm_part, ctx->lm_part2, s));
-        recs = ctx->lm_part2;
-        nrec = kMergeChunks;
-      }
-    }
-    DF_HIP(launch_commit(batch, K, n_cap, commit_per_pass, last, recs, nrec,
-                         bs, draft_tokens, confidence, top2_margin, s));
-  }
-  return DFLASH_OK;
+dflash_status dflash_draft_block_noalloc(
+    dflash_ctx* ctx, void* stream, int32_t batch, const int32_t* anchor,
+    const int32_t* block_tokens, const int32_t* ctx_len, int32_t max_ctx_len,
+    void* kv_cache, int32_t num_passes, int32_t commit_per_pass,
+    int32_t* draft_tokens, float* confidence, float* top2_margin,
+    float* logits_debug) {
+  g_last_error.clear();
+  if (!ctx) return fail(DFLASH_E_INVALID, "ctx is NULL");
+  dflash_status st = check_draft_args(ctx, batch, anchor, block_tokens,
+                                      ctx_len, max_ctx_len, kv_cache,
+                                      num_passes, commit_per_pass,
+                                      draft_tokens);
+  if (st != DFLASH_OK) return st;
+  char* base = static_cast<char*>(ctx->static_scratch);
+  if (!base)
+    return fail(DFLASH_E_DEVICE, "static scratch of device %d not resolved",
+                ctx->device);
+  DraftWs ws;
+  const size_t need = static_layout(ctx, batch, max_ctx_len, nullptr, &ws);
+  if (need > kStaticScratchBytes)
+    return fail(DFLASH_E_CAPACITY,
+                "batch %d with max_ctx_len %d needs %zu bytes of scratch, "
+                "more than the %zu of the static buffer",
+                batch, max_ctx_len, need, (size_t)kStaticScratchBytes);
+  static_layout(ctx, batch, max_ctx_len, base, &ws);
+  return draft_impl(ctx, ws, stream, batch, anchor, block_tokens, ctx_len,
+                    max_ctx_len, kv_cache, num_passes, commit_per_pass,
+                    draft_tokens, confidence, top2_margin, logits_debug);
 }
 
 dflash_status dflash_verify_greedy(void* stream, int32_t batch,

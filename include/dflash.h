@@ -281,6 +281,41 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t batch,
                                  int32_t* draft_tokens, float* confidence,
                                  float* top2_margin, float* logits_debug);
 
+/* Allocation-free variant of dflash_draft_block, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): same arguments, same launch sequence,
+ * same kernels and results, but the per-call scratch (activations,
+ * attention and LM-head partials, the block state between passes, split-
+ * contraction copies) comes from a static device buffer of
+ * DFLASH_NOALLOC_SCRATCH_BYTES per GPU instead of the context's workspace.
+ * The call allocates and frees nothing.
+ *
+ * The buffer is part of the library's code object: each GPU the library
+ * runs on holds its own copy until the process ends.  Its device address is
+ * resolved at dflash_create (with the context's device current).  Every call
+ * on one GPU shares that GPU's buffer, and the buffer keeps the last call's
+ * contents (nothing in it needs to start at zero), so calls that overlap on
+ * one GPU -- on different streams, or through different contexts -- race:
+ * order them.
+ *
+ * Scratch needed (256-byte aligned pieces, R = batch * K rows):
+ *   R * D * 4 + 2 * R * D * esz + 2 * R * Hq*d * esz + R * I * esz
+ *   + 3 * R * 4 + batch*(K-1) * (vocab/16 + 16) * 16
+ *   + batch * Hq * nch * K * (d + 2) * 4 + 4 * R * D * 4
+ * where esz is the dtype's size and nch the attention chunks per (sequence,
+ * kv head) for this max_ctx_len; a call needing more than the buffer
+ * returns DFLASH_E_CAPACITY and launches nothing.  With Qwen3-8B shapes
+ * (D 4096, 32/8 heads of 128, I 12288, vocab 151936) a batch-1 call needs
+ * about 9 MiB at a context of 2048, 19 MiB at 32768, and batch 4 at 32768
+ * about 34 MiB. */
+#define DFLASH_NOALLOC_SCRATCH_BYTES (64u << 20)
+dflash_status dflash_draft_block_noalloc(
+    dflash_ctx* ctx, void* stream, int32_t batch, const int32_t* anchor,
+    const int32_t* block_tokens, const int32_t* ctx_len, int32_t max_ctx_len,
+    void* kv_cache, int32_t num_passes, int32_t commit_per_pass,
+    int32_t* draft_tokens, float* confidence, float* top2_margin,
+    float* logits_debug);
+
 /* Greedy verification.
  *
  * Passage: "DFlash Guide", section "The Cost Breakdown of Speculative Rounds"

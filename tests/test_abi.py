@@ -166,6 +166,9 @@ def test_calls_with_null_context_are_rejected():
     st = L.dflash_draft_block(None, None, 1, p, None, p, 10, p, 1, 0, p,
                               None, None, None)
     assert binding.STATUS[st] == "DFLASH_E_INVALID"
+    st = L.dflash_draft_block_noalloc(None, None, 1, p, None, p, 10, p, 1, 0,
+                                      p, None, None, None)
+    assert binding.STATUS[st] == "DFLASH_E_INVALID"
     assert binding.STATUS[L.dflash_set_kernel_timing(None, 1)] == \
         "DFLASH_E_INVALID"
     assert binding.STATUS[L.dflash_check_device_errors(None, None, None)] == \
