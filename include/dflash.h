@@ -257,7 +257,12 @@ dflash_status dflash_inject_kv(dflash_ctx* ctx, void* stream,
  * ctx_len:        [batch] int32 L_b in [0, max_ctx_len] (values outside
  *                 are clamped and set DFLASH_DEVERR_CTX_LEN).
  * max_ctx_len:    host upper bound on every ctx_len[b] (sizes the attention
- *                 grid), 0 <= max_ctx_len <= max_ctx.
+ *                 grid), 0 <= max_ctx_len <= max_ctx.  A step captured in a
+ *                 HIP graph keeps the grid of its capture: capture it with a
+ *                 bound that covers every later ctx_len (e.g. max_ctx) when
+ *                 the contexts grow between replays.  Results depend on the
+ *                 bound only through float rounding (it sets how the keys
+ *                 are split into chunks).
  * kv_cache:       as for dflash_inject_kv; positions [L_b, L_b+K) of each
  *                 slot are overwritten with the block's own K/V.
  * num_passes:     S >= 1; commit_per_pass c >= 1 when S > 1, with

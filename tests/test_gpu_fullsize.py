@@ -16,15 +16,11 @@ data for both sides (injecting 32k rows through the float64 oracle would take
 far too long); the new rows are injected by both sides from the same seeded
 target hidden states.
 
-Tolerances: the stated bounds (logits max-abs 2e-2, token ids exact where the
-top-2 margin exceeds 1e-2) apply as they are to the one-layer drafter.  Every
-layer adds eight bf16 rounding points whose rare disagreements between any
-two correct implementations are amplified by the following normalisation and
-MLP; an exact float32 evaluation of the same computation (tests/
-precision_floor.py) already differs from the float64 oracle by up to 1.8e-2,
-3.4e-2 and 4.5e-2 in the logits of 1, 3 and 5-layer drafters.  So for deeper
-drafters the logit, log-confidence and margin bounds and the token-margin
-threshold are scaled by the number of draft layers.
+Tolerances: the stated bounds (logits max-abs 2e-2, token ids exact where
+the top-2 margin exceeds 1e-2), or for the deeper drafters 1.25 times the
+largest distance from the oracle of an ensemble of float32 evaluations of
+the same inputs, where a token differing at a margin above 1e-2 must be
+differed on by one of those evaluations too (tests/gpu_common.py says why).
 """
 import gc
 
@@ -35,8 +31,9 @@ import torch
 import workloads as W
 from oracle import (OracleModel, draft_batch, inject_rows, synthetic_target,
                     verify_greedy as oracle_verify)
-from tests.gpu_common import (DEV, logconf_tol, logit_tol, margin_min,
-                              check_bf16_close, compare_draft, f64, say)
+from tests.gpu_common import (DEV, Float32Floor, check_bf16_close,
+                              check_single_pass, check_two_pass, f64,
+                              kv_flip_stats, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -147,59 +144,107 @@ def test_full_size_step_parity(name):
         per_seq.append(ctx_kv)
     ref = draft_batch(model, per_seq, lens, anchors=anchors, num_passes=S,
                       commit_per_pass=c, keep_logits=True, seqs=seqs)
-    tol, mmin = logit_tol(wl), margin_min(wl)
+    # float32 evaluations of the same step: the same prefix as data, their
+    # own injection of the same new rows
+    fl = Float32Floor(wl, w_cpu, [{l: prefix[(b, l)] for l in
+                                   range(wl.num_layers)} for b in seqs],
+                      [lens[b] for b in seqs],
+                      inject=[([h[b * n_new:(b + 1) * n_new] for h in Hc],
+                               np.arange(int(lens[b]) - n_new, int(lens[b])))
+                              for b in seqs])
+    for j, b in enumerate(seqs):
+        L = int(lens[b])
+        for l in range(wl.num_layers):
+            gk = f64(kv[l, 0, b, :, L - n_new:L]).transpose(1, 0, 2)
+            new_or = per_seq[j][l][0][L - n_new:]
+            members = [fl.injected(m, j)[l][0] for m in range(fl.members)]
+            kv_flip_stats(gk, new_or, members, f"K l{l} b{b}",
+                          quiet=l > 0 or j > 0)
     if S == 1:
-        g["logits"] = g["logits_all"][0]
-        comp, excl, dl = compare_draft(wl, g, ref, tol=tol,
-                                       margin_min=mmin)
-        say(f"  tokens compared {comp}, excluded {excl}, max |dlogit| {dl:.2e}"
-            f" (bound {tol:.0e})")
-        assert comp > 0
-        lc = np.abs(np.log(g["conf"]) -
-                    np.log(np.stack([o["conf"][1:] for o in ref])))
-        assert lc.max() <= logconf_tol(wl)
-        mg = np.stack([o["margin"][1:] for o in ref])
-        assert np.abs(g["margin"] - mg).max() <= 2 * tol
+        check_single_pass(wl, name, g, ref, fl, [anchors[b] for b in seqs])
     else:
-        teacher = np.full((B, wl.block_size), wl.mask_id, dtype=np.int32)
-        teacher[:, 0] = anchors
-        clear = 0
-        for j, (b, o) in enumerate(zip(seqs, ref)):
-            z1 = g["logits_all"][0][j]
-            assert np.abs(z1 - o["logits"][0]).max() <= tol
-            c1 = o["pass_conf"][0][1:]
-            order = sorted(range(15), key=lambda i: (-c1[i], i))
-            gap = np.log(c1[order[c - 1]]) - np.log(c1[order[c]])
-            oracle_set = set(np.nonzero(o["pass"] == 0)[0].tolist())
-            gpu_set = set(range(1, 16)) - set(
-                np.nonzero(~np.isnan(g["logits_all"][1][j][:, 0]))[0] + 1)
-            if gap > mmin:
-                clear += 1
-                assert gpu_set == oracle_set, f"seq {b}: commit sets differ"
-                same = True
-                for i in oracle_set:
-                    tok_ok = g["draft"][j, i - 1] == o["tokens"][i]
-                    if o["pass_margin"][0][i] > mmin:
-                        assert tok_ok, f"seq {b} pos {i}: committed token differs"
-                    same &= bool(tok_ok)
-                if same:  # else a near-tie went the other way: pass 2 differs
-                    rows2 = o["masked_rows"][1]
-                    assert np.abs(g["logits_all"][1][j][rows2 - 1] -
-                                  o["logits"][1]).max() <= tol
-            for i in oracle_set:
-                teacher[b, i] = o["tokens"][i]
-        say(f"  pass-1 commit sets with a clear cut: {clear} of {len(seqs)}")
-        # second pass teacher-forced with the oracle's pass-1 commits (other
-        # sequences draft a fresh block in the same launch)
-        tf = gpu_draft(ctx, wl, lens, kv, seqs, block=teacher, S=1)
-        for j, (b, o) in enumerate(zip(seqs, ref)):
-            rows2 = o["masked_rows"][1]
-            assert np.abs(tf["logits_all"][0][j][rows2 - 1] -
-                          o["logits"][1]).max() <= tol
-            for i in rows2:
-                if o["pass_margin"][1][int(i)] > mmin:
-                    assert tf["draft"][j, i - 1] == o["pass_token"][1][int(i)]
+        check_two_pass(wl, name,
+                       lambda blk: gpu_draft(ctx, wl, lens, kv, seqs,
+                                             block=blk),
+                       g, ref, fl, anchors, c, seqs=seqs)
     ctx.close()
     del kv, w_dev, H
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+DEEP = [n for n in FULL if W.WORKLOADS[n].num_layers > 1]
+
+
+@pytest.mark.parametrize("name", DEEP)
+def test_full_size_each_layer_alone(name):
+    """Each layer of a deeper drafter run alone as a one-layer drafter (its
+    own attention and MLP weights; the shared embedding, fc, final norm and
+    LM head; that layer's context K/V) at full size, in the benchmark's
+    launch configuration: inject the step's new rows, one pass, against the
+    oracle on the sampled sequences.  A defect in any one layer shows here
+    at one-layer tolerances, without the other layers' amplification."""
+    wl = W.WORKLOADS[name]
+    wl1 = wl.replace(num_layers=1, num_passes=1, commit_per_pass=0)
+    B, n_new = wl.batch, wl.new_rows
+    lens = W.gen_ctx_lens(wl)
+    seqs = sample_seqs(lens)
+    say(f"[full size, each layer alone] {name}: oracle on {seqs}")
+    w_dev = W.gen_weights(wl, device=DEV)
+    H = W.gen_hiddens(wl, B * n_new, device=DEV, index=0, tag="step")
+    Hc = [h.cpu() for h in H]
+    row_seq = torch.arange(B, dtype=torch.int32,
+                           device=DEV).repeat_interleave(n_new)
+    row_pos = torch.from_numpy(np.concatenate(
+        [np.arange(int(L) - n_new, int(L)) for L in lens]).astype(
+            np.int32)).to(DEV)
+    anchors = W.gen_anchors(wl)
+    shared = {k: v.cpu() for k, v in w_dev.items() if not isinstance(v, list)}
+    worst = 0.0
+    for l in range(wl.num_layers):
+        w1 = {k: ([v[l]] if isinstance(v, list) else v)
+              for k, v in w_dev.items()}
+        ctx = dfl.DFlash(wl1, w1, max_inject_rows=max(2048, B * n_new))
+        kv = ctx.new_kv_cache()
+        prefix = {}
+        for b, L in enumerate(lens):
+            n_pre = int(L) - n_new
+            k = W.gen_kv_prefix(wl, l, "k", b, n_pre, device=DEV)
+            v = W.gen_kv_prefix(wl, l, "v", b, n_pre, device=DEV)
+            kv[0, 0, b, :, :n_pre] = k
+            kv[0, 1, b, :, :n_pre] = v
+            if b in seqs:
+                prefix[b] = (f64(k).transpose(1, 0, 2),
+                             f64(v).transpose(1, 0, 2))
+        ctx.inject_kv(H, row_seq, row_pos, kv)
+        g = gpu_draft(ctx, wl1, lens, kv, seqs, anchors=anchors)
+        w_cpu = dict(shared)
+        for k, v in w_dev.items():
+            if isinstance(v, list):
+                w_cpu[k] = [v[l].cpu()]
+        model = OracleModel(wl1, w_cpu)
+        per_seq, inj = [], []
+        for b in seqs:
+            L = int(lens[b])
+            rows = [h[b * n_new:(b + 1) * n_new] for h in Hc]
+            pos = np.arange(L - n_new, L)
+            new = inject_rows(model, rows, pos)
+            per_seq.append({0: (np.concatenate([prefix[b][0], new[0][0]]),
+                                np.concatenate([prefix[b][1], new[0][1]]))})
+            inj.append((rows, pos))
+        ref = draft_batch(model, per_seq, lens, anchors=anchors,
+                          keep_logits=True, seqs=seqs)
+        fl = Float32Floor(wl1, w_cpu, [{0: prefix[b]} for b in seqs],
+                          [lens[b] for b in seqs], inject=inj)
+        st = check_single_pass(wl1, f"{name} layer {l} alone", g, ref, fl,
+                               [anchors[b] for b in seqs])
+        worst = max(worst, st["max_dl"])
+        ctx.close()
+        del kv, fl, model
+        gc.collect()
+        torch.cuda.empty_cache()
+    say(f"  {name}: worst single layer max |dlogit| {worst:.2e} (stated "
+        f"bound 2e-2)")
+    del w_dev, H
     gc.collect()
     torch.cuda.empty_cache()

@@ -14,7 +14,9 @@ import pytest
 import torch
 
 import workloads as W
-from tests.gpu_common import DEV, say, to_dev
+from oracle import OracleModel, draft_batch, inject_rows
+from tests.gpu_common import (DEV, Float32Floor, check_bf16_close,
+                              check_single_pass, f64, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -158,12 +160,16 @@ def test_paged_step_in_a_hip_graph_follows_table_updates():
     """Serving pattern: the step is captured once with a paged cache; the
     block table is device memory read at run time, so moving a sequence's
     pages (copy the page contents, rewrite the table in place) between
-    replays must give the same results."""
+    replays must give the same results.  Each replay is also checked
+    against the oracle directly: the injected K/V of every sequence
+    gathered through the moved table, and the drafted logits, tokens,
+    confidences and margins."""
     wl = W.small_bf16(batch=8, ctx_min=20, ctx_max=150, name="small-bf16-b8",
                       seed=78)
     ps = 64
     say("[paged graph] small-bf16-b8, pages of 64")
-    ctx = dfl.DFlash(wl, to_dev(W.gen_weights(wl)))
+    w_cpu = W.gen_weights(wl)
+    ctx = dfl.DFlash(wl, to_dev(w_cpu))
     K, B, n_new = wl.block_size, wl.batch, wl.new_rows
     cfg = ctx.cfg
     lens = W.gen_ctx_lens(wl)
@@ -190,11 +196,14 @@ def test_paged_step_in_a_hip_graph_follows_table_updates():
     anchor = torch.from_numpy(W.gen_anchors(wl)).to(DEV)
     draft = torch.empty(B, K - 1, dtype=torch.int32, device=DEV)
     conf = torch.empty(B, K - 1, dtype=torch.float32, device=DEV)
+    margin = torch.empty(B, K - 1, dtype=torch.float32, device=DEV)
+    logits = torch.empty(1, B, K - 1, wl.vocab, dtype=torch.float32,
+                         device=DEV)
 
     def step():
         ctx.inject_kv(H, row_seq, row_pos, kv)
         ctx.draft_block(ctx_len, kv, int(lens.max()), anchor=anchor,
-                        draft=draft, conf=conf)
+                        draft=draft, conf=conf, margin=margin, logits=logits)
 
     step()
     torch.cuda.synchronize()
@@ -210,6 +219,46 @@ def test_paged_step_in_a_hip_graph_follows_table_updates():
     with torch.cuda.graph(graph):
         step()
     torch.cuda.synchronize()
+
+    # the oracle: every sequence's context (prefix and the step's rows)
+    # injected from the same hidden states, then the draft
+    model = OracleModel(wl, w_cpu)
+    Hs = W.gen_hiddens(wl, B * n_new, index=0, tag="step")
+    per_seq, hid_pos = [], []
+    for b, L in enumerate(lens):
+        n_pre = max(int(L) - n_new, 0)
+        hp = W.gen_hiddens(wl, n_pre, index=b, tag="prefix") if n_pre else None
+        rows = [h[b * n_new:(b + 1) * n_new] for h in Hs]
+        hb = rows if hp is None else [torch.cat([a, r]) for a, r in
+                                      zip(hp, rows)]
+        pos = np.concatenate([np.arange(n_pre),
+                              np.arange(int(L) - n_new, int(L))])
+        per_seq.append(inject_rows(model, hb, pos))
+        hid_pos.append((hb, pos))
+    anchors = W.gen_anchors(wl)
+    ref_or = draft_batch(model, per_seq, lens, anchors=anchors,
+                         keep_logits=True)
+    empty = {l: (np.zeros((0, wl.num_kv_heads, wl.head_dim)),) * 2
+             for l in range(wl.num_layers)}
+    fl = Float32Floor(wl, w_cpu, [empty] * B, lens, inject=hid_pos)
+
+    def against_oracle(rep):
+        kv_h = kv.cpu()
+        for b, L in enumerate(lens):
+            pos = np.arange(int(L))
+            pages = torch.from_numpy(table[b, pos // ps].astype(np.int64))
+            slots = torch.from_numpy(pos % ps)
+            got = kv_h[:, :, pages, :, slots, :]  # [L, Nl, 2, Hkv, d]
+            for l in range(wl.num_layers):
+                check_bf16_close(f64(got[:, l, 0]), per_seq[b][l][0],
+                                 f"replay {rep} K l{l} b{b}")
+                check_bf16_close(f64(got[:, l, 1]), per_seq[b][l][1],
+                                 f"replay {rep} V l{l} b{b}")
+        g = {"draft": draft.cpu().numpy(), "conf": conf.cpu().numpy(),
+             "margin": margin.cpu().numpy(),
+             "logits_all": logits.cpu().numpy().astype(np.float64)}
+        check_single_pass(wl, f"paged graph replay {rep}", g, ref_or, fl,
+                          anchors)
 
     rng = np.random.default_rng(12)
     for rep in range(3):
@@ -231,4 +280,5 @@ def test_paged_step_in_a_hip_graph_follows_table_updates():
         assert torch.equal(draft, ref[0]) and torch.equal(conf, ref[1]), \
             f"replay {rep} after moving the pages differs from eager"
         say(f"  replay {rep}: pages moved, draft and confidence equal eager")
+        against_oracle(rep)
     assert ctx.check_device_errors() == 0
