@@ -41,8 +41,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=W.HEADLINE,
-                    choices=list(W.WORKLOADS))
+    ap.add_argument("--workload", default=W.BENCH_DEFAULT,
+                    choices=list(W.WORKLOADS),
+                    help="the headline workload of the JSON line")
+    ap.add_argument("--only", action="store_true",
+                    help="measure the headline workload only (by default "
+                         "every other workload follows in `workloads`)")
     ap.add_argument("--timed-kernel", default="auto",
                     choices=["auto", "lmhead", "attention", "gemm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -315,30 +319,17 @@ def cpu_baseline(wl, weights, lens, budget_s):
                        f"{elapsed:.1f} s of float64 numpy on the host")}
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); the drafting path is not sharded in this "
-              "build.", file=sys.stderr)
-        sys.exit(2)
+def auto_kernel(wl):
+    """The kernel class that dominates a workload's step."""
+    return {"qwen3-8b-3L-b4-ctx32k": "attention",
+            "qwen3-8b-3L-b64-ctx256-2k-S2": "gemm",
+            "qwen3-8b-5L-b16-ctx1k-4k": "gemm"}.get(wl.name, "lmhead")
 
-    import torch
-    import block_diffusion_drafting_dflash_amd as dfl
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    wl = W.WORKLOADS[args.workload]
-    kind = args.timed_kernel
-    if kind == "auto":
-        kind = {"qwen3-8b-3L-b4-ctx32k": "attention",
-                "qwen3-8b-3L-b64-ctx256-2k-S2": "gemm",
-                "qwen3-8b-5L-b16-ctx1k-4k": "gemm"}.get(wl.name, "lmhead")
-
+def measure(wl, args, torch, dfl, dev, kind, full=True):
+    """Time one workload: exactly args.steps steps after args.warmup, then
+    the same steps with dispatch-bound events on the timed kernel class,
+    then with one event per step boundary.  Returns (entry, extras)."""
     ctx, kv, lens, inp, weights = setup(wl, torch, dfl, dev, args.page_size)
     step = make_step(ctx, kv, lens, inp, wl, torch, dfl)
     for _ in range(args.warmup):
@@ -351,6 +342,7 @@ def main():
     # instrumentation inside (an event bound to a kernel dispatch holds the
     # stream for a few microseconds on either side of that kernel).
     run = step
+    graph = None
     if args.graph:
         # the step's launches captured once (the calls enqueue kernels only);
         # the step closure binds the stream that is current when it is made
@@ -397,30 +389,35 @@ def main():
     torch.cuda.synchronize()
     per_step = np.array([evs[i].elapsed_time(evs[i + 1])
                          for i in range(args.steps)])
-    # Host cost of issuing one step (the calls only enqueue work): each step
-    # is issued onto an idle stream, timed on the host clock until the calls
-    # return, then synchronised.
-    host_us = []
-    for _ in range(min(args.steps, 20)):
+    extras = {}
+    if full:
+        # Host cost of issuing one step (the calls only enqueue work): each
+        # step is issued onto an idle stream, timed on the host clock until
+        # the calls return, then synchronised.
+        host_us = []
+        for _ in range(min(args.steps, 20)):
+            torch.cuda.synchronize()
+            h0 = time.perf_counter()
+            run()
+            host_us.append((time.perf_counter() - h0) * 1e6)
         torch.cuda.synchronize()
-        h0 = time.perf_counter()
-        run()
-        host_us.append((time.perf_counter() - h0) * 1e6)
-    torch.cuda.synchronize()
-    # Injection of a whole context chunk (the untimed set-up's first call,
-    # repeated with the same rows and values).
-    prefill = None
-    if inp["prefill"] is not None:
-        H, seq, pos = inp["prefill"]
-        ctx.inject_kv(H, seq, pos, kv)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        ctx.inject_kv(H, seq, pos, kv)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        pf_ms = t0.elapsed_time(t1)
-        prefill = {"rows": int(seq.numel()), "ms": round(pf_ms, 4),
-                   "rows_per_s": round(seq.numel() / (pf_ms / 1e3), 1)}
+        extras["host_enqueue_us_per_step"] = round(float(np.median(host_us)),
+                                                   1)
+        # Injection of a whole context chunk (the untimed set-up's first
+        # call, repeated with the same rows and values).
+        prefill = None
+        if inp["prefill"] is not None:
+            H, seq, pos = inp["prefill"]
+            ctx.inject_kv(H, seq, pos, kv)
+            torch.cuda.synchronize()
+            t0.record(stream)
+            ctx.inject_kv(H, seq, pos, kv)
+            t1.record(stream)
+            torch.cuda.synchronize()
+            pf_ms = t0.elapsed_time(t1)
+            prefill = {"rows": int(seq.numel()), "ms": round(pf_ms, 4),
+                       "rows_per_s": round(seq.numel() / (pf_ms / 1e3), 1)}
+        extras["prefill_inject"] = prefill
     if ctx.check_device_errors() != 0:
         raise RuntimeError("device error during the timed steps")
     ms_step = ms_total / args.steps
@@ -437,22 +434,26 @@ def main():
     else:
         ach, peak, unit = kf / k_avg_s / 1e12, MFMA_PEAK[wl.dtype], "TFLOP/s"
     acc = inp["accept"].cpu().numpy()
-
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
-        "data": "synthetic",
+    K = wl.block_size
+    p10, p50, p90 = (float(np.percentile(per_step, q)) for q in (10, 50, 90))
+    entry = {
+        "workload": wl.name, "dtype": wl.dtype,
         "config": {"workload": wl.name, "batch": wl.batch,
                    "ctx_len": [int(lens.min()), int(lens.max())],
-                   "block": wl.block_size, "draft_layers": wl.num_layers,
+                   "block": K, "draft_layers": wl.num_layers,
                    "passes": wl.num_passes,
                    "commit_per_pass": wl.commit_per_pass,
                    "new_rows_per_seq": wl.new_rows,
                    "launch": "hip_graph" if args.graph else "stream",
                    "kv_cache": (f"paged-{args.page_size}" if args.page_size
                                 else "contiguous")},
+        "value": round(value, 1), "ms_per_step": round(ms_step, 5),
+        "step_ms_p10_p50_p90": [round(p10, 5), round(p50, 5), round(p90, 5)],
+        "tokens_per_s_at_median_step": round(drafted / (p50 / 1e3), 1),
+        "block_rows_per_s": round(wl.batch * K * args.steps /
+                                  (ms_total / 1e3), 1),
+        "accepted_tokens_per_s": round(float(acc.sum()) * args.steps /
+                                       (ms_total / 1e3), 1),
         "roofline": {"kernel": kind, "bound": bound, "achieved": round(ach, 1),
                      "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
                      "traffic": measured_traffic(wl, kind),
@@ -465,16 +466,63 @@ def main():
                          ms_total_ev / args.steps, 5),
                      "alg_bytes_per_launch": int(kb),
                      "alg_flops_per_launch": kf},
-        "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 5)
-                                for q in (10, 50, 90)],
-        "prefill_inject": prefill,
-        "host_enqueue_us_per_step": round(float(np.median(host_us)), 1),
         "step": {"alg_bytes": int(by), "alg_flops": fl,
-                 "hbm_frac": round(by / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "hbm_frac": round(by / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                   4),
                  "mfma_frac": round(fl / (ms_step / 1e3) / 1e12 /
                                     MFMA_PEAK[wl.dtype], 4),
-                 "mean_accept_len": float(acc.mean())},
+                 "mean_accept_len": float(acc.mean()),
+                 # accept length a = tau + 1 in [1, K]; drafts wasted per
+                 # sequence-step = (K - 1) - tau
+                 "accept_len_hist": np.bincount(acc, minlength=K + 1)[
+                     1:].astype(int).tolist(),
+                 "drafts_wasted_per_seq_step": float(
+                     ((K - 1) - (acc - 1)).mean())},
     }
+    del ctx, kv, inp, graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return entry, extras, weights, lens
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the drafting path is not sharded in this "
+              "build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_diffusion_drafting_dflash_amd as dfl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = W.WORKLOADS[args.workload]
+    kind = args.timed_kernel if args.timed_kernel != "auto" else auto_kernel(wl)
+    head, extras, weights, lens = measure(wl, args, torch, dfl, dev, kind)
+    print(f"# {wl.name}: {head['ms_per_step']} ms/step, {head['value']} "
+          f"tokens/s", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "step_ms_p10_p50_p90": head["step_ms_p10_p50_p90"],
+        "tokens_per_s_at_median_step": head["tokens_per_s_at_median_step"],
+        "block_rows_per_s": head["block_rows_per_s"],
+        "accepted_tokens_per_s": head["accepted_tokens_per_s"],
+    }
+    out.update(extras)
+    out["step"] = head["step"]
     if args.copy_calibration:
         n = 1 << 28
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -483,11 +531,27 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = n * 4
+        del a, b
     if not args.no_cpu_baseline:
-        del ctx, kv
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(wl, weights, lens, args.cpu_budget)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 3)
+    del weights
+    torch.cuda.empty_cache()
+    if not args.only:
+        rest = []
+        for name in W.WORKLOAD_ORDER:
+            if name == wl.name:
+                continue
+            w2 = W.WORKLOADS[name]
+            e, _, wts, _ = measure(w2, args, torch, dfl, dev, auto_kernel(w2),
+                                   full=False)
+            del wts
+            torch.cuda.empty_cache()
+            print(f"# {name}: {e['ms_per_step']} ms/step, {e['value']} "
+                  f"tokens/s", file=sys.stderr, flush=True)
+            rest.append(e)
+        out["workloads"] = rest
     print(json.dumps(out), flush=True)
 
 

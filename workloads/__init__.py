@@ -111,9 +111,12 @@ WORKLOADS: Dict[str, Workload] = {
         match_prob=(0.75,), seed=1005, **_QWEN),
 }
 # Order of the five workloads: tiny parity case first, then the batch-1
-# Qwen3-8B-shaped drafter whose throughput is the headline number.
+# Qwen3-8B-shaped drafter, then the batched ones.
 WORKLOAD_ORDER: List[str] = list(WORKLOADS)
 HEADLINE = "qwen3-8b-1L-b1-ctx2048"
+# The benchmark's headline line: the largest workload that fits one GPU
+# (batch 64, two refinement passes); the others follow in the same line.
+BENCH_DEFAULT = "qwen3-8b-3L-b64-ctx256-2k-S2"
 
 
 def small_bf16(**kw) -> Workload:
