@@ -17,12 +17,19 @@ Sources (cited per function by page title and section):
     abstract page, arXiv 2602.06036)
   * "DFlash: Diffusion Drafts the Block" (stable-lab tutorial chapter)
 
+FP8 drafter weights (the guide's "FP4/FP8 mixed execution", section
+"Production Benchmarks on NVIDIA Blackwell B200", names no format): a
+projection may be given as FP8 E4M3 codes with one float32 scale per output
+row; the oracle decodes the codes from the E4M3 definition and computes
+with scale * value in float64, otherwise unchanged.
+
 Parity status: every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_*.py`` except draft *quality* (acceptance on real text),
 which needs trained weights: parity unpinned, and not claimed.
 """
 from .numerics import (round_bf16, identity_round, rms_norm, silu, rope,
-                       rope_angles, softmax, logsumexp)
+                       rope_angles, softmax, logsumexp, decode_e4m3,
+                       dequant_rows)
 from .drafter import (OracleModel, fuse_features, inject_kv, inject_rows,
                       block_attention, decoder_layer, lm_head_reduce,
                       confidence_commit, draft_sequence, draft_batch)

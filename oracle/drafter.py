@@ -29,8 +29,8 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-from .numerics import (identity_round, logsumexp, rms_norm, rope, round_bf16,
-                       silu, softmax)
+from .numerics import (dequant_rows, identity_round, logsumexp, rms_norm,
+                       rope, round_bf16, silu, softmax)
 
 
 def _f64(t):
@@ -45,6 +45,26 @@ def _f32(t):
         return t.astype(np.float32)
     import torch
     return t.detach().to("cpu", torch.float32).numpy()
+
+
+def _codes(t):
+    """Raw bytes of an FP8 weight tensor (torch float8 or uint8)."""
+    import torch
+    t = t.detach().to("cpu")
+    if t.dtype != torch.uint8:
+        t = t.view(torch.uint8)
+    return t.numpy()
+
+
+def _weight(weights, key, l=None):
+    """A projection matrix as float64: given in the drafter dtype, or as
+    FP8 E4M3 codes with a per-output-row scale (key + "_scale")."""
+    t = weights[key] if l is None else weights[key][l]
+    sk = key + "_scale"
+    if sk in weights and weights[sk] is not None:
+        sc = weights[sk] if l is None else weights[sk][l]
+        return dequant_rows(_codes(t), _f64(sc))
+    return _f64(t)
 
 
 class OracleModel:
@@ -63,8 +83,16 @@ class OracleModel:
         self.theta, self.eps, self.K = wl.rope_theta, wl.rms_eps, wl.block_size
         self.mask_id = wl.mask_id
         self.E = _f32(weights["embed"])
-        self.W_lm = _f32(weights["lm_head"])
-        self.W_fc = _f64(weights["fc"])
+        # the LM head is widened to float64 a slice at a time (lm_rows): kept
+        # in float32 (exact for bf16 / f32 values) or, FP8, as its codes and
+        # per-row scales
+        if weights.get("lm_head_scale") is not None:
+            self.W_lm = None
+            self.lm_codes = _codes(weights["lm_head"])
+            self.lm_scale = _f64(weights["lm_head_scale"])
+        else:
+            self.W_lm = _f32(weights["lm_head"])
+        self.W_fc = _weight(weights, "fc")
         self.g_h = _f64(weights["hidden_norm"])
         self.g_f = _f64(weights["final_norm"])
         n = wl.num_layers
@@ -72,9 +100,20 @@ class OracleModel:
         self.L = {}
         for l in self.layers:
             self.L[l] = {k: _f64(weights[k][l]) for k in (
-                "attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate",
-                "w_up", "w_down")}
+                "attn_norm", "mlp_norm")}
+            self.L[l].update({k: _weight(weights, k, l) for k in (
+                "wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")})
         self.layer_calls = 0  # decoder-layer invocations (single-pass check)
+
+    @property
+    def vocab(self) -> int:
+        return (self.W_lm if self.W_lm is not None else self.lm_codes).shape[0]
+
+    def lm_rows(self, c0: int, c1: int):
+        """LM-head rows [c0, c1) in float64."""
+        if self.W_lm is not None:
+            return self.W_lm[c0:c1].astype(np.float64)
+        return dequant_rows(self.lm_codes[c0:c1], self.lm_scale[c0:c1])
 
 
 # ---------------------------------------------------------------------------
@@ -163,11 +202,10 @@ def decoder_layer(model: OracleModel, l: int, x, ctx_k, ctx_v, pos):
 def lm_logits(model: OracleModel, x_rows, chunk: int = 16384):
     """z = W_lm . RMSNorm(x; g_f) in float64, never rounded."""
     hf = model.rnd(rms_norm(x_rows, model.g_f, model.eps))
-    V = model.W_lm.shape[0]
+    V = model.vocab
     z = np.empty((hf.shape[0], V), dtype=np.float64)
     for c0 in range(0, V, chunk):
-        z[:, c0:c0 + chunk] = hf @ model.W_lm[c0:c0 + chunk].astype(
-            np.float64).T
+        z[:, c0:c0 + chunk] = hf @ model.lm_rows(c0, c0 + chunk).T
     return z
 
 

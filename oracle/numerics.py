@@ -83,3 +83,26 @@ def softmax(z, axis=-1):
     m = np.max(z, axis=axis, keepdims=True)
     e = np.exp(z - m)
     return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def decode_e4m3(codes):
+    """Values of FP8 E4M3 codes (the OCP 8-bit float: 1 sign bit, 4 exponent
+    bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 is NaN).
+
+    exponent field e > 0: (-1)^s * (1 + m/8) * 2^(e - 7)
+    exponent field e = 0: (-1)^s * (m/8) * 2^(-6)   (subnormal)
+    """
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e > 0, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0),
+                   (m / 8.0) * 2.0 ** -6)
+    val = sign * val
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def dequant_rows(codes, scale):
+    """Weights stored as E4M3 codes with one float32 scale per output row
+    (row-major [out, in]): w[j, k] = scale[j] * value(codes[j, k])."""
+    return decode_e4m3(codes) * np.asarray(scale, dtype=np.float64)[:, None]

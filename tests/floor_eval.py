@@ -39,16 +39,29 @@ class Prepared:
                  layers: Optional[Sequence[int]] = None):
         self.wl, self.dtype = wl, dtype
         cv = lambda t: t.detach().to("cpu").to(dtype)
+
+        def mat(key, l=None):
+            # a projection: (matrix, per-row scale or None); FP8 codes are
+            # widened exactly and their scale applied after the product
+            t = w[key] if l is None else w[key][l]
+            sc = w.get(key + "_scale")
+            if sc is not None:
+                sc = cv(sc if l is None else sc[l])
+            return (cv(t), sc)
+
         self.embed = w["embed"]  # gathered by row, converted per pass
-        self.fc = cv(w["fc"])
+        self.fc = mat("fc")
         self.hidden_norm = cv(w["hidden_norm"])
         self.final_norm = cv(w["final_norm"])
-        self.lm_head = cv(w["lm_head"])
+        self.lm_head = mat("lm_head")
         self.layers = list(range(wl.num_layers)) if layers is None else list(
             layers)
-        self.L = {l: {k: cv(w[k][l]) for k in (
-            "attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up",
-            "w_down")} for l in self.layers}
+        self.L = {l: dict({k: cv(w[k][l]) for k in ("attn_norm",
+                                                      "mlp_norm")},
+                          **{k: mat(k, l) for k in (
+                              "wq", "wk", "wv", "wo", "w_gate", "w_up",
+                              "w_down")})
+                  for l in self.layers}
 
 
 def _store(p: Prepared, t: torch.Tensor) -> torch.Tensor:
@@ -59,10 +72,17 @@ def _store(p: Prepared, t: torch.Tensor) -> torch.Tensor:
     return torch.from_numpy(r).to(p.dtype)
 
 
-def _linear(p: Prepared, x: torch.Tensor, W: torch.Tensor, member: int,
+def _linear(p: Prepared, x: torch.Tensor, Ws, member: int,
             tag: int) -> torch.Tensor:
-    """x . W^T in the evaluation dtype; member > 0 sums the contraction in
-    seeded chunks in a seeded order."""
+    """x . W^T in the evaluation dtype (times the per-row scale of FP8
+    weights); member > 0 sums the contraction in seeded chunks in a seeded
+    order."""
+    W, sc = Ws
+    y = _product(x, W, member, tag)
+    return y if sc is None else y * sc
+
+
+def _product(x, W, member, tag):
     if member == 0:
         return F.linear(x, W)
     Kd = W.shape[1]

@@ -53,6 +53,9 @@ class Workload:
     rms_eps: float = 1.0e-6
     new_rows: int = BLOCK  # context rows injected per sequence per step
     seed: int = 0
+    # "dtype": projection matrices in the drafter dtype; "fp8": FP8 E4M3
+    # codes with one float32 scale per output row (bf16 drafters)
+    weight_format: str = "dtype"
 
     @property
     def mask_id(self) -> int:
@@ -113,6 +116,11 @@ WORKLOADS: Dict[str, Workload] = {
 # Order of the five workloads: tiny parity case first, then the batch-1
 # Qwen3-8B-shaped drafter, then the batched ones.
 WORKLOAD_ORDER: List[str] = list(WORKLOADS)
+# The batch-1 drafter with FP8 E4M3 projection weights (per-row scales).
+WORKLOADS["qwen3-8b-1L-b1-ctx2048-fp8"] = WORKLOADS[
+    "qwen3-8b-1L-b1-ctx2048"].replace(name="qwen3-8b-1L-b1-ctx2048-fp8",
+                                      weight_format="fp8")
+EXTRA_WORKLOADS: List[str] = ["qwen3-8b-1L-b1-ctx2048-fp8"]
 HEADLINE = "qwen3-8b-1L-b1-ctx2048"
 # The benchmark's headline line: the largest workload that fits one GPU
 # (batch 64, two refinement passes); the others follow in the same line.
@@ -195,7 +203,26 @@ def gen_weights(wl: Workload, device="cpu", random_gains: bool = False,
     for key, shp in shapes.items():
         w[key] = [normal(wl, key, shp, std, device, index=l)
                   for l in range(wl.num_layers)]
+    if wl.weight_format == "fp8":
+        for key in ("fc", "lm_head"):
+            w[key], w[key + "_scale"] = to_fp8_rows(w[key])
+        for key in shapes:
+            pairs = [to_fp8_rows(t) for t in w[key]]
+            w[key] = [c for c, _ in pairs]
+            w[key + "_scale"] = [sc for _, sc in pairs]
     return w
+
+
+def to_fp8_rows(t: torch.Tensor):
+    """FP8 E4M3 storage of a [out, in] matrix with one float32 scale per
+    output row: scale = max |row| / 448 (the largest E4M3 value), codes =
+    torch's own round-to-nearest conversion of row / scale (clamped to the
+    E4M3 range).  Returns (codes as torch.float8_e4m3fn, scales)."""
+    x = t.to(torch.float32)
+    amax = x.abs().amax(dim=1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (x / scale[:, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q, scale.contiguous()
 
 
 def gen_hiddens(wl: Workload, rows: int, device="cpu", index: int = 0,
