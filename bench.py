@@ -66,6 +66,14 @@ def parse():
 # algorithmic cost of a step (bytes that must cross HBM, flops of the math)
 # ---------------------------------------------------------------------------
 
+def weight_bytes(wl, rows, cols):
+    """Bytes of one projection matrix: the drafter dtype, or FP8 codes plus
+    one float32 scale per output row."""
+    if getattr(wl, "weight_format", "dtype") == "fp8":
+        return rows * cols + 4 * rows
+    return rows * cols * (4 if wl.dtype == "f32" else 2)
+
+
 def step_cost(wl, lens):
     esz = 4 if wl.dtype == "f32" else 2
     D, I, V, d = wl.hidden, wl.intermediate, wl.vocab, wl.head_dim
@@ -73,9 +81,10 @@ def step_cost(wl, lens):
     B, K, Nl = wl.batch, wl.block_size, wl.num_layers
     T = B * wl.new_rows
     ntd = wl.num_target_layers * wl.target_hidden
+    wb = lambda r, c: weight_bytes(wl, r, c)
     by = fl = 0.0
     # injection
-    by += T * ntd * esz + D * ntd * esz + Nl * 2 * kvd * D * esz
+    by += T * ntd * esz + wb(D, ntd) + Nl * wb(2 * kvd, D)
     by += T * Nl * 2 * kvd * esz + D * esz
     fl += 2.0 * T * D * ntd + 2.0 * T * Nl * 2 * kvd * D
     lm = []
@@ -83,12 +92,13 @@ def step_cost(wl, lens):
     for s in range(wl.num_passes):
         masked = B * (K - 1 - s * wl.commit_per_pass)
         by += R * D * esz
-        layer_w = ((qd + 2 * kvd) * D + qd * D + 3 * I * D + 2 * D) * esz
+        layer_w = (wb(qd + 2 * kvd, D) + wb(D, qd) + wb(2 * I, D) +
+                   wb(D, I) + 2 * D * esz)
         kv_read = sum((int(L) + K) * 2 * kvd * esz for L in lens)
         by += Nl * (layer_w + kv_read + R * 2 * kvd * esz)
         fl += Nl * 2.0 * R * ((qd + 2 * kvd) * D + qd * D + 3 * I * D)
         fl += Nl * sum(4.0 * wl.num_q_heads * K * (int(L) + K) * d for L in lens)
-        lm_bytes = V * D * esz + masked * D * esz + D * esz
+        lm_bytes = wb(V, D) + masked * D * esz + D * esz
         lm_flops = 2.0 * masked * V * D
         by += lm_bytes
         fl += lm_flops
@@ -121,7 +131,7 @@ def kernel_cost(wl, lens, kind):
     for _ in range(wl.num_passes):
         for _ in range(wl.num_layers):
             shapes += [(R, qd + 2 * kvd, D), (R, D, qd), (R, 2 * I, D), (R, D, I)]
-    by = sum((n * k + m * k) * esz for m, n, k in shapes)
+    by = sum(weight_bytes(wl, n, k) + m * k * esz for m, n, k in shapes)
     fl = sum(2.0 * m * n * k for m, n, k in shapes)
     return by / len(shapes), fl / len(shapes)
 
@@ -438,6 +448,8 @@ def measure(wl, args, torch, dfl, dev, kind, full=True):
     p10, p50, p90 = (float(np.percentile(per_step, q)) for q in (10, 50, 90))
     entry = {
         "workload": wl.name, "dtype": wl.dtype,
+        "weights": ("fp8-e4m3, per-row fp32 scales" if wl.weight_format ==
+                    "fp8" else wl.dtype),
         "config": {"workload": wl.name, "batch": wl.batch,
                    "ctx_len": [int(lens.min()), int(lens.max())],
                    "block": K, "draft_layers": wl.num_layers,
@@ -540,7 +552,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.only:
         rest = []
-        for name in W.WORKLOAD_ORDER:
+        for name in W.WORKLOAD_ORDER + W.EXTRA_WORKLOADS:
             if name == wl.name:
                 continue
             w2 = W.WORKLOADS[name]

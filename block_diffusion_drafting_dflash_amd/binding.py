@@ -22,6 +22,7 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_E_INVALID", -2: "DFLASH_E_SHAPE",
           -3: "DFLASH_E_CAPACITY", -4: "DFLASH_E_DEVICE",
           -5: "DFLASH_E_UNSUPPORTED"}
 DTYPE = {"f32": 0, "bf16": 1}
+WEIGHT_FORMAT = {"dtype": 0, "fp8": 1}
 
 # C-ABI symbols declared in include/dflash.h and include/dflash_harness.h
 LIB_SYMBOLS = ["dflash_create", "dflash_destroy", "dflash_kv_cache_bytes",
@@ -32,7 +33,8 @@ LIB_SYMBOLS = ["dflash_create", "dflash_destroy", "dflash_kv_cache_bytes",
                "dflash_set_kv_pages", "dflash_kv_cache_paged_bytes",
                "dflash_draft_block_noalloc"]
 TIME_KIND = {"off": 0, "lmhead": 1, "attention": 2, "gemm": 3}
-HARNESS_SYMBOLS = ["dflash_harness_synth_target"]
+HARNESS_SYMBOLS = ["dflash_harness_synth_target",
+                   "dflash_harness_fp8_to_bf16"]
 
 
 class DFlashError(RuntimeError):
@@ -47,10 +49,13 @@ class Config(ctypes.Structure):
         "intermediate", "vocab", "num_target_layers", "target_hidden",
         "block_size", "mask_token_id", "dtype", "max_batch", "max_ctx",
         "max_inject_rows")] + [("rope_theta", ctypes.c_float),
-                               ("rms_eps", ctypes.c_float)]
+                               ("rms_eps", ctypes.c_float),
+                               ("weight_format", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
+
+LAYER_MATRICES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
 
 class Weights(ctypes.Structure):
@@ -58,7 +63,10 @@ class Weights(ctypes.Structure):
                 ("hidden_norm", ctypes.c_void_p)] + [
         (n, _PP) for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm",
                            "w_gate", "w_up", "w_down")] + [
-        ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p)]
+        ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+        ("fc_scale", ctypes.c_void_p)] + [
+        (n + "_scale", _PP) for n in LAYER_MATRICES] + [
+        ("lm_head_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -126,6 +134,8 @@ def load_harness():
     h.dflash_harness_synth_target.argtypes = [vp, i32, i32, i32, vp, vp, vp,
                                               vp, vp, vp]
     h.dflash_harness_synth_target.restype = ctypes.c_int
+    h.dflash_harness_fp8_to_bf16.argtypes = [vp, i32, vp, vp]
+    h.dflash_harness_fp8_to_bf16.restype = ctypes.c_int
     _harness = h
     return h
 
@@ -158,7 +168,8 @@ def make_config(wl, max_batch=None, max_ctx=None,
         mask_token_id=wl.mask_id, dtype=DTYPE[wl.dtype],
         max_batch=max_batch or wl.batch, max_ctx=max_ctx or wl.ctx_max,
         max_inject_rows=max_inject_rows or max(wl.batch * wl.new_rows, 2048),
-        rope_theta=wl.rope_theta, rms_eps=wl.rms_eps)
+        rope_theta=wl.rope_theta, rms_eps=wl.rms_eps,
+        weight_format=WEIGHT_FORMAT[getattr(wl, "weight_format", "dtype")])
 
 
 def kv_cache_bytes(cfg: Config) -> int:
@@ -195,6 +206,11 @@ class DFlash:
         for key in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate",
                     "w_up", "w_down"):
             setattr(w, key, plist(key))
+        if weights.get("fc_scale") is not None:  # FP8 E4M3 projections
+            w.fc_scale = weights["fc_scale"].data_ptr()
+            w.lm_head_scale = weights["lm_head_scale"].data_ptr()
+            for key in LAYER_MATRICES:
+                setattr(w, key + "_scale", plist(key + "_scale"))
         self._w = w
         ctx = ctypes.c_void_p()
         _check(self.lib.dflash_create(ctypes.byref(self.cfg), ctypes.byref(w),
@@ -345,6 +361,18 @@ def verify_greedy(draft: torch.Tensor, target: torch.Tensor,
                                     _ptr(target), _ptr(accept),
                                     _ptr(next_anchor)))
     return accept, next_anchor
+
+
+def fp8_to_bf16(codes: torch.Tensor, stream=None) -> torch.Tensor:
+    """The kernels' E4M3 -> bf16 widening of a uint8 code tensor (harness)."""
+    h = load_harness()
+    n = codes.numel()
+    out = torch.empty(n, dtype=torch.int16, device=codes.device)
+    st = h.dflash_harness_fp8_to_bf16(_stream(stream), n, _ptr(codes),
+                                      _ptr(out))
+    if st != 0:
+        raise RuntimeError(f"dflash_harness_fp8_to_bf16 failed ({st})")
+    return out
 
 
 def synth_target(draft, u, r, tail, p, vocab, target=None, stream=None):

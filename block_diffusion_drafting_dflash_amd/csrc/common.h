@@ -114,6 +114,23 @@ __device__ __forceinline__ void mma32(f32x16& acc, u32x4 a, u32x4 b) {
       0);
 }
 
+// Eight FP8 E4M3 values (the 8 bytes of lo, hi in memory order) widened to
+// one 16-byte bf16 fragment, element k from byte k.  Every E4M3 value is a
+// bf16 value (3 of bf16's 7 mantissa bits, exponents well inside its range),
+// so the conversion is exact; the per-row scale is applied to the sums.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+  r.x = __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+  r.y = __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+  r.z = __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+  r.w = __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+  return r;
+}
+
 // Prefetch loads of pipelined loops are issued as inline assembly, so that
 // the compiler's wait insertion (which drains every outstanding load at a
 // loop header or a branch) does not see them; the loop waits for exactly the

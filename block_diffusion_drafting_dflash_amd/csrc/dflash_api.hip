@@ -59,6 +59,14 @@ DispatchTiming& dispatch_timing() {
 }
 }  // namespace dflash
 
+// One projection matrix in the context's layout.
+struct PW {
+  void* w = nullptr;        // packed: dtype fragments, or FP8 step pairs
+  void* w16 = nullptr;      // FP8: codes widened to the bf16 layout, for the
+                            // tiled kernels (null if no call can tile)
+  float* scale = nullptr;   // FP8: per output column, packed column order
+};
+
 struct dflash_ctx {
   dflash_config cfg;
   bool bf16 = true;
@@ -75,11 +83,12 @@ struct dflash_ctx {
   std::vector<const void*> attn_norm, mlp_norm;
 
   // packed copies of every projection matrix (fragment-major, see kernels.h)
+  bool fp8 = false;        // projections stored as FP8 E4M3 step pairs
   void* wpack = nullptr;
-  void* pk_fc = nullptr;   // [D][n_t * D_t]
-  void* pk_kv = nullptr;   // [N_l * 2 * Hkv * d][D], K/V heads, RoPE pairs
-  void* pk_lm = nullptr;   // [V][D]
-  std::vector<void*> pk_qkv, pk_o, pk_gu, pk_down;
+  PW pk_fc;                // [D][n_t * D_t]
+  PW pk_kv;                // [N_l * 2 * Hkv * d][D], K/V heads, RoPE pairs
+  PW pk_lm;                // [V][D]
+  std::vector<PW> pk_qkv, pk_o, pk_gu, pk_down;
 
   // workspace
   void* ws = nullptr;
@@ -160,6 +169,11 @@ dflash_status check_config(const dflash_config* c) {
                 c->mask_token_id, c->vocab);
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f))
     return fail(DFLASH_E_INVALID, "rope_theta must be > 0, rms_eps >= 0");
+  if (c->weight_format != DFLASH_WEIGHTS_DTYPE &&
+      c->weight_format != DFLASH_WEIGHTS_FP8_E4M3)
+    return fail(DFLASH_E_INVALID, "unknown weight_format %d", c->weight_format);
+  if (c->weight_format == DFLASH_WEIGHTS_FP8_E4M3 && c->dtype != DFLASH_BF16)
+    return fail(DFLASH_E_UNSUPPORTED, "FP8 weights need a bf16 drafter");
   if (c->block_size != 16)
     return fail(DFLASH_E_UNSUPPORTED, "block_size %d (only 16)", c->block_size);
   if (c->head_dim != 64 && c->head_dim != 128)
@@ -270,6 +284,14 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
     a.a_packed = 1;
     a.a_seg_k = a.Kd;
   }
+  if (tiled && a.wfp8) {
+    // the tiled kernels take the widened codes (same values) and the scales
+    if (!a.w_tiled)
+      return fail(DFLASH_E_UNSUPPORTED, "no bf16 layout of the FP8 weights "
+                  "for %d rows (created for fewer)", a.M);
+    a.w = a.w_tiled;
+    a.wfp8 = 0;
+  }
   if (tiled) {
     const int cfg = plan_tiled(a.M, a.N, splittable(a));
     const int S = plan_ksplit(c, a, cfg, sw);
@@ -296,12 +318,16 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
 }
 
 // GEMM on a packed activation operand (rows M, contraction Kd).
-GemmArgs packed_args(const void* A, const void* W, int M, int N, int Kd) {
+GemmArgs packed_args(const void* A, const PW& W, bool fp8, int M, int N,
+                     int Kd) {
   GemmArgs a{};
   a.a_ptr[0] = A;
   a.a_packed = 1;
   a.a_seg_k = Kd;
-  a.w = W;
+  a.w = W.w;
+  a.wfp8 = fp8 ? 1 : 0;
+  a.wscale = W.scale;
+  a.w_tiled = W.w16;
   a.M = M;
   a.N = N;
   a.Kd = Kd;
@@ -518,7 +544,7 @@ dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
       if (l > 0 || !fuse_norm)
         DF_HIP(launch_rmsnorm(bf, R, D, ws.x, nullptr, ctx->attn_norm[l],
                               c.rms_eps, ws.h, s));
-      GemmArgs a = packed_args(ws.h, ctx->pk_qkv[l], R, qd + 2 * kvd, D);
+      GemmArgs a = packed_args(ws.h, ctx->pk_qkv[l], ctx->fp8, R, qd + 2 * kvd, D);
       set_pairs(a, d, d / 2);
       set_cache_geometry(a, ctx);
       a.ep = EP_QKV;
@@ -536,7 +562,7 @@ dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
         DF_HIP(launch_attention(bf, d, batch, at, s));
       }
       // x += o . Wo^T
-      GemmArgs o = packed_args(ws.ob, ctx->pk_o[l], R, D, qd);
+      GemmArgs o = packed_args(ws.ob, ctx->pk_o[l], ctx->fp8, R, D, qd);
       o.ep = EP_RESID;
       o.out_f32 = ws.x;
       o.ldo = D;
@@ -545,14 +571,14 @@ dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
       // act = silu(h Wg^T) * (h Wu^T), h = RMSNorm(x)
       DF_HIP(launch_rmsnorm(bf, R, D, ws.x, nullptr, ctx->mlp_norm[l],
                             c.rms_eps, ws.h, s));
-      GemmArgs gu = packed_args(ws.h, ctx->pk_gu[l], R, 2 * I, D);
+      GemmArgs gu = packed_args(ws.h, ctx->pk_gu[l], ctx->fp8, R, 2 * I, D);
       set_pairs(gu, 2 * I, I);
       gu.ep = EP_SWIGLU;
       gu.out_t = ws.act;
       st = run_gemm(ctx, gu, s, ws.split);
       if (st != DFLASH_OK) return st;
       // x += act . Wd^T
-      GemmArgs dn = packed_args(ws.act, ctx->pk_down[l], R, D, I);
+      GemmArgs dn = packed_args(ws.act, ctx->pk_down[l], ctx->fp8, R, D, I);
       dn.ep = EP_RESID;
       dn.out_f32 = ws.x;
       dn.ldo = D;
@@ -564,7 +590,7 @@ dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
     const int Mh = batch * n_cap;
     DF_HIP(launch_rmsnorm(bf, Mh, D, ws.x, ws.rowmap, ctx->final_norm,
                           c.rms_eps, ws.hf, s));
-    GemmArgs hd = packed_args(ws.hf, ctx->pk_lm, Mh, V, D);
+    GemmArgs hd = packed_args(ws.hf, ctx->pk_lm, ctx->fp8, Mh, V, D);
     hd.ep = EP_TOP2;
     hd.top2 = ws.lm_part;
     hd.rowmap = ws.rowmap;
@@ -695,9 +721,31 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
     }
   }
 
+  if (c.weight_format == DFLASH_WEIGHTS_FP8_E4M3) {
+    const float* sing[] = {w->fc_scale, w->lm_head_scale};
+    const char* sn[] = {"fc_scale", "lm_head_scale"};
+    for (int i = 0; i < 2; ++i)
+      if (!sing[i] || (reinterpret_cast<uintptr_t>(sing[i]) & 3u))
+        return fail(DFLASH_E_INVALID, "FP8 weights: %s NULL or misaligned",
+                    sn[i]);
+    const float* const* sl[] = {w->wq_scale, w->wk_scale, w->wv_scale,
+                                w->wo_scale, w->w_gate_scale, w->w_up_scale,
+                                w->w_down_scale};
+    const char* sln[] = {"wq_scale", "wk_scale", "wv_scale", "wo_scale",
+                         "w_gate_scale", "w_up_scale", "w_down_scale"};
+    for (int i = 0; i < 7; ++i) {
+      if (!sl[i]) return fail(DFLASH_E_INVALID, "FP8 weights: %s is NULL", sln[i]);
+      for (int l = 0; l < c.num_layers; ++l)
+        if (!sl[i][l] || (reinterpret_cast<uintptr_t>(sl[i][l]) & 3u))
+          return fail(DFLASH_E_INVALID, "FP8 weights: %s[%d] NULL or "
+                      "misaligned", sln[i], l);
+    }
+  }
+
   dflash_ctx* x = new dflash_ctx();
   x->cfg = c;
   x->bf16 = c.dtype == DFLASH_BF16;
+  x->fp8 = c.weight_format == DFLASH_WEIGHTS_FP8_E4M3;
   x->esz = x->bf16 ? 2 : 4;
   x->P = c.max_ctx + c.block_size;
   int dev = 0;
@@ -729,23 +777,35 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
   const size_t esz = x->esz;
 
   // ---- packed weights: one allocation, repacked by pack kernels ----
-  struct PItem { void** p; size_t elems; };
+  // One entry per projection matrix: its packed form (dtype fragments, or
+  // FP8 step pairs), and with FP8 weights the per-column scales and, where
+  // some call can run the tiled kernels, the codes widened to the bf16
+  // layout (inject above 16 rows, drafting batches above one sequence).
+  const bool fp8 = x->fp8;
+  const bool w16_inject = fp8 && c.max_inject_rows > 16;
+  const bool w16_draft = fp8 && c.max_batch > 1;
+  struct PItem { PW* pw; size_t rows, cols; bool w16; };
   std::vector<PItem> pit;
   x->pk_qkv.resize(Nl);
   x->pk_o.resize(Nl);
   x->pk_gu.resize(Nl);
   x->pk_down.resize(Nl);
-  pit.push_back({&x->pk_fc, (size_t)D * ntd});
-  pit.push_back({&x->pk_kv, (size_t)Nl * 2 * kvd * D});
-  pit.push_back({&x->pk_lm, (size_t)c.vocab * D});
+  pit.push_back({&x->pk_fc, (size_t)D, (size_t)ntd, w16_inject});
+  pit.push_back({&x->pk_kv, (size_t)Nl * 2 * kvd, (size_t)D, w16_inject});
+  pit.push_back({&x->pk_lm, (size_t)c.vocab, (size_t)D, w16_draft});
   for (int l = 0; l < Nl; ++l) {
-    pit.push_back({&x->pk_qkv[l], (size_t)(qd + 2 * kvd) * D});
-    pit.push_back({&x->pk_o[l], (size_t)D * qd});
-    pit.push_back({&x->pk_gu[l], (size_t)2 * I * D});
-    pit.push_back({&x->pk_down[l], (size_t)D * I});
+    pit.push_back({&x->pk_qkv[l], (size_t)(qd + 2 * kvd), (size_t)D, w16_draft});
+    pit.push_back({&x->pk_o[l], (size_t)D, (size_t)qd, w16_draft});
+    pit.push_back({&x->pk_gu[l], (size_t)2 * I, (size_t)D, w16_draft});
+    pit.push_back({&x->pk_down[l], (size_t)D, (size_t)I, w16_draft});
   }
+  const size_t wsz = fp8 ? 1 : esz;
   size_t ptotal = 0;
-  for (auto& it : pit) ptotal += align_up(it.elems * esz, 256);
+  for (auto& it : pit) {
+    ptotal += align_up(it.rows * it.cols * wsz, 256);
+    if (fp8) ptotal += align_up(it.rows * sizeof(float), 256);
+    if (it.w16) ptotal += align_up(it.rows * it.cols * 2, 256);
+  }
   if (hipMalloc(&x->wpack, ptotal) != hipSuccess) {
     delete x;
     return fail(DFLASH_E_DEVICE, "packed-weight allocation of %zu bytes failed",
@@ -754,12 +814,21 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
   {
     char* p = static_cast<char*>(x->wpack);
     for (auto& it : pit) {
-      *it.p = p;
-      p += align_up(it.elems * esz, 256);
+      it.pw->w = p;
+      p += align_up(it.rows * it.cols * wsz, 256);
+      if (fp8) {
+        it.pw->scale = reinterpret_cast<float*>(p);
+        p += align_up(it.rows * sizeof(float), 256);
+      }
+      if (it.w16) {
+        it.pw->w16 = p;
+        p += align_up(it.rows * it.cols * 2, 256);
+      }
     }
   }
-  auto pack = [&](std::vector<std::pair<const void*, int>> segs, int Kd,
-                  void* dst, int cmap, int group, int off) -> bool {
+  using Segs = std::vector<std::pair<const void*, int>>;
+  auto pack1 = [&](const Segs& segs, int Kd, void* dst, int cmap, int group,
+                   int off, int mode) -> bool {
     PackArgs a{};
     int n = 0;
     a.n0[0] = 0;
@@ -773,26 +842,50 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
     a.cmap = cmap;
     a.pair_group = group;
     a.pair_off = off;
+    a.mode = mode;
     a.dst = dst;
     return launch_pack(x->bf16, a, nullptr) == hipSuccess;
   };
-  bool ok = pack({{w->fc, D}}, ntd, x->pk_fc, MAP_LINEAR, 0, 0) &&
-            pack({{w->lm_head, c.vocab}}, D, x->pk_lm, MAP_LINEAR, 0, 0);
+  // a matrix from its row segments (and, FP8, their scale vectors)
+  auto pack = [&](const Segs& segs, const Segs& scales, int Kd, PW& pw,
+                  int cmap, int group, int off) -> bool {
+    if (!fp8) return pack1(segs, Kd, pw.w, cmap, group, off, PACK_SAME);
+    return pack1(segs, Kd, pw.w, cmap, group, off, PACK_FP8) &&
+           pack1(scales, 1, pw.scale, cmap, group, off, PACK_SCALE) &&
+           (!pw.w16 ||
+            pack1(segs, Kd, pw.w16, cmap, group, off, PACK_FP8_BF16));
+  };
+  bool ok = pack({{w->fc, D}}, {{w->fc_scale, D}}, ntd, x->pk_fc, MAP_LINEAR,
+                 0, 0) &&
+            pack({{w->lm_head, c.vocab}}, {{w->lm_head_scale, c.vocab}}, D,
+                 x->pk_lm, MAP_LINEAR, 0, 0);
   {
-    std::vector<std::pair<const void*, int>> kvsegs;
+    Segs kvsegs, kvsc;
     for (int l = 0; l < Nl; ++l) {
       kvsegs.push_back({w->wk[l], kvd});
       kvsegs.push_back({w->wv[l], kvd});
+      if (fp8) {
+        kvsc.push_back({w->wk_scale[l], kvd});
+        kvsc.push_back({w->wv_scale[l], kvd});
+      }
     }
-    ok = ok && pack(kvsegs, D, x->pk_kv, MAP_PAIRS, d, d / 2);
+    ok = ok && pack(kvsegs, kvsc, D, x->pk_kv, MAP_PAIRS, d, d / 2);
   }
   for (int l = 0; l < Nl && ok; ++l) {
-    ok = pack({{w->wq[l], qd}, {w->wk[l], kvd}, {w->wv[l], kvd}}, D,
-              x->pk_qkv[l], MAP_PAIRS, d, d / 2) &&
-         pack({{w->wo[l], D}}, qd, x->pk_o[l], MAP_LINEAR, 0, 0) &&
-         pack({{w->w_gate[l], I}, {w->w_up[l], I}}, D, x->pk_gu[l], MAP_PAIRS,
-              2 * I, I) &&
-         pack({{w->w_down[l], D}}, I, x->pk_down[l], MAP_LINEAR, 0, 0);
+    auto sc = [&](const float* const* v, int n) -> std::pair<const void*, int> {
+      return {fp8 ? v[l] : nullptr, n};
+    };
+    ok = pack({{w->wq[l], qd}, {w->wk[l], kvd}, {w->wv[l], kvd}},
+              {sc(w->wq_scale, qd), sc(w->wk_scale, kvd),
+               sc(w->wv_scale, kvd)},
+              D, x->pk_qkv[l], MAP_PAIRS, d, d / 2) &&
+         pack({{w->wo[l], D}}, {sc(w->wo_scale, D)}, qd, x->pk_o[l],
+              MAP_LINEAR, 0, 0) &&
+         pack({{w->w_gate[l], I}, {w->w_up[l], I}},
+              {sc(w->w_gate_scale, I), sc(w->w_up_scale, I)}, D, x->pk_gu[l],
+              MAP_PAIRS, 2 * I, I) &&
+         pack({{w->w_down[l], D}}, {sc(w->w_down_scale, D)}, I,
+              x->pk_down[l], MAP_LINEAR, 0, 0);
   }
   if (!ok || hipDeviceSynchronize() != hipSuccess) {
     dflash_destroy(x);
@@ -961,7 +1054,10 @@ dflash_status dflash_inject_kv(dflash_ctx* ctx, void* stream,
   a.lda = ld;
   a.a_seg_k = c.target_hidden;
   a.a_packed = 0;
-  a.w = ctx->pk_fc;
+  a.w = ctx->pk_fc.w;
+  a.wfp8 = ctx->fp8 ? 1 : 0;
+  a.wscale = ctx->pk_fc.scale;
+  a.w_tiled = ctx->pk_fc.w16;
   a.M = T;
   a.N = D;
   a.Kd = ntd;
@@ -977,7 +1073,7 @@ dflash_status dflash_inject_kv(dflash_ctx* ctx, void* stream,
                         c.rms_eps, ctx->cond, s));
   // every layer's K and V projection of H_cond in one pass; RoPE on K;
   // scatter into the cache
-  GemmArgs b = packed_args(ctx->cond, ctx->pk_kv, T, c.num_layers * 2 * kvd, D);
+  GemmArgs b = packed_args(ctx->cond, ctx->pk_kv, ctx->fp8, T, c.num_layers * 2 * kvd, D);
   set_pairs(b, d, d / 2);
   set_cache_geometry(b, ctx);
   b.ep = EP_KV;

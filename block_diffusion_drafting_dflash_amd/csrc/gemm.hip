@@ -47,6 +47,82 @@ namespace {
 // next step, where fp32 accumulation error over thousands of terms flips
 // roundings that then spread through the layer.  The LM head's logits feed
 // nothing further and accumulate in fp32.
+// The same over FP8 step-pair weights (packed A): a wave takes pairs wave,
+// wave + W, ...; each pair's weight load is widened to two bf16 fragments.
+template <int MT, int W, int U, bool F64>
+__device__ __forceinline__ void gemm_core_fp8(const GemmArgs& p, int tile,
+                                              int m_base,
+                                              double (&acc)[MT][4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int npairs = p.Kd / 64, nsteps = p.Kd / 32;
+  const char* wbase =
+      static_cast<const char*>(p.w) + ((int64_t)tile * npairs * 64 + lane) * 16;
+  const char* abase[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int mt = min(m_base / 16 + m, (p.M + 15) / 16 - 1);
+    abase[m] = static_cast<const char*>(p.a_ptr[0]) +
+               ((int64_t)mt * nsteps * 64 + lane) * 16;
+  }
+  f32x4 acc32[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    acc32[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[m][j] = 0.0;
+  }
+  auto step = [&](int m, u32x4 a, u32x4 b) {
+    if constexpr (F64) {
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+      mma16(t, a, b, bf16_t());
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[m][j] += (double)t[j];
+    } else {
+      mma16(acc32[m], a, b, bf16_t());
+    }
+  };
+  int s = wave;
+  for (; s + (U - 1) * W < npairs; s += U * W) {
+    u32x4 bw[U], af[U][MT][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      bw[u] = load16(wbase + (int64_t)(s + u * W) * 1024);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        af[u][m][0] = load16(abase[m] + (int64_t)(2 * (s + u * W)) * 1024);
+        af[u][m][1] = load16(abase[m] + (int64_t)(2 * (s + u * W) + 1) * 1024);
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x4 b0 = fp8x8_to_bf16(bw[u].x, bw[u].y);
+      const u32x4 b1 = fp8x8_to_bf16(bw[u].z, bw[u].w);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        step(m, af[u][m][0], b0);
+        step(m, af[u][m][1], b1);
+      }
+    }
+  }
+  for (; s < npairs; s += W) {
+    const u32x4 bw = load16(wbase + (int64_t)s * 1024);
+    const u32x4 b0 = fp8x8_to_bf16(bw.x, bw.y);
+    const u32x4 b1 = fp8x8_to_bf16(bw.z, bw.w);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      step(m, load16(abase[m] + (int64_t)(2 * s) * 1024), b0);
+      step(m, load16(abase[m] + (int64_t)(2 * s + 1) * 1024), b1);
+    }
+  }
+  if constexpr (!F64) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[m][j] += (double)acc32[m][j];
+  }
+}
+
 template <typename T, int MT, int AP, int W, int U, bool F64>
 __device__ __forceinline__ void gemm_core(const GemmArgs& p, int tile,
                                           int m_base, double (&acc)[MT][4]) {
@@ -138,39 +214,56 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& p, int tile,
 // alternate, so that while one block is multiplied the loads of the next
 // are in flight.  The loads are the staging loads with exact waits: the
 // compiler's own waits would drain both sets at every loop edge.
-template <int AHEAD, int NL, int U, int MT, typename T, bool F64>
+// With WF8 a unit is a pair of contraction steps: one FP8 weight load (two
+// steps) and two A fragments per row tile; otherwise one step.
+template <int AHEAD, int NL, int U, int MT, typename T, bool F64, bool WF8>
 __device__ __forceinline__ void packed_block(u32x4 (&st)[NL], int first,
                                              int n_i, double (&acc)[MT][4],
                                              f32x4 (&acc32)[MT]) {
+  constexpr int AS = WF8 ? 2 : 1, UL = 1 + AS * MT;
   stage_wait<0, NL, AHEAD>(st);
+  auto step = [&](int m, u32x4 a, u32x4 b) {
+    if constexpr (F64) {
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+      mma16(t, a, b, T());
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[m][j] += (double)t[j];
+    } else {
+      mma16(acc32[m], a, b, T());
+    }
+  };
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (first + u >= n_i) break;  // uniform: past this wave's last step
+    if constexpr (WF8) {
+      const u32x4 w = st[u * UL];
+      const u32x4 b0 = fp8x8_to_bf16(w.x, w.y), b1 = fp8x8_to_bf16(w.z, w.w);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if constexpr (F64) {
-        f32x4 t = {0.f, 0.f, 0.f, 0.f};
-        mma16(t, st[u * (1 + MT) + 1 + m], st[u * (1 + MT)], T());
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[m][j] += (double)t[j];
-      } else {
-        mma16(acc32[m], st[u * (1 + MT) + 1 + m], st[u * (1 + MT)], T());
+      for (int m = 0; m < MT; ++m) {
+        step(m, st[u * UL + 1 + 2 * m], b0);
+        step(m, st[u * UL + 2 + 2 * m], b1);
       }
+    } else {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) step(m, st[u * UL + 1 + m], st[u * UL]);
     }
   }
 }
 
-template <typename T, int MT, int W, int U, bool F64>
+template <typename T, int MT, int W, int U, bool F64, bool WF8>
 __device__ __forceinline__ void gemm_core_packed(const GemmArgs& p, int tile,
                                                  int m_base,
                                                  double (&acc)[MT][4]) {
   constexpr int KC = Storage<T>::KC;
-  constexpr int NL = U * (1 + MT);  // loads per block: weight, then A tiles
+  constexpr int AS = WF8 ? 2 : 1;
+  constexpr int UL = 1 + AS * MT;  // loads per unit: weight, then A tiles
+  constexpr int NL = U * UL;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nsteps = p.Kd / KC;
+  const int nunits = WF8 ? nsteps / 2 : nsteps;
   const char* wbase =
-      static_cast<const char*>(p.w) + ((int64_t)tile * nsteps * 64 + lane) * 16;
+      static_cast<const char*>(p.w) + ((int64_t)tile * nunits * 64 + lane) * 16;
   const char* abase[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -185,17 +278,21 @@ __device__ __forceinline__ void gemm_core_packed(const GemmArgs& p, int tile,
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[m][j] = 0.0;
   }
-  const int n_i = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;
+  const int n_i = wave < nunits ? (nunits - 1 - wave) / W + 1 : 0;
   const int nb = (n_i + U - 1) / U;
-  // block b holds this wave's steps bU .. bU + U - 1 (clamped to the last)
+  // block b holds this wave's units bU .. bU + U - 1 (clamped to the last)
   auto load = [&](u32x4(&st)[NL], int blk) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = min(blk * U + u, n_i - 1);
-      const int64_t off = (int64_t)(wave + i * W) * 1024;
-      st[u * (1 + MT)] = stage_load(wbase + off);
+      const int unit = wave + i * W;
+      st[u * UL] = stage_load(wbase + (int64_t)unit * 1024);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) st[u * (1 + MT) + 1 + m] = stage_load(abase[m] + off);
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int h = 0; h < AS; ++h)
+          st[u * UL + 1 + AS * m + h] =
+              stage_load(abase[m] + (int64_t)(AS * unit + h) * 1024);
     }
   };
   if (nb > 0) {
@@ -203,19 +300,20 @@ __device__ __forceinline__ void gemm_core_packed(const GemmArgs& p, int tile,
     // exists, then the last pair with no refill.  Every set has a single
     // consumer, so no in-flight register is ever copied.  With an odd block
     // count the last refill of s1 (or, for one block, s1 itself) repeats
-    // the wave's last step and is not multiplied.
+    // the wave's last unit and is not multiplied.
     u32x4 s0[NL], s1[NL];
     load(s0, 0);
     load(s1, 1);
     int blk = 0;
     for (; blk + 2 < nb; blk += 2) {
-      packed_block<NL, NL, U, MT, T, F64>(s0, blk * U, n_i, acc, acc32);
+      packed_block<NL, NL, U, MT, T, F64, WF8>(s0, blk * U, n_i, acc, acc32);
       load(s0, blk + 2);
-      packed_block<NL, NL, U, MT, T, F64>(s1, (blk + 1) * U, n_i, acc, acc32);
+      packed_block<NL, NL, U, MT, T, F64, WF8>(s1, (blk + 1) * U, n_i, acc,
+                                               acc32);
       load(s1, blk + 3);
     }
-    packed_block<NL, NL, U, MT, T, F64>(s0, blk * U, n_i, acc, acc32);
-    packed_block<0, NL, U, MT, T, F64>(s1, (blk + 1) * U, n_i, acc, acc32);
+    packed_block<NL, NL, U, MT, T, F64, WF8>(s0, blk * U, n_i, acc, acc32);
+    packed_block<0, NL, U, MT, T, F64, WF8>(s1, (blk + 1) * U, n_i, acc, acc32);
   }
   if constexpr (!F64) {
 #pragma unroll
@@ -228,9 +326,12 @@ __device__ __forceinline__ void gemm_core_packed(const GemmArgs& p, int tile,
 // Sums the waves' tiles in wave order (float64, one row tile at a time
 // through redd); red[(m*4 + j)*64 + lane] then holds row 16m + 4(lane/16) + j,
 // tile column lane % 16.
+// With FP8 weights each column's sum is multiplied by its row scale before
+// the one rounding to float.
 template <int MT, int W>
 __device__ __forceinline__ void reduce_waves(const double (&acc)[MT][4],
-                                             double* redd, float* red) {
+                                             double* redd, float* red,
+                                             const float* wscale, int tile) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -241,6 +342,7 @@ __device__ __forceinline__ void reduce_waves(const double (&acc)[MT][4],
       double v = redd[idx];
 #pragma unroll
       for (int w = 1; w < W; ++w) v += redd[w * 256 + idx];
+      if (wscale != nullptr) v *= (double)wscale[tile * 16 + (idx & 15)];
       red[m * 256 + idx] = (float)v;
     }
     __syncthreads();
@@ -300,18 +402,23 @@ __device__ void apply_epilogue(const GemmArgs& p, int tile, int m_base,
 
 // PIPE: the software-pipelined core (packed A only; it holds two blocks of
 // U steps in registers, so it suits workgroups of up to 8 waves)
-template <typename T, int MT, int AP, int W, int U, bool F64, bool PIPE>
+// WF8: FP8 step-pair weights (bf16 drafters, packed A).
+template <typename T, int MT, int AP, int W, int U, bool F64, bool PIPE,
+          bool WF8>
 __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmArgs p) {
   static_assert(!PIPE || AP, "the pipelined core reads packed A");
+  static_assert(!WF8 || AP, "FP8 weights take packed A");
   __shared__ double redd[W * 256];
   __shared__ float red[MT * 256];
   const int tile = blockIdx.x, m_base = blockIdx.y * 16 * MT;
   double acc[MT][4];
   if constexpr (PIPE)
-    gemm_core_packed<T, MT, W, U, F64>(p, tile, m_base, acc);
+    gemm_core_packed<T, MT, W, U, F64, WF8>(p, tile, m_base, acc);
+  else if constexpr (WF8)
+    gemm_core_fp8<MT, W, U, F64>(p, tile, m_base, acc);
   else
     gemm_core<T, MT, AP, W, U, F64>(p, tile, m_base, acc);
-  reduce_waves<MT, W>(acc, redd, red);
+  reduce_waves<MT, W>(acc, redd, red, p.wscale, tile);
   apply_epilogue<T, MT, W>(p, tile, m_base, red);
 }
 
@@ -329,18 +436,28 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmArgs p) {
 
 // AHEAD: staging loads issued after this tile's set (the other set's, or
 // none for the last tile).  The tile is multiplied from set b; with REFILL
-// b is then reloaded with the tile two ahead, before the wave sums.
-template <typename T, int W, int NS, int AHEAD, bool REFILL, typename LoadW>
-__device__ __forceinline__ void lm_tile(const GemmArgs& p, u32x4 (&a)[NS],
-                                        u32x4 (&b)[NS], int n_i, int i,
+// b is then reloaded with the tile two ahead, before the wave sums.  With
+// WF8 each of the NB weight loads of a set is a pair of contraction steps
+// (activation fragments a[2u], a[2u + 1]); otherwise one step (a[u]).
+template <typename T, int W, int NA, int NB, int AHEAD, bool REFILL, bool WF8,
+          typename LoadW>
+__device__ __forceinline__ void lm_tile(const GemmArgs& p, u32x4 (&a)[NA],
+                                        u32x4 (&b)[NB], int n_i, int i,
                                         int tile, bool valid, double* redd,
                                         Top2& run, const LoadW& load_w) {
-  stage_wait<0, NS, AHEAD>(b);
+  stage_wait<0, NB, AHEAD>(b);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    if (s < n_i) mma16(acc, a[s], b[s], T());
+  for (int s = 0; s < NB; ++s)
+    if (s < n_i) {
+      if constexpr (WF8) {
+        mma16(acc, a[2 * s], fp8x8_to_bf16(b[s].x, b[s].y), T());
+        mma16(acc, a[2 * s + 1], fp8x8_to_bf16(b[s].z, b[s].w), T());
+      } else {
+        mma16(acc, a[s], b[s], T());
+      }
+    }
   if constexpr (REFILL) load_w(b, i + 2);
 #pragma unroll
   for (int j = 0; j < 4; ++j) redd[wave * 256 + j * 64 + lane] = (double)acc[j];
@@ -351,6 +468,7 @@ __device__ __forceinline__ void lm_tile(const GemmArgs& p, u32x4 (&a)[NS],
     double v = redd[idx];
 #pragma unroll
     for (int w = 1; w < W; ++w) v += redd[w * 256 + idx];
+    if (p.wscale != nullptr) v *= (double)p.wscale[tile * 16 + (idx & 15)];
     const float z = (float)v;
     const int row = 4 * ((idx & 63) >> 4) + (idx >> 6);
     const int col = tile * 16 + (idx & 15);
@@ -367,54 +485,65 @@ __device__ __forceinline__ void lm_tile(const GemmArgs& p, u32x4 (&a)[NS],
   }
 }
 
-template <typename T, int W, int NS>
+// NS: the most contraction steps a wave holds.  A wave's units (steps, or
+// with WF8 pairs of steps) are wave, wave + W, ...
+template <typename T, int W, int NS, bool WF8>
 __global__ __launch_bounds__(64 * W) void lm_head_kernel(GemmArgs p) {
   constexpr int KC = Storage<T>::KC;
+  constexpr int NB = WF8 ? NS / 2 : NS;  // weight loads per tile per wave
   __shared__ double redd[2][W * 256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nsteps = p.Kd / KC;
+  const int nunits = WF8 ? nsteps / 2 : nsteps;
   const int ntiles = p.N / 16, P = gridDim.x, wg = blockIdx.x;
   // tiles wg, wg + P, ...: the workgroups sweep the matrix together
   const int nt = (ntiles - 1 - wg) / P + 1;  // >= 1: P <= ntiles
   auto tile_of = [&](int i) { return wg + min(i, nt - 1) * P; };
-  // this wave's steps: wave, wave + W, ... (n_i of them, n_i <= NS)
-  const int n_i = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;
-  const int64_t step_off = (int64_t)wave * 1024 + lane * 16;
-  // a step past the wave's last repeats the last (a wave with no steps
-  // reads step 0), a slot past the last tile repeats the last tile; neither
+  // this wave's units: wave, wave + W, ... (n_i of them, n_i <= NB)
+  const int n_i = wave < nunits ? (nunits - 1 - wave) / W + 1 : 0;
+  const int64_t unit_off = (int64_t)wave * 1024 + lane * 16;
+  // a unit past the wave's last repeats the last (a wave with no units
+  // reads unit 0), a slot past the last tile repeats the last tile; neither
   // is multiplied or summed
-  auto load_w = [&](u32x4(&b)[NS], int i) {  // this workgroup's i-th tile
+  auto load_w = [&](u32x4(&b)[NB], int i) {  // this workgroup's i-th tile
     const char* wt = static_cast<const char*>(p.w) +
-                     (int64_t)tile_of(i) * nsteps * 1024 + step_off;
+                     (int64_t)tile_of(i) * nunits * 1024 + unit_off;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NB; ++s)
       b[s] = stage_load(wt + (int64_t)min(s, max(n_i - 1, 0)) * W * 1024);
   };
-  u32x4 a[NS], b0[NS], b1[NS];
+  u32x4 a[NS], b0[NB], b1[NB];
   {
-    const char* at = static_cast<const char*>(p.a_ptr[0]) + step_off;
+    const char* at = static_cast<const char*>(p.a_ptr[0]) + lane * 16;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      a[s] = stage_load(at + (int64_t)min(s, max(n_i - 1, 0)) * W * 1024);
+    for (int s = 0; s < NB; ++s) {
+      const int64_t unit = wave + (int64_t)min(s, max(n_i - 1, 0)) * W;
+      if constexpr (WF8) {
+        a[2 * s] = stage_load(at + (2 * unit) * 1024);
+        a[2 * s + 1] = stage_load(at + (2 * unit + 1) * 1024);
+      } else {
+        a[s] = stage_load(at + unit * 1024);
+      }
+    }
   }
   load_w(b0, 0);
   load_w(b1, 1);
-  stage_wait<0, NS, 2 * NS>(a);
+  stage_wait<0, NS, 2 * NB>(a);
   Top2 run = top2_empty();
   int i = 0;
   for (; i + 2 < nt; i += 2) {
-    lm_tile<T, W, NS, NS, true>(p, a, b0, n_i, i, tile_of(i), true, redd[0],
-                                run, load_w);
-    lm_tile<T, W, NS, NS, true>(p, a, b1, n_i, i + 1, tile_of(i + 1), true,
-                                redd[1], run, load_w);
+    lm_tile<T, W, NS, NB, NB, true, WF8>(p, a, b0, n_i, i, tile_of(i), true,
+                                         redd[0], run, load_w);
+    lm_tile<T, W, NS, NB, NB, true, WF8>(p, a, b1, n_i, i + 1, tile_of(i + 1),
+                                         true, redd[1], run, load_w);
   }
-  lm_tile<T, W, NS, NS, false>(p, a, b0, n_i, i, tile_of(i), true, redd[0],
-                               run, load_w);
+  lm_tile<T, W, NS, NB, NB, false, WF8>(p, a, b0, n_i, i, tile_of(i), true,
+                                        redd[0], run, load_w);
   // the second set was loaded whether or not its tile exists: wait for it
   // either way (only its sums are skipped)
-  lm_tile<T, W, NS, 0, false>(p, a, b1, n_i, i + 1, tile_of(i + 1), i + 1 < nt,
-                              redd[1], run, load_w);
+  lm_tile<T, W, NS, NB, 0, false, WF8>(p, a, b1, n_i, i + 1, tile_of(i + 1),
+                                       i + 1 < nt, redd[1], run, load_w);
   if (threadIdx.x < 256 && (threadIdx.x & 15) == 0) {
     const int row = 4 * ((threadIdx.x & 63) >> 4) + (threadIdx.x >> 6);
     if (row < p.M) p.top2[(int64_t)row * P + wg] = run;
@@ -442,23 +571,67 @@ __global__ void pack_kernel(PackArgs a) {
   }
 }
 
-template <typename T, int AP>
+// FP8 E4M3 codes [N][K] (1 byte each): PACK_FP8 writes the step-pair layout
+// (one 16-byte chunk per thread: 8 codes of each step of a pair);
+// PACK_FP8_BF16 writes the bf16 layout with every code widened exactly.
+__global__ void pack_fp8_kernel(PackArgs a) {
+  const bool pairs = a.mode == PACK_FP8;
+  const int units = pairs ? a.K / 64 : a.K / 32;
+  const int64_t total = (int64_t)a.N / 16 * units * 64;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(q & 63);
+    const int64_t ts = q >> 6;
+    const int s = (int)(ts % units), t = (int)(ts / units);
+    const int row = map_col(a.cmap, a.pair_group, a.pair_off, t, l & 15);
+    int sg = 0;
+    while (sg + 1 < a.nseg && row >= a.n0[sg + 1]) ++sg;
+    const unsigned char* src = static_cast<const unsigned char*>(a.src[sg]) +
+                               (int64_t)(row - a.n0[sg]) * a.K;
+    u32x4 v;
+    if (pairs) {
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(src + s * 64 + (l >> 4) * 8);
+      const u32x2 hi =
+          *reinterpret_cast<const u32x2*>(src + s * 64 + 32 + (l >> 4) * 8);
+      v = u32x4{lo.x, lo.y, hi.x, hi.y};
+    } else {
+      const u32x2 c = *reinterpret_cast<const u32x2*>(src + s * 32 + (l >> 4) * 8);
+      v = fp8x8_to_bf16(c.x, c.y);
+    }
+    *reinterpret_cast<u32x4*>(static_cast<char*>(a.dst) + q * 16) = v;
+  }
+}
+
+// Per-row scales (float) into packed column order: dst[16 t + c].
+__global__ void pack_scale_kernel(PackArgs a) {
+  const int n = a.N;
+  for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < n;
+       q += gridDim.x * blockDim.x) {
+    const int row = map_col(a.cmap, a.pair_group, a.pair_off, q >> 4, q & 15);
+    int sg = 0;
+    while (sg + 1 < a.nseg && row >= a.n0[sg + 1]) ++sg;
+    static_cast<float*>(a.dst)[q] =
+        static_cast<const float*>(a.src[sg])[row - a.n0[sg]];
+  }
+}
+
+template <typename T, int AP, bool WF8>
 hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream_t s) {
   dim3 grid(pl.gx, pl.gy, 1), block(pl.waves * 64);
   if (pl.MT == 1 && a.ep == EP_TOP2)
-    launch_k(
-        (gemm_kernel<T, 1, AP, DFLASH_LM_W, DFLASH_LM_U, false, false>), grid,
-        block, 0, s, a);
+    launch_k((gemm_kernel<T, 1, AP, DFLASH_LM_W, DFLASH_LM_U, false, false,
+                          WF8>),
+             grid, block, 0, s, a);
   else if (pl.MT == 1)
-    launch_k((gemm_kernel<T, 1, AP, DFLASH_GEMM_W, DFLASH_GEMM_U,
-                                    true, AP == 1>),
-                       grid, block, 0, s, a);
+    launch_k((gemm_kernel<T, 1, AP, DFLASH_GEMM_W, DFLASH_GEMM_U, true,
+                          AP == 1, WF8>),
+             grid, block, 0, s, a);
   else if (pl.MT == 2)
-    launch_k((gemm_kernel<T, 2, AP, 4, 8, true, false>), grid, block,
-                       0, s, a);
+    launch_k((gemm_kernel<T, 2, AP, 4, 8, true, false, WF8>), grid, block, 0,
+             s, a);
   else if (pl.MT == 4)
-    launch_k((gemm_kernel<T, 4, AP, 16, 2, true, false>), grid,
-                       block, 0, s, a);
+    launch_k((gemm_kernel<T, 4, AP, 16, 2, true, false, WF8>), grid, block,
+             0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -478,11 +651,16 @@ GemmPlan plan_gemm(int M, int N, bool lm_head) {
 
 hipError_t launch_gemm(bool bf16, const GemmPlan& pl, const GemmArgs& a,
                        hipStream_t s) {
+  if (a.wfp8) {
+    // FP8 step pairs: bf16 activations, packed, contraction in whole pairs
+    if (!bf16 || !a.a_packed || a.Kd % 64 != 0) return hipErrorInvalidValue;
+    return launch_gemm_t<bf16_t, 1, true>(pl, a, s);
+  }
   if (bf16)
-    return a.a_packed ? launch_gemm_t<bf16_t, 1>(pl, a, s)
-                      : launch_gemm_t<bf16_t, 0>(pl, a, s);
-  return a.a_packed ? launch_gemm_t<float, 1>(pl, a, s)
-                    : launch_gemm_t<float, 0>(pl, a, s);
+    return a.a_packed ? launch_gemm_t<bf16_t, 1, false>(pl, a, s)
+                      : launch_gemm_t<bf16_t, 0, false>(pl, a, s);
+  return a.a_packed ? launch_gemm_t<float, 1, false>(pl, a, s)
+                    : launch_gemm_t<float, 0, false>(pl, a, s);
 }
 
 constexpr int kLmW = DFLASH_LMP_W, kLmNS = DFLASH_LMP_NS;
@@ -496,26 +674,42 @@ int lm_head_parts(bool bf16, int M, int N, int Kd, int num_cu) {
 hipError_t launch_lm_head(bool bf16, int parts, const GemmArgs& a,
                           hipStream_t s) {
   if (parts <= 0 || !a.a_packed) return hipErrorInvalidValue;
-  if (bf16)
-    launch_k((lm_head_kernel<bf16_t, kLmW, kLmNS>), dim3(parts),
-                       dim3(64 * kLmW), 0, s, a);
-  else
-    launch_k((lm_head_kernel<float, kLmW, kLmNS>), dim3(parts),
-                       dim3(64 * kLmW), 0, s, a);
+  if (a.wfp8) {
+    if (!bf16 || a.Kd % 64 != 0) return hipErrorInvalidValue;
+    launch_k((lm_head_kernel<bf16_t, kLmW, kLmNS, true>), dim3(parts),
+             dim3(64 * kLmW), 0, s, a);
+  } else if (bf16) {
+    launch_k((lm_head_kernel<bf16_t, kLmW, kLmNS, false>), dim3(parts),
+             dim3(64 * kLmW), 0, s, a);
+  } else {
+    launch_k((lm_head_kernel<float, kLmW, kLmNS, false>), dim3(parts),
+             dim3(64 * kLmW), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_pack(bool bf16, const PackArgs& a, hipStream_t s) {
+  if (a.mode == PACK_SCALE) {
+    launch_k(pack_scale_kernel, dim3((a.N + 255) / 256), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  if (a.mode == PACK_FP8 || a.mode == PACK_FP8_BF16) {
+    if (!bf16 || a.K % 64 != 0) return hipErrorInvalidValue;
+    const int64_t chunks =
+        (int64_t)a.N / 16 * (a.mode == PACK_FP8 ? a.K / 64 : a.K / 32) * 64;
+    int64_t blocks = (chunks + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    launch_k(pack_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const int E = bf16 ? Storage<bf16_t>::E : Storage<float>::E;
   const int64_t chunks = (int64_t)a.N * a.K / E;
   int64_t blocks = (chunks + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (bf16)
-    launch_k(pack_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0,
-                       s, a);
+    launch_k(pack_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
-    launch_k(pack_kernel<float>, dim3((unsigned)blocks), dim3(256), 0,
-                       s, a);
+    launch_k(pack_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -291,6 +291,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
   // the block's sums there, then run the epilogue over whole rows.
   __syncthreads();
   float* L = reinterpret_cast<float*>(lds);  // [BM][BN + 1]
+  // FP8 weights: each column's sum times its row scale (one float rounding)
+  float sc[TN];
+#pragma unroll
+  for (int n = 0; n < TN; ++n) {
+    const int col = nb * BN + (wn * TN + n) * 32 + (lane & 31);
+    sc[n] = (p.wscale != nullptr && col < p.N) ? p.wscale[col] : 1.f;
+  }
 #pragma unroll
   for (int m = 0; m < TM; ++m)
 #pragma unroll
@@ -300,7 +307,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
         const int r = (wm * TM + m) * 32 + 4 * (lane >> 5) + 8 * (j >> 2) +
                       (j & 3);
         const int c = (wn * TN + n) * 32 + (lane & 31);
-        L[r * (BN + 1) + c] = acc[m][n][j];
+        L[r * (BN + 1) + c] =
+            p.wscale != nullptr ? acc[m][n][j] * sc[n] : acc[m][n][j];
       }
   __syncthreads();
   if (p.ep == EP_TOP2)
@@ -443,7 +451,8 @@ int tiled_blocks(int cfg, int M, int N) {
 
 hipError_t launch_gemm_tiled(bool bf16, int cfg, const GemmArgs& a,
                              int ksplit, hipStream_t s) {
-  if (!bf16) return hipErrorInvalidValue;  // fp32 drafters use gemm_kernel
+  // fp32 drafters use gemm_kernel; FP8 weights come here widened to bf16
+  if (!bf16 || a.wfp8) return hipErrorInvalidValue;
   // every split needs at least one contraction step
   if (ksplit < 1 || ksplit > a.Kd / Storage<bf16_t>::KC ||
       (ksplit > 1 && a.ep != EP_STORE))

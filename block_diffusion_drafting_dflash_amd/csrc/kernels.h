@@ -55,6 +55,20 @@ __host__ __device__ __forceinline__ int64_t packed_offset(int row, int k,
          (int64_t)(k % E) * (int64_t)sizeof(T);
 }
 
+// FP8 E4M3 weights (bf16 drafters) are packed in pairs of contraction steps:
+// fragment (column tile t, pair s) is 16 columns x 64 contraction elements in
+// 1 KiB, lane l holding column l % 16 with bytes 0-7 = elements
+// 64s + 8(l/16) .. +8 and bytes 8-15 = elements 64s + 32 + 8(l/16) .. +8, so
+// one 16-byte load per lane feeds two bf16 MFMA steps (fp8x8_to_bf16 of each
+// half gives the step's bf16 fragment).  Each output column's scale is
+// stored in packed column order: scale[16 t + c] for column c of tile t.
+__host__ __device__ __forceinline__ int64_t packed_offset_fp8(int row, int k,
+                                                              int K) {
+  const int t = row >> 4, r = row & 15, s = k / 64, h = (k % 64) / 32,
+            g = (k % 32) / 8;
+  return (((int64_t)t * (K / 64) + s) * 64 + g * 16 + r) * 16 + h * 8 + k % 8;
+}
+
 // Column order inside packed weight tiles.
 enum ColMap : int {
   MAP_LINEAR = 0,  // tile t = output columns [16t, 16t + 16)
@@ -121,6 +135,10 @@ struct GemmArgs {
   int a_seg_k;      // row-major A: contraction width of each segment
   int a_packed;
   const void* w;    // packed weights [N rows][Kd]
+  int wfp8;         // w holds FP8 E4M3 step pairs (packed_offset_fp8)
+  const float* wscale;  // per output column, packed column order, or null
+  const void* w_tiled;  // host side: the bf16 layout of FP8 weights (codes
+                        // widened) for the tiled kernels, or null
   int M, N, Kd;
   int cmap, pair_group, pair_off;
   // epilogue
@@ -193,11 +211,18 @@ hipError_t launch_pack_act(bool bf16, const GemmArgs& a, void* dst,
 
 // Packs rows of up to kMaxBSeg row-major segments [n_s][K] (concatenated
 // along rows) into dst with the given column map.
+// Modes: PACK_SAME copies elements of the storage type; PACK_FP8 packs
+// 1-byte E4M3 codes into step pairs; PACK_FP8_BF16 widens E4M3 codes to bf16
+// in the bf16 layout; PACK_SCALE writes one float per row (the source
+// segments are float vectors) in packed column order.
+enum PackMode : int { PACK_SAME = 0, PACK_FP8 = 1, PACK_FP8_BF16 = 2,
+                      PACK_SCALE = 3 };
 struct PackArgs {
   const void* src[kMaxBSeg];
   int n0[kMaxBSeg + 1];
   int nseg;
   int N, K, cmap, pair_group, pair_off;
+  int mode;
   void* dst;
 };
 hipError_t launch_pack(bool bf16, const PackArgs& a, hipStream_t s);

@@ -73,6 +73,22 @@ typedef enum {
 
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
+/* Storage of the projection matrices (fc, wq, wk, wv, wo, w_gate, w_up,
+ * w_down, lm_head).  DFLASH_WEIGHTS_DTYPE: the config dtype.
+ * DFLASH_WEIGHTS_FP8_E4M3 (bf16 drafters): one byte per element, the OCP
+ * FP8 E4M3 code (1 sign, 4 exponent bits of bias 7, 3 mantissa bits; codes
+ * 0x7F/0xFF are NaN and must not occur), with one fp32 scale per output
+ * row: W[j][k] = scale[j] * value(code[j][k]).  Activations stay bf16 and
+ * every row's sum is scaled once, in fp32 or wider, before it is stored.
+ * The embedding and the norm gains stay in the config dtype.  This is the
+ * FP8 drafter-weight execution of "DFlash Guide", section "Production
+ * Benchmarks on NVIDIA Blackwell B200" (FP4/FP8 mixed execution; the page
+ * fixes no format, this is the reading taken). */
+typedef enum {
+  DFLASH_WEIGHTS_DTYPE = 0,
+  DFLASH_WEIGHTS_FP8_E4M3 = 1
+} dflash_weight_format;
+
 /* Device error word bits (dflash_check_device_errors). */
 #define DFLASH_DEVERR_TOKEN    0x1  /* token id outside [0, vocab), or a drafted position whose logits had no finite maximum (id -1) */
 #define DFLASH_DEVERR_CTX_LEN  0x2  /* context length outside [0, max_ctx_len] */
@@ -83,7 +99,8 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 /* Drafter shape and capacities.  Supported: block_size == 16; head_dim 64 or
  * 128; num_q_heads equal to 2, 4 or 8 times num_kv_heads; hidden,
  * intermediate, target_hidden and num_q_heads*head_dim multiples of 64;
- * vocab a multiple of 16.  Anything else returns DFLASH_E_UNSUPPORTED. */
+ * vocab a multiple of 16; FP8 weights with a bf16 dtype only.  Anything
+ * else returns DFLASH_E_UNSUPPORTED. */
 typedef struct {
   int32_t num_layers;        /* N_l draft layers */
   int32_t hidden;            /* D */
@@ -102,14 +119,18 @@ typedef struct {
   int32_t max_inject_rows;   /* max rows T per dflash_inject_kv call */
   float rope_theta;          /* RoPE base */
   float rms_eps;             /* RMSNorm epsilon */
+  int32_t weight_format;     /* dflash_weight_format of the projections */
 } dflash_config;
 
 /* Drafter weights, PyTorch Linear layout [out, in], row-major, dtype of the
- * config.  Per-layer entries are HOST arrays of num_layers DEVICE pointers.
- * dflash_create copies every projection matrix (fc, wq, wk, wv, wo, w_gate,
- * w_up, w_down, lm_head) into the context's own fragment-major layout and
- * never reads them again; embed and the norm gains are read in place and
- * must stay alive and unchanged until dflash_destroy. */
+ * config (projections: see weight_format).  Per-layer entries are HOST
+ * arrays of num_layers DEVICE pointers.  dflash_create copies every
+ * projection matrix (fc, wq, wk, wv, wo, w_gate, w_up, w_down, lm_head) and
+ * its scales into the context's own fragment-major layout and never reads
+ * them again; embed and the norm gains are read in place and must stay
+ * alive and unchanged until dflash_destroy.  The *_scale entries are read
+ * only with FP8 weights ([out] fp32 each; 4-byte aligned) and are ignored
+ * (may be NULL) otherwise. */
 typedef struct {
   const void* embed;        /* [V, D] */
   const void* fc;           /* [D, n_t * D_t]: fuses the concatenated layers */
@@ -125,6 +146,15 @@ typedef struct {
   const void* const* w_down;     /* [D, I]     per layer */
   const void* final_norm;   /* [D] */
   const void* lm_head;      /* [V, D] */
+  const float* fc_scale;              /* [D] */
+  const float* const* wq_scale;       /* [Hq*d]  per layer */
+  const float* const* wk_scale;       /* [Hkv*d] per layer */
+  const float* const* wv_scale;       /* [Hkv*d] per layer */
+  const float* const* wo_scale;       /* [D]     per layer */
+  const float* const* w_gate_scale;   /* [I]     per layer */
+  const float* const* w_up_scale;     /* [I]     per layer */
+  const float* const* w_down_scale;   /* [D]     per layer */
+  const float* lm_head_scale;         /* [V] */
 } dflash_weights;
 
 typedef struct dflash_ctx dflash_ctx;

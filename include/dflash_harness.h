@@ -30,6 +30,13 @@ int dflash_harness_synth_target(void* stream, int32_t batch, int32_t block_size,
                                 const int32_t* tail, const float* p,
                                 int32_t* target);
 
+/* The drafting kernels' FP8 E4M3 -> bf16 widening applied to n codes
+ * (n a multiple of 8; codes 8-byte aligned, out 16-byte aligned), so a test
+ * can check it on every code: out[k] = bf16 bits of value(codes[k]).
+ * Returns 0, -1 on a bad argument, -4 on a HIP launch error. */
+int dflash_harness_fp8_to_bf16(void* stream, int32_t n, const uint8_t* codes,
+                               uint16_t* out);
+
 #ifdef __cplusplus
 }
 #endif

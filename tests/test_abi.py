@@ -109,6 +109,7 @@ def good_config(**kw):
     ("rope_theta", 0.0, "DFLASH_E_INVALID", "rope_theta"),
     ("num_target_layers", 9, "DFLASH_E_UNSUPPORTED", "num_target_layers"),
     ("mask_token_id", 4000, "DFLASH_E_INVALID", None),
+    ("weight_format", 2, "DFLASH_E_INVALID", "weight_format"),
 ])
 def test_create_rejects_bad_config(field, value, status, msg):
     cfg = good_config(**{field: value})
@@ -118,6 +119,54 @@ def test_create_rejects_bad_config(field, value, status, msg):
     assert out.value is None
     if msg:
         assert msg in last_error()
+
+
+def _fake_weights(wl, scales):
+    """Non-null, aligned stand-in pointers (never dereferenced: validation
+    fails before any device work)."""
+    n = wl.num_layers
+    keep = []
+
+    def lst(v):
+        arr = (ctypes.c_void_p * n)(*([v] * n))
+        keep.append(arr)
+        return ctypes.cast(arr, binding._PP)
+
+    w = binding.Weights(embed=4096, fc=4096, hidden_norm=4096,
+                        final_norm=4096, lm_head=4096)
+    for k in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate",
+              "w_up", "w_down"):
+        setattr(w, k, lst(4096))
+    if scales:
+        w.fc_scale = 4096
+        w.lm_head_scale = 4096
+        for k in binding.LAYER_MATRICES:
+            setattr(w, k + "_scale", lst(4096))
+    return w, keep
+
+
+def test_create_rejects_fp8_without_scales_and_fp8_f32():
+    wl = W.small_bf16(weight_format="fp8")
+    cfg = binding.make_config(wl)
+    assert cfg.weight_format == 1
+    out = ctypes.c_void_p()
+    w, keep = _fake_weights(wl, scales=False)
+    st = lib().dflash_create(ctypes.byref(cfg), ctypes.byref(w),
+                             ctypes.byref(out))
+    assert binding.STATUS[st] == "DFLASH_E_INVALID"
+    assert "FP8 weights" in last_error()
+    w, keep2 = _fake_weights(wl, scales=True)
+    w.wk_scale[1] = 4098  # misaligned scale vector of one layer
+    st = lib().dflash_create(ctypes.byref(cfg), ctypes.byref(w),
+                             ctypes.byref(out))
+    assert binding.STATUS[st] == "DFLASH_E_INVALID"
+    assert "wk_scale[1]" in last_error()
+    f32 = binding.make_config(W.WORKLOADS["tiny-f32"].replace(
+        weight_format="fp8"))
+    st = lib().dflash_create(ctypes.byref(f32), ctypes.byref(w),
+                             ctypes.byref(out))
+    assert binding.STATUS[st] == "DFLASH_E_UNSUPPORTED"
+    assert out.value is None
 
 
 def test_create_rejects_null_weights_and_out():

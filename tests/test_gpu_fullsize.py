@@ -39,7 +39,8 @@ pytestmark = pytest.mark.gpu
 
 dfl = pytest.importorskip("block_diffusion_drafting_dflash_amd")
 
-FULL = [n for n in W.WORKLOAD_ORDER if W.WORKLOADS[n].dtype == "bf16"]
+FULL = [n for n in W.WORKLOAD_ORDER if W.WORKLOADS[n].dtype == "bf16"] + \
+    W.EXTRA_WORKLOADS
 
 
 def sample_seqs(lens):
