@@ -33,6 +33,8 @@ from .numerics import (round_bf16, identity_round, rms_norm, silu, rope,
 from .drafter import (OracleModel, fuse_features, inject_kv, inject_rows,
                       block_attention, decoder_layer, lm_head_reduce,
                       confidence_commit, draft_sequence, draft_batch)
+from .target import (TargetModel, target_forward, greedy_stream,
+                     speculative_loop)
 from .verify import (verify_greedy, verify_sampling, sample_inverse_cdf,
                      synthetic_target, expected_accept_len,
                      latency_per_token, simulate_rounds, toy_race_ratio,
@@ -45,4 +47,5 @@ __all__ = [
     "confidence_commit", "draft_sequence", "draft_batch", "verify_greedy",
     "synthetic_target", "expected_accept_len", "latency_per_token",
     "simulate_rounds", "toy_race_ratio", "simulate_toy_race",
+    "TargetModel", "target_forward", "greedy_stream", "speculative_loop",
 ]

@@ -284,3 +284,28 @@ def to_f64(t) -> np.ndarray:
     if isinstance(t, np.ndarray):
         return t.astype(np.float64)
     return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+
+
+def gen_target_weights(wl: Workload, device="cpu", std: float = 0.02):
+    """Seeded weights of the small stand-in target model whose hooked layers
+    feed the drafter: embedding [V, D_t], n_t residual layers [D_t, D_t]
+    with RMSNorm gains U(0.5, 1.5), greedy head [V, D_t]; bf16 values."""
+    Dt, V, nt = wl.target_hidden, wl.vocab, wl.num_target_layers
+    bf = lambda t: t.to(torch.bfloat16)
+    return {
+        "embed": bf(normal(wl, "target-embed", (V, Dt), 1.0, device)
+                    .float()),
+        "layers": [bf(normal(wl, "target-layer", (Dt, Dt), std, device,
+                             index=k).float()) for k in range(nt)],
+        "gains": [bf(uniform_gains(wl, f"target-gain{k}", Dt, device)
+                     .float()) for k in range(nt)],
+        "head": bf(normal(wl, "target-head", (V, Dt), std, device).float()),
+        "eps": wl.rms_eps,
+    }
+
+
+def gen_prompt(wl: Workload, length: int, index: int = 0) -> np.ndarray:
+    """Seeded prompt token ids in [0, V - 2] (the mask id never occurs)."""
+    rng = np.random.default_rng(_seed(wl.seed, "prompt", index))
+    return rng.integers(0, wl.vocab - 1, size=length,
+                        dtype=np.int64).astype(np.int32)
