@@ -34,7 +34,8 @@ LIB_SYMBOLS = ["dflash_create", "dflash_destroy", "dflash_kv_cache_bytes",
                "dflash_draft_block_noalloc"]
 TIME_KIND = {"off": 0, "lmhead": 1, "attention": 2, "gemm": 3}
 HARNESS_SYMBOLS = ["dflash_harness_synth_target",
-                   "dflash_harness_fp8_to_bf16"]
+                   "dflash_harness_fp8_to_bf16",
+                   "dflash_harness_target_forward"]
 
 
 class DFlashError(RuntimeError):
@@ -136,6 +137,10 @@ def load_harness():
     h.dflash_harness_synth_target.restype = ctypes.c_int
     h.dflash_harness_fp8_to_bf16.argtypes = [vp, i32, vp, vp]
     h.dflash_harness_fp8_to_bf16.restype = ctypes.c_int
+    h.dflash_harness_target_forward.argtypes = [
+        vp, i32, i32, i32, i32, vp, vp, _PP, _PP, vp, ctypes.c_float, _PP,
+        ctypes.c_int64, vp, vp]
+    h.dflash_harness_target_forward.restype = ctypes.c_int
     _harness = h
     return h
 
@@ -373,6 +378,32 @@ def fp8_to_bf16(codes: torch.Tensor, stream=None) -> torch.Tensor:
     if st != 0:
         raise RuntimeError(f"dflash_harness_fp8_to_bf16 failed ({st})")
     return out
+
+
+def target_forward(tw, tokens: torch.Tensor, hooks=None, stream=None):
+    """The harness's stand-in target over int32 `tokens` [rows]: returns
+    (hooks: list of n_t bf16 [rows, D_t], next token [rows] int32, margin
+    [rows] fp32).  tw: gen_target_weights' dict on the device."""
+    h = load_harness()
+    rows = tokens.numel()
+    V, Dt = tw["embed"].shape
+    nt = len(tw["layers"])
+    dev = tokens.device
+    if hooks is None:
+        hooks = [torch.empty(rows, Dt, dtype=torch.bfloat16, device=dev)
+                 for _ in range(nt)]
+    nxt = torch.empty(rows, dtype=torch.int32, device=dev)
+    margin = torch.empty(rows, dtype=torch.float32, device=dev)
+    arr = lambda ts: ctypes.cast((ctypes.c_void_p * nt)(
+        *[t.data_ptr() for t in ts]), _PP)
+    st = h.dflash_harness_target_forward(
+        _stream(stream), rows, nt, Dt, V, _ptr(tokens), _ptr(tw["embed"]),
+        arr(tw["layers"]), arr(tw["gains"]), _ptr(tw["head"]),
+        float(tw["eps"]), arr(hooks), hooks[0].stride(0), _ptr(nxt),
+        _ptr(margin))
+    if st != 0:
+        raise RuntimeError(f"dflash_harness_target_forward failed ({st})")
+    return hooks, nxt, margin
 
 
 def synth_target(draft, u, r, tail, p, vocab, target=None, stream=None):

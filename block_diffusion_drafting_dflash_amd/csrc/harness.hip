@@ -34,7 +34,154 @@ __global__ void synth_target_kernel(int B, int K, int V, const int32_t* draft,
   target[idx] = u[o] < p[j] ? dj : (int)(((int64_t)dj + 1 + r[o]) % V);
 }
 
+// The stand-in target model, one workgroup of 4 waves per position:
+//   x_0 = E[token]; x_k = bf16(RMSNorm(x_{k-1} + W_k x_{k-1}) * g_k) for the
+//   n_t hooked layers; next = argmax(W_o x_{n_t}), lowest id on ties.
+// A wave computes one output at a time: lanes take every 64th contraction
+// element in order, then a fixed butterfly, so a position's values do not
+// depend on which other positions share the launch.  Norm statistics and
+// the scaling are float64 with one rounding to bf16.
+constexpr int kTgtMaxHooks = 8;
+struct TargetArgs {
+  const void* layers[kTgtMaxHooks];
+  const void* gains[kTgtMaxHooks];
+  void* hooks[kTgtMaxHooks];
+  int nt, Dt, V;
+  int64_t ld;
+  float eps;
+  const int32_t* tokens;
+  const void* embed;
+  const void* head;
+  int32_t* next;
+  float* margin;
+};
+
+__device__ __forceinline__ float bf(const unsigned short* p, int64_t i) {
+  return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+__device__ __forceinline__ float row_dot(const unsigned short* w,
+                                         const float* x, int n, int lane) {
+  float acc = 0.f;
+  for (int i = lane; i < n; i += 64) acc += bf(w, i) * x[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  return acc;
+}
+
+__global__ __launch_bounds__(256) void target_kernel(TargetArgs a) {
+  extern __shared__ float sm[];
+  float* x = sm;           // [Dt]
+  float* u = sm + a.Dt;    // [Dt]
+  __shared__ double red[4];
+  __shared__ float bm1[4], bm2[4];
+  __shared__ int bi1[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int Dt = a.Dt;
+  int tok = a.tokens[row];
+  tok = min(max(tok, 0), a.V - 1);
+  const unsigned short* E =
+      static_cast<const unsigned short*>(a.embed) + (int64_t)tok * Dt;
+  for (int j = tid; j < Dt; j += 256) x[j] = bf(E, j);
+  __syncthreads();
+  for (int k = 0; k < a.nt; ++k) {
+    const unsigned short* W = static_cast<const unsigned short*>(a.layers[k]);
+    for (int j = wave; j < Dt; j += 4) {
+      const float d = row_dot(W + (int64_t)j * Dt, x, Dt, lane);
+      if (lane == 0) u[j] = x[j] + d;
+    }
+    __syncthreads();
+    double ss = 0.0;
+    for (int j = tid; j < Dt; j += 256) ss += (double)u[j] * u[j];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    const double inv =
+        1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / Dt + (double)a.eps);
+    const unsigned short* g = static_cast<const unsigned short*>(a.gains[k]);
+    unsigned short* h =
+        static_cast<unsigned short*>(a.hooks[k]) + (int64_t)row * a.ld;
+    for (int j = tid; j < Dt; j += 256) {
+      const uint32_t b = dflash::f64_to_bf16((double)u[j] * inv * bf(g, j));
+      h[j] = (unsigned short)b;
+      x[j] = __uint_as_float(b << 16);
+    }
+    __syncthreads();
+  }
+  // greedy head: per wave (max, lowest index of the max, second max)
+  const unsigned short* Wo = static_cast<const unsigned short*>(a.head);
+  float m1 = -INFINITY, m2 = -INFINITY;
+  int i1 = 0x7fffffff;
+  for (int v = wave; v < a.V; v += 4) {
+    const float z = row_dot(Wo + (int64_t)v * Dt, x, Dt, lane);
+    if (z > m1) {
+      m2 = m1;
+      m1 = z;
+      i1 = v;
+    } else if (z > m2) {
+      m2 = z;
+    }
+  }
+  if (lane == 0) {
+    bm1[wave] = m1;
+    bm2[wave] = m2;
+    bi1[wave] = i1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float t1 = bm1[0], t2 = bm2[0];
+    int ti = bi1[0];
+    for (int w = 1; w < 4; ++w) {
+      const bool wins = bm1[w] > t1 || (bm1[w] == t1 && bi1[w] < ti);
+      if (wins) {
+        t2 = fmaxf(t1, bm2[w]);
+        t1 = bm1[w];
+        ti = bi1[w];
+      } else {
+        t2 = fmaxf(t2, bm1[w]);
+      }
+    }
+    a.next[row] = ti;
+    if (a.margin) a.margin[row] = t1 - t2;
+  }
+}
+
 }  // namespace
+
+extern "C" int dflash_harness_target_forward(
+    void* stream, int32_t rows, int32_t num_hooks, int32_t hidden,
+    int32_t vocab, const int32_t* tokens, const void* embed,
+    const void* const* layers, const void* const* gains, const void* head,
+    float eps, void* const* hooks, int64_t ld, int32_t* next_token,
+    float* margin) {
+  if (rows < 1 || num_hooks < 1 || num_hooks > kTgtMaxHooks || hidden < 64 ||
+      hidden > 4096 || vocab < 2 || ld < hidden || !tokens || !embed ||
+      !layers || !gains || !head || !hooks || !next_token)
+    return -1;
+  TargetArgs a{};
+  for (int k = 0; k < num_hooks; ++k) {
+    if (!layers[k] || !gains[k] || !hooks[k]) return -1;
+    a.layers[k] = layers[k];
+    a.gains[k] = gains[k];
+    a.hooks[k] = hooks[k];
+  }
+  a.nt = num_hooks;
+  a.Dt = hidden;
+  a.V = vocab;
+  a.ld = ld;
+  a.eps = eps;
+  a.tokens = tokens;
+  a.embed = embed;
+  a.head = head;
+  a.next = next_token;
+  a.margin = margin;
+  hipLaunchKernelGGL(target_kernel, dim3(rows), dim3(256),
+                     2 * hidden * sizeof(float),
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
 
 extern "C" int dflash_harness_synth_target(void* stream, int32_t batch,
                                            int32_t block_size, int32_t vocab,

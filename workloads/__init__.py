@@ -286,10 +286,13 @@ def to_f64(t) -> np.ndarray:
     return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
 
 
-def gen_target_weights(wl: Workload, device="cpu", std: float = 0.02):
+def gen_target_weights(wl: Workload, device="cpu", std: float = 0.02,
+                       head_std: float = 0.1):
     """Seeded weights of the small stand-in target model whose hooked layers
     feed the drafter: embedding [V, D_t], n_t residual layers [D_t, D_t]
-    with RMSNorm gains U(0.5, 1.5), greedy head [V, D_t]; bf16 values."""
+    with RMSNorm gains U(0.5, 1.5), greedy head [V, D_t]; bf16 values.  The
+    head's scale puts logits at a few units, as a trained head's are, so
+    near ties between its top two tokens are rare."""
     Dt, V, nt = wl.target_hidden, wl.vocab, wl.num_target_layers
     bf = lambda t: t.to(torch.bfloat16)
     return {
@@ -299,7 +302,8 @@ def gen_target_weights(wl: Workload, device="cpu", std: float = 0.02):
                              index=k).float()) for k in range(nt)],
         "gains": [bf(uniform_gains(wl, f"target-gain{k}", Dt, device)
                      .float()) for k in range(nt)],
-        "head": bf(normal(wl, "target-head", (V, Dt), std, device).float()),
+        "head": bf(normal(wl, "target-head", (V, Dt), head_std, device)
+                   .float()),
         "eps": wl.rms_eps,
     }
 
