@@ -14,7 +14,9 @@ from typing import Dict, List, Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdflash.so")
+# DFLASH_LIB may name another build of the same library (the host-sanitized
+# one that the ABI tests load); by default the in-tree build
+LIB_PATH = os.environ.get("DFLASH_LIB") or os.path.join(_HERE, "libdflash.so")
 HARNESS_PATH = os.path.join(_HERE, "libdflash_harness.so")
 
 DFLASH_OK = 0

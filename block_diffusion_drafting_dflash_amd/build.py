@@ -43,9 +43,29 @@ def common_flags():
             "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (device code is
+# built as usual): each -fsanitize applies to the host compilation only.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                 "-fsanitize=undefined", "-Xarch_host",
+                 "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def asan_runtime() -> str:
+    """The shared AddressSanitizer runtime of the ROCm clang (to preload
+    into an uninstrumented interpreter that loads a sanitized library)."""
+    import glob
+    c = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/"
+                         "libclang_rt.asan-x86_64.so"))
+    if not c:
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found under "
+                           "/opt/rocm/llvm")
+    return c[-1]
+
+
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *common_flags(), *extra, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n"
@@ -53,10 +73,10 @@ def _compile(src: str) -> str:
     return obj
 
 
-def _link(objs, out):
+def _link(objs, out, extra=()):
     tmp = out + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o",
-           tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra,
+           *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
@@ -72,6 +92,18 @@ def build(jobs: int = 8, verbose: bool = False) -> None:
     _link([objs[s] for s in HARNESS_SOURCES], HARNESS_LIB)
     if verbose:
         print(f"built {LIB} and {HARNESS_LIB}")
+
+
+def build_sanitized(out_dir: str, jobs: int = 8) -> str:
+    """libdflash.so with host ASan + UBSan into out_dir (for the ABI
+    validation tests on a machine without a GPU); returns its path."""
+    os.makedirs(out_dir, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, 16))) as ex:
+        objs = list(ex.map(lambda f: _compile(f, out_dir, SANITIZE_HOST),
+                           LIB_SOURCES))
+    out = os.path.join(out_dir, "libdflash.so")
+    _link(objs, out, SANITIZE_HOST)
+    return out
 
 
 if __name__ == "__main__":
