@@ -116,7 +116,9 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
 
   constexpr int kSets = attn_sets<G>();
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  int L = p.ctx_len[b];
+  // one value for the workgroup: the tile positions (and page lookups)
+  // derived from it stay scalar
+  int L = __builtin_amdgcn_readfirstlane(p.ctx_len[b]);
   L = min(max(L, 0), p.max_len);
   const int nkeys = L + p.K;
   const int k0 = c * p.chunk;
@@ -136,21 +138,25 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
     const int pk = min(kt, k1 - 1);
     const int first = p.pages.log2 < 0 ? 0 : (pk >> p.pages.log2) << p.pages.log2;
     const int64_t off =
-        (kv_row(p.pages, p.P, p.Hkv, b, kvh, first, p.err) - first) * D * SZ;
+        (kv_row_uniform(p.pages, p.P, p.Hkv, b, kvh, first, p.err) - first) *
+        D * SZ;
     load_tile<T, D, G>(t, static_cast<const char*>(p.kc) + off,
                        static_cast<const char*>(p.vc) + off, kt, k1 - 1, tid);
   };
-  TileRegs<T, D, G> regs0, regs1, regs2;
-  load_at(regs0, k0);
-  load_at(regs1, k0 + kKeyTile);
-  if constexpr (kSets == 3) load_at(regs2, k0 + 2 * kKeyTile);
-
-  // Q fragments of this wave's head: lane (query r, group g)
+  // Q fragments of this wave's head: lane (query r, group g).  They are
+  // staging loads issued ahead of the K/V prefetch and waited for once
+  // below: a compiler-tracked load would make each use inside the tile loop
+  // wait for every load then in flight, draining the prefetch at each tile.
   const char* qrow = static_cast<const char*>(p.q) +
                      ((int64_t)(b * p.K + r) * p.Hq * D + hq * D + g * E) * SZ;
   u32x4 qf[DC];
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) qf[dc] = load16(qrow + dc * KC * SZ);
+  for (int dc = 0; dc < DC; ++dc) qf[dc] = stage_load(qrow + dc * KC * SZ);
+  TileRegs<T, D, G> regs0, regs1, regs2;
+  load_at(regs0, k0);
+  load_at(regs1, k0 + kKeyTile);
+  if constexpr (kSets == 3) load_at(regs2, k0 + 2 * kKeyTile);
+  stage_wait<0, DC, kSets * 2 * NP>(qf);
 
   // running max (log2 domain), softmax numerator o and denominator l
   float m_run = -INFINITY, l_run = 0.f;

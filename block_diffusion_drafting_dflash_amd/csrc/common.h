@@ -147,6 +147,7 @@ __device__ __forceinline__ void vm_wait(u32x4& v) {
   asm volatile("s_waitcnt vmcnt(%1)" : "+v"(v) : "n"(N));
 }
 
+
 // Waits for registers st[0 .. LIM) of one batch of staging loads, issued in
 // that order, with AHEAD further loads issued after the batch: register I
 // is complete once at most AHEAD + LIM - 1 - I loads are outstanding.

@@ -17,7 +17,7 @@ namespace dflash {
 namespace {
 
 // Waves per workgroup and fragment steps in flight per wave at batch 1
-// (one 16-row tile); measured on MI355X, see the design notes.
+// (one 16-row tile); measured on MI355X.
 #ifndef DFLASH_GEMM_W
 #define DFLASH_GEMM_W 8
 #endif
@@ -438,13 +438,27 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmArgs p) {
 // none for the last tile).  The tile is multiplied from set b; with REFILL
 // b is then reloaded with the tile two ahead, before the wave sums.  With
 // WF8 each of the NB weight loads of a set is a pair of contraction steps
-// (activation fragments a[2u], a[2u + 1]); otherwise one step (a[u]).
+// (activation fragments a[2u], a[2u + 1]); otherwise one step (a[u]).  The
+// tile's 16 row scales (WF8) are scalar loads through the constant address
+// space: a vector load here would make its use wait for every load in
+// flight, the next tiles' weights included.
 template <typename T, int W, int NA, int NB, int AHEAD, bool REFILL, bool WF8,
           typename LoadW>
 __device__ __forceinline__ void lm_tile(const GemmArgs& p, u32x4 (&a)[NA],
                                         u32x4 (&b)[NB], int n_i, int i,
                                         int tile, bool valid, double* redd,
                                         Top2& run, const LoadW& load_w) {
+  float s16[16];
+  if constexpr (WF8) {
+    typedef const float __attribute__((address_space(4))) cfloat;
+    const uint64_t ad = (uint64_t)(uintptr_t)(p.wscale + (int64_t)tile * 16);
+    const uint64_t au =
+        ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(ad >> 32)) << 32) |
+        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ad);
+    const cfloat* ws = (const cfloat*)(uintptr_t)au;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) s16[c] = ws[c];
+  }
   stage_wait<0, NB, AHEAD>(b);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -468,7 +482,12 @@ __device__ __forceinline__ void lm_tile(const GemmArgs& p, u32x4 (&a)[NA],
     double v = redd[idx];
 #pragma unroll
     for (int w = 1; w < W; ++w) v += redd[w * 256 + idx];
-    if (p.wscale != nullptr) v *= (double)p.wscale[tile * 16 + (idx & 15)];
+    if constexpr (WF8) {
+      float sc = s16[0];
+#pragma unroll
+      for (int c = 1; c < 16; ++c) sc = (idx & 15) == c ? s16[c] : sc;
+      v *= (double)sc;
+    }
     const float z = (float)v;
     const int row = 4 * ((idx & 63) >> 4) + (idx >> 6);
     const int col = tile * 16 + (idx & 15);
@@ -674,6 +693,8 @@ int lm_head_parts(bool bf16, int M, int N, int Kd, int num_cu) {
 hipError_t launch_lm_head(bool bf16, int parts, const GemmArgs& a,
                           hipStream_t s) {
   if (parts <= 0 || !a.a_packed) return hipErrorInvalidValue;
+  // row scales come with FP8 weights only (and always with them)
+  if ((a.wscale != nullptr) != (a.wfp8 != 0)) return hipErrorInvalidValue;
   if (a.wfp8) {
     if (!bf16 || a.Kd % 64 != 0) return hipErrorInvalidValue;
     launch_k((lm_head_kernel<bf16_t, kLmW, kLmNS, true>), dim3(parts),

@@ -117,6 +117,30 @@ __device__ __forceinline__ int64_t kv_row(const KvPages& g, int P, int Hkv,
   }
   return (((int64_t)page * Hkv + h) << g.log2) + (pos & ((1 << g.log2) - 1));
 }
+// kv_row for a (seq, pos) that is the same across the workgroup: the page
+// id is read through the constant address space, which makes it a scalar
+// load, counted apart from the vector loads a pipelined loop keeps in flight
+// (a vector load here would make its use wait for all of them).  The page
+// table is not written while a drafting call runs.
+__device__ __forceinline__ int64_t kv_row_uniform(const KvPages& g, int P,
+                                                  int Hkv, int seq, int h,
+                                                  int pos, int* err) {
+  if (g.log2 < 0) return ((int64_t)seq * Hkv + h) * P + pos;
+  typedef const int32_t __attribute__((address_space(4))) cint32;
+  // the entry's address, moved to scalar registers (it is the same in
+  // every lane)
+  const uint64_t a =
+      (uint64_t)(uintptr_t)(g.table + (int64_t)seq * g.ld + (pos >> g.log2));
+  const uint64_t au =
+      ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  int page = *(const cint32*)(uintptr_t)au;
+  if (page < 0 || page >= g.npages) {
+    set_error(err, DFLASH_DEVERR_PAGE);
+    page = 0;
+  }
+  return (((int64_t)page * Hkv + h) << g.log2) + (pos & ((1 << g.log2) - 1));
+}
 // Rows of one plane.
 __host__ __device__ __forceinline__ int64_t kv_plane_rows(const KvPages& g,
                                                           int max_batch,

@@ -14,7 +14,7 @@ Order and notation follow the pages:
     Comparison"), optionally repeated for S refinement passes that commit
     positions in confidence order (stable-lab, "The Model at a Glance").
 
-Readings where the pages are silent (each is listed in the design notes):
+Readings taken where the pages are silent:
 block = [anchor, m, ..., m] with the anchor the last verified token, drafts at
 block indices 1..K-1; fusion = concat of the n_t layers in caller order -> fc
 -> RMSNorm with gain; no norm between H_cond and the K/V projections; RoPE on

@@ -1,7 +1,6 @@
 """Scalar building blocks of the oracle, in float64.
 
-The pages fix none of these details (the readings taken are listed in the
-design notes): RMSNorm with a gain, rotate-half RoPE with inverse frequencies
+The pages fix none of these details; the readings taken are: RMSNorm with a gain, rotate-half RoPE with inverse frequencies
 theta^(-2i/d), SiLU-gated MLP, softmax in float64, and bf16 storage rounding
 to nearest-even at the points where the drafter stores bf16 tensors.
 """
