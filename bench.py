@@ -59,6 +59,11 @@ def parse():
                          "(handed out in a shuffled order); 0: contiguous")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter scale)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="instead of the step: time torch.matmul (the vendor "
+                         "GEMM library) at the workload's projection and "
+                         "LM-head shapes, as a reference for the MFMA "
+                         "fraction the tiled kernels reach")
     return ap.parse_args()
 
 
@@ -497,6 +502,49 @@ def measure(wl, args, torch, dfl, dev, kind, full=True):
     return entry, extras, weights, lens
 
 
+def vendor_gemm(wl, torch, dev, reps=10):
+    """Median time of torch.matmul(A, W^T) in the drafter dtype at the
+    shapes of one batched step's GEMMs (A: rows x K, W: N x K as stored)."""
+    B, K = wl.batch, wl.block_size
+    D, I, V, d = wl.hidden, wl.intermediate, wl.vocab, wl.head_dim
+    qd, kvd = wl.num_q_heads * d, wl.num_kv_heads * d
+    R = B * K
+    shapes = [("qkv", R, D, qd + 2 * kvd), ("o", R, qd, D),
+              ("gate_up", R, D, 2 * I), ("down", R, I, D),
+              ("fc", B * wl.new_rows, wl.num_target_layers * wl.target_hidden,
+               D),
+              ("lm_head", B * (K - 1), D, V)]
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    peak = MFMA_PEAK["f32" if wl.dtype == "f32" else "bf16"]
+    out = []
+    for name, m, k, n in shapes:
+        a = torch.randn(m, k, device=dev, dtype=dt)
+        w = torch.randn(n, k, device=dev, dtype=dt)
+        for _ in range(3):
+            torch.matmul(a, w.t())
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, w.t())
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.sort()
+        us = ts[len(ts) // 2]
+        tf = 2.0 * m * n * k / us / 1e6
+        out.append({"gemm": name, "m": m, "k": k, "n": n, "us": round(us, 2),
+                    "tflops": round(tf, 1), "frac": round(tf / peak, 4)})
+        print(f"# {name} {m}x{k}x{n}: {us:.1f} us, {tf:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        del a, w
+    return {"vendor_gemm": out, "workload": wl.name,
+            "library": "torch.matmul (hipBLASLt)", "peak_tflops": peak,
+            "timing": f"median of {reps} calls, HIP events"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -515,6 +563,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     wl = W.WORKLOADS[args.workload]
+    if args.vendor_gemm:
+        print(json.dumps(vendor_gemm(wl, torch, dev)), flush=True)
+        return
     kind = args.timed_kernel if args.timed_kernel != "auto" else auto_kernel(wl)
     head, extras, weights, lens = measure(wl, args, torch, dfl, dev, kind)
     print(f"# {wl.name}: {head['ms_per_step']} ms/step, {head['value']} "
