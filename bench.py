@@ -59,6 +59,12 @@ def parse():
                          "(handed out in a shuffled order); 0: contiguous")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter scale)")
+    ap.add_argument("--block-vs-one", action="store_true",
+                    help="instead of the step: time the injection of 16 rows "
+                         "against 1 row per sequence and a drafting pass with "
+                         "15 masked positions against one with 1 (the LM "
+                         "head's row count); the block-versus-step ratio of "
+                         "the pages at this batch")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="instead of the step: time torch.matmul (the vendor "
                          "GEMM library) at the workload's projection and "
@@ -545,6 +551,62 @@ def vendor_gemm(wl, torch, dev, reps=10):
             "timing": f"median of {reps} calls, HIP events"}
 
 
+def block_vs_one(wl, torch, dfl, dev, reps=30):
+    """The pages compare one K-token block pass with one single-token draft
+    step.  The library drafts K = 16 positions per pass, so the parts whose
+    cost depends on the row count are timed at both sizes: the injection of
+    the new context rows (fc and the K/V projections: 16 rows per sequence
+    against 1) and the drafting pass with 15 masked positions against a pass
+    whose block gives 14 of them (one masked position: one LM-head row per
+    sequence; the layers still run the 16 block rows)."""
+    ctx, kv, lens, inp, weights = setup(wl, torch, dfl, dev)
+    B, K = wl.batch, wl.block_size
+    maxL = int(max(lens))
+    last = torch.arange(B, device=dev) * wl.new_rows + wl.new_rows - 1
+    H1 = [h.index_select(0, last).contiguous() for h in inp["H"]]
+    seq1 = inp["row_seq"].index_select(0, last).contiguous()
+    pos1 = inp["row_pos"].index_select(0, last).contiguous()
+    rng = np.random.default_rng(11)
+    blk = rng.integers(0, wl.vocab - 1, (B, K)).astype(np.int32)
+    blk[:, 0] = inp["anchor"].cpu().numpy()
+    blk[:, K - 1] = wl.mask_id
+    blk = torch.from_numpy(blk).to(dev)
+    draft = torch.zeros(B, K - 1, dtype=torch.int32, device=dev)
+    cases = {
+        "inject_16_rows": lambda: ctx.inject_kv(
+            inp["H"], inp["row_seq"], inp["row_pos"], kv),
+        "inject_1_row": lambda: ctx.inject_kv(H1, seq1, pos1, kv),
+        "draft_pass_15_masked": lambda: ctx.draft_block(
+            inp["ctx_len"], kv, maxL, anchor=inp["anchor"], draft=draft),
+        "draft_pass_1_masked": lambda: ctx.draft_block(
+            inp["ctx_len"], kv, maxL, block_tokens=blk, draft=draft),
+    }
+    out = {}
+    for name, fn in cases.items():
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        out[name + "_ms"] = round(ts[len(ts) // 2], 5)
+        print(f"# {name}: {out[name + '_ms']} ms", file=sys.stderr, flush=True)
+    if ctx.check_device_errors() != 0:
+        raise RuntimeError("device error in the block-versus-one runs")
+    t16 = out["inject_16_rows_ms"] + out["draft_pass_15_masked_ms"]
+    t1 = out["inject_1_row_ms"] + out["draft_pass_1_masked_ms"]
+    out["block_over_one"] = round(t16 / t1, 4)
+    return {"block_vs_one": out, "workload": wl.name,
+            "timing": f"median of {reps} calls, HIP events"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -565,6 +627,9 @@ def main():
     wl = W.WORKLOADS[args.workload]
     if args.vendor_gemm:
         print(json.dumps(vendor_gemm(wl, torch, dev)), flush=True)
+        return
+    if args.block_vs_one:
+        print(json.dumps(block_vs_one(wl, torch, dfl, dev)), flush=True)
         return
     kind = args.timed_kernel if args.timed_kernel != "auto" else auto_kernel(wl)
     head, extras, weights, lens = measure(wl, args, torch, dfl, dev, kind)
