@@ -303,7 +303,7 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
     a.wfp8 = 0;
   }
   if (tiled) {
-    const int cfg = plan_tiled(a.M, a.N, splittable(a));
+    const int cfg = plan_tiled(a.M, a.N, a.ep, splittable(a));
     const int S = plan_ksplit(c, a, cfg, sw);
     TimedLaunch tl(c, kind, s, S > 1 ? 2 : 1);
     if (S > 1) {
@@ -320,6 +320,14 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
     }
     DF_HIP(launch_gemm_tiled(true, cfg, a, 1, s));
     return DFLASH_OK;
+  }
+  if (!lm && a.a_packed) {
+    const int parts = proj_stream_parts(c->bf16, a, c->num_cu);
+    if (parts > 0) {
+      TimedLaunch tl(c, kind, s);
+      DF_HIP(launch_proj_stream(c->bf16, parts, a, s));
+      return DFLASH_OK;
+    }
   }
   const GemmPlan pl = plan_gemm(a.M, a.N, lm);
   TimedLaunch tl(c, kind, s);
@@ -624,7 +632,7 @@ dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
     } else {
       dflash_status st = run_gemm(ctx, hd, s, ws.split, DFLASH_TIME_LMHEAD);
       if (st != DFLASH_OK) return st;
-      nrec = gemm_is_tiled(ctx, hd) ? tiled_top2_records(plan_tiled(Mh, V), V)
+      nrec = gemm_is_tiled(ctx, hd) ? tiled_top2_records(plan_tiled(Mh, V, EP_TOP2, false), V)
                                     : V / 16;
       if (nrec > kCommitMaxRecords) {
         // many records per row: merge them to kMergeChunks per row first,

@@ -23,15 +23,24 @@ __device__ __forceinline__ void rope_pair(double a, double b, double2 cs,
 // evaluation.  Near a midpoint, for large |a| and for zero, denormal or
 // non-finite results the float64 evaluation decides.
 constexpr uint32_t kSiluGuard = 64;
-__device__ __forceinline__ uint32_t swiglu_bf16(float a, float b) {
+// The float evaluation: true, with the bf16 in `bits`, where it decides.
+__device__ __forceinline__ bool swiglu_bf16_float(float a, float b,
+                                                  uint32_t& bits) {
   const float r = a / (1.f + expf(-a)) * b;
   const uint32_t u = __float_as_uint(r);
   const uint32_t lo = u & 0xFFFFu, ex = u & 0x7F800000u;
-  const bool clear = fabsf(a) < 64.f && ex != 0u && ex != 0x7F800000u &&
-                     (lo + kSiluGuard < 0x8000u || lo > 0x8000u + kSiluGuard);
-  if (clear) return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  bits = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return fabsf(a) < 64.f && ex != 0u && ex != 0x7F800000u &&
+         (lo + kSiluGuard < 0x8000u || lo > 0x8000u + kSiluGuard);
+}
+// The float64 evaluation, for the cases the float one leaves open.
+__device__ __forceinline__ uint32_t swiglu_bf16_f64(float a, float b) {
   const double da = a;
   return f64_to_bf16(da / (1.0 + exp(-da)) * (double)b);
+}
+__device__ __forceinline__ uint32_t swiglu_bf16(float a, float b) {
+  uint32_t bits;
+  return swiglu_bf16_float(a, b, bits) ? bits : swiglu_bf16_f64(a, b);
 }
 
 // One finished output pair of a MAP_PAIRS GEMM: `a` is low column `col`,
@@ -40,18 +49,25 @@ __device__ __forceinline__ uint32_t swiglu_bf16(float a, float b) {
 //   EP_QKV:    q -> RoPE -> q buffer; block k -> RoPE and v -> this layer's
 //              cache at position L_b + i
 //   EP_KV:     injected row -> RoPE(k), v -> cache of layer col / (2 Hkv d)
+// The EP_SWIGLU element alone.
+template <typename T>
+__device__ __forceinline__ void swiglu_store(const GemmArgs& p, int row,
+                                             int col, float a, float b) {
+  T* act = static_cast<T*>(p.out_t);
+  const int64_t off = packed_offset<T>(row, col, p.pair_off) / sizeof(T);
+  if constexpr (sizeof(T) == 2) {
+    act[off].bits = (uint16_t)swiglu_bf16(a, b);
+  } else {
+    const double da = a;
+    store_elem(act, off, da / (1.0 + exp(-da)) * (double)b);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void pair_epilogue(const GemmArgs& p, int row,
                                               int col, float a, float b) {
   if (p.ep == EP_SWIGLU) {
-    T* act = static_cast<T*>(p.out_t);
-    const int64_t off = packed_offset<T>(row, col, p.pair_off) / sizeof(T);
-    if constexpr (sizeof(T) == 2) {
-      act[off].bits = (uint16_t)swiglu_bf16(a, b);
-    } else {
-      const double da = a;
-      store_elem(act, off, da / (1.0 + exp(-da)) * (double)b);
-    }
+    swiglu_store<T>(p, row, col, a, b);
     return;
   }
   const int half = p.d / 2;

@@ -414,10 +414,24 @@ int tiled_block_cols(int cfg) {
 #define DFLASH_TILED_CFG -1
 #endif
 
-// Block shape by rows and columns (measured on MI355X at 64, 256 and 1024
-// rows over the drafter's projection and LM-head shapes).
-int plan_tiled(int M, int N, bool splittable) {
+#ifndef DFLASH_MID_ROWS
+#define DFLASH_MID_ROWS 256
+#endif
+
+// Block shape by rows, columns and epilogue (measured on MI355X at 64, 256
+// and 1024 rows over the drafter's projection and LM-head shapes).
+int plan_tiled(int M, int N, int ep, bool splittable) {
   if (DFLASH_TILED_CFG >= 0) return DFLASH_TILED_CFG;
+  // 129 to 256 rows (measured at 240 and 256): the LM head takes one row
+  // block of 256 x 128 on eight waves, so each weight block is read once
+  // (240 x 151936: 346 against 369 us in 128 x 128), and a wide SwiGLU
+  // output with a multiple of 192 columns takes 128 x 192 blocks, which
+  // fill every CU where 128 x 128 gives half of them a second block
+  // (256 x 24576: 69 against 84 us)
+  if (M > 128 && M <= DFLASH_MID_ROWS) {
+    if (ep == EP_TOP2) return TILE_256x128_W8;
+    if (ep == EP_SWIGLU && N >= 16384 && N % 192 == 0) return TILE_128x192;
+  }
   // above 512 rows, outputs narrower than 16384 columns take 256 x 128
   // blocks on eight waves (with split-K filling the CUs): 16% faster than
   // 128 x 128 there at 1024 rows, slower for the wide gate/up and LM head.

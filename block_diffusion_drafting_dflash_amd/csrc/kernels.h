@@ -198,6 +198,13 @@ hipError_t launch_gemm(bool bf16, const GemmPlan& pl, const GemmArgs& a,
 int lm_head_parts(bool bf16, int M, int N, int Kd, int num_cu);
 hipError_t launch_lm_head(bool bf16, int parts, const GemmArgs& a,
                           hipStream_t s);
+// The FP8 gate/up projection (EP_SWIGLU, MAP_PAIRS, packed activations) of
+// at most 16 rows on the same persistent stream, each tile's pairs finished
+// by SwiGLU: returns the number of workgroups (> 0) when the call is
+// supported and has enough tiles to keep every workgroup streaming, else 0.
+int proj_stream_parts(bool bf16, const GemmArgs& a, int num_cu);
+hipError_t launch_proj_stream(bool bf16, int parts, const GemmArgs& a,
+                              hipStream_t s);
 
 // Tiled MFMA GEMM for batched rows (gemm_tiled.hip): output block shapes
 // rows x columns; each instance keeps its fragments in LDS per step.
@@ -212,9 +219,9 @@ enum TileCfg : int {
   TILE_128x192 = 7,     // 128 x 192 on four waves of 64 x 96
   TILE_NCFG = 8,
 };
-// Block shape of an M x N tiled GEMM; `splittable`: its contraction may be
-// split (plain-store and residual epilogues).
-int plan_tiled(int M, int N, bool splittable = false);
+// Block shape of an M x N tiled GEMM with epilogue `ep`; `splittable`: its
+// contraction may be split (plain-store and residual epilogues).
+int plan_tiled(int M, int N, int ep, bool splittable);
 // Top-2 records per row that the tiled LM head writes with block shape cfg
 // (one per column block: top2[row * records + block]).
 int tiled_top2_records(int cfg, int N);

@@ -49,6 +49,12 @@ CASES = {
                                  weight_format="fp8"),
     "small-fp8-b3": W.small_bf16(batch=3, name="small-fp8-b3", seed=86,
                                  weight_format="fp8"),
+    # the persistent SwiGLU stream on FP8 pairs: 1104 gate/up tiles (four or
+    # five per workgroup), a contraction of 16 pairs (one per wave)
+    "ffn-fp8-b1": W.small_bf16(batch=1, num_layers=1, hidden=1024,
+                               intermediate=8832, ctx_min=120, ctx_max=120,
+                               name="ffn-fp8-b1", seed=97,
+                               weight_format="fp8"),
 }
 
 

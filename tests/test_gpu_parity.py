@@ -51,6 +51,12 @@ WLS = {
     "small-bf16-g8-b8": W.small_bf16(num_q_heads=16, num_kv_heads=2, batch=8,
                                      ctx_min=30, ctx_max=260,
                                      name="small-bf16-g8-b8", seed=82),
+    # 16 sequences (256 block rows, 240 LM-head rows): the LM head in one
+    # 256-row block on eight waves, and a SwiGLU output of 16512 columns (a
+    # multiple of 192) in 128 x 192 blocks
+    "small-bf16-b16-ffn": W.small_bf16(batch=16, intermediate=8256,
+                                       ctx_min=20, ctx_max=120,
+                                       name="small-bf16-b16-ffn", seed=98),
 }
 
 
