@@ -65,6 +65,11 @@ def parse():
                          "15 masked positions against one with 1 (the LM "
                          "head's row count); the block-versus-step ratio of "
                          "the pages at this batch")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="instead of the step: the HBM read rate a plain "
+                         "streaming read of 1 GiB reaches (harness kernel), "
+                         "the practical ceiling for the bandwidth-bound "
+                         "kernels")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="instead of the step: time torch.matmul (the vendor "
                          "GEMM library) at the workload's projection and "
@@ -551,6 +556,36 @@ def vendor_gemm(wl, torch, dev, reps=10):
             "timing": f"median of {reps} calls, HIP events"}
 
 
+def read_probe(torch, dfl, dev, reps=5):
+    """Median time of the harness's plain streaming read of 1 GiB at several
+    grid sizes (16 waves per workgroup, 8 KiB per wave in flight)."""
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = []
+    for grid in (256, 512, 1024, 2048):
+        dfl.read_probe(buf, grid, sink)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dfl.read_probe(buf, grid, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.sort()
+        us = ts[len(ts) // 2]
+        gbs = nbytes / us / 1e3
+        out.append({"grid": grid, "us": round(us, 1), "GB/s": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+        print(f"# read probe grid {grid}: {us:.1f} us, {gbs:.1f} GB/s",
+              file=sys.stderr, flush=True)
+    return {"read_probe": out, "bytes": nbytes, "peak_GBs": HBM_PEAK_GBS,
+            "timing": f"median of {reps} calls, HIP events"}
+
+
 def block_vs_one(wl, torch, dfl, dev, reps=30):
     """The pages compare one K-token block pass with one single-token draft
     step.  The library drafts K = 16 positions per pass, so the parts whose
@@ -612,8 +647,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); the drafting path is not sharded in this "
-              "build.", file=sys.stderr)
+              f"WORLD_SIZE {world}); the drafting path runs on one GPU.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -627,6 +662,9 @@ def main():
     wl = W.WORKLOADS[args.workload]
     if args.vendor_gemm:
         print(json.dumps(vendor_gemm(wl, torch, dev)), flush=True)
+        return
+    if args.read_probe:
+        print(json.dumps(read_probe(torch, dfl, dev)), flush=True)
         return
     if args.block_vs_one:
         print(json.dumps(block_vs_one(wl, torch, dfl, dev)), flush=True)

@@ -37,7 +37,8 @@ LIB_SYMBOLS = ["dflash_create", "dflash_destroy", "dflash_kv_cache_bytes",
 TIME_KIND = {"off": 0, "lmhead": 1, "attention": 2, "gemm": 3}
 HARNESS_SYMBOLS = ["dflash_harness_synth_target",
                    "dflash_harness_fp8_to_bf16",
-                   "dflash_harness_target_forward"]
+                   "dflash_harness_target_forward",
+                   "dflash_harness_read_probe"]
 
 
 class DFlashError(RuntimeError):
@@ -143,6 +144,8 @@ def load_harness():
         vp, i32, i32, i32, i32, vp, vp, _PP, _PP, vp, ctypes.c_float, _PP,
         ctypes.c_int64, vp, vp]
     h.dflash_harness_target_forward.restype = ctypes.c_int
+    h.dflash_harness_read_probe.argtypes = [vp, vp, ctypes.c_int64, i32, vp]
+    h.dflash_harness_read_probe.restype = ctypes.c_int
     _harness = h
     return h
 
@@ -380,6 +383,19 @@ def fp8_to_bf16(codes: torch.Tensor, stream=None) -> torch.Tensor:
     if st != 0:
         raise RuntimeError(f"dflash_harness_fp8_to_bf16 failed ({st})")
     return out
+
+
+def read_probe(buf: torch.Tensor, grid: int, sink: torch.Tensor,
+               stream=None) -> None:
+    """The harness's plain streaming read of all of `buf` (a device tensor
+    of a multiple of 256 KiB) by `grid` workgroups; `sink` an int32 device
+    tensor it practically never writes."""
+    h = load_harness()
+    st = h.dflash_harness_read_probe(_stream(stream), _ptr(buf),
+                                     buf.numel() * buf.element_size(),
+                                     int(grid), _ptr(sink))
+    if st != 0:
+        raise RuntimeError(f"dflash_harness_read_probe failed ({st})")
 
 
 def target_forward(tw, tokens: torch.Tensor, hooks=None, stream=None):

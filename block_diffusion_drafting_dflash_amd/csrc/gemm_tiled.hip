@@ -384,6 +384,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
 #ifndef DFLASH_D128_NBUF
 #define DFLASH_D128_NBUF 4
 #endif
+#ifndef DFLASH_D192_NBUF
+#define DFLASH_D192_NBUF 4
+#endif
+#ifndef DFLASH_W8_NBUF
+#define DFLASH_W8_NBUF 4
+#endif
 hipError_t tiled_cfg(int cfg, const GemmArgs& a, int ks, hipStream_t s) {
   switch (cfg) {
     case TILE_64x64: return dma_t<1, 1, 2, 2, DFLASH_D64_NBUF>(a, ks, s);
@@ -391,8 +397,8 @@ hipError_t tiled_cfg(int cfg, const GemmArgs& a, int ks, hipStream_t s) {
     case TILE_256x64: return dma_t<4, 1, 2, 2, 4>(a, ks, s);
     case TILE_256x128: return dma_t<4, 2, 2, 2, 4>(a, ks, s);
     case TILE_128x256: return dma_t<2, 4, 2, 2, 4>(a, ks, s);
-    case TILE_256x128_W8: return dma_t<2, 2, 4, 2, 4>(a, ks, s);
-    case TILE_128x192: return dma_t<2, 3, 2, 2, 4>(a, ks, s);
+    case TILE_256x128_W8: return dma_t<2, 2, 4, 2, DFLASH_W8_NBUF>(a, ks, s);
+    case TILE_128x192: return dma_t<2, 3, 2, 2, DFLASH_D192_NBUF>(a, ks, s);
   }
   return hipErrorInvalidValue;  // 256 x 256: its logit block exceeds LDS
 }

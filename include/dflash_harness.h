@@ -59,6 +59,15 @@ int dflash_harness_target_forward(void* stream, int32_t rows,
 int dflash_harness_fp8_to_bf16(void* stream, int32_t n, const uint8_t* codes,
                                uint16_t* out);
 
+/* A plain streaming read of `bytes` (a multiple of 256 KiB; buf 16-byte
+ * aligned) by `grid` workgroups of 16 waves, 8 KiB per wave in flight, for
+ * measuring the HBM read rate the machine delivers to a pure stream (the
+ * reference for the drafting kernels' bandwidth fractions).  Nothing is
+ * written except, practically never, sink[0].  Returns 0, -1 on a bad
+ * argument, -4 on a HIP launch error. */
+int dflash_harness_read_probe(void* stream, const void* buf, int64_t bytes,
+                              int32_t grid, int32_t* sink);
+
 #ifdef __cplusplus
 }
 #endif
