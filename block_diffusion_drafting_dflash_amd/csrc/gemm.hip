@@ -567,8 +567,8 @@ __device__ __forceinline__ void lm_tile(const GemmArgs& p, u32x4 (&a)[NA],
 
 // NS: the most contraction steps a wave holds.  A wave's units (steps, or
 // with WF8 pairs of steps) are wave, wave + W, ...
-template <typename T, int W, int NS, bool WF8, bool PROJ = false>
-__global__ __launch_bounds__(64 * W) void lm_head_kernel(GemmArgs p) {
+template <typename T, int W, int NS, bool WF8, bool PROJ>
+__device__ __forceinline__ void persistent_sweep(const GemmArgs& p) {
   static_assert(!PROJ || WF8, "the SwiGLU stream takes FP8 weights");
   constexpr int KC = Storage<T>::KC;
   constexpr int NB = WF8 ? NS / 2 : NS;  // weight loads per tile per wave
@@ -649,6 +649,17 @@ __global__ __launch_bounds__(64 * W) void lm_head_kernel(GemmArgs p) {
     const int row = 4 * ((threadIdx.x & 63) >> 4) + (threadIdx.x >> 6);
     if (row < p.M) p.top2[(int64_t)row * P + wg] = run;
   }
+}
+
+template <typename T, int W, int NS, bool WF8>
+__global__ __launch_bounds__(64 * W) void lm_head_kernel(GemmArgs p) {
+  persistent_sweep<T, W, NS, WF8, false>(p);
+}
+
+// The FP8 gate/up projection on the same sweep (its own name in traces).
+template <int W, int NS>
+__global__ __launch_bounds__(64 * W) void gemm_stream_kernel(GemmArgs p) {
+  persistent_sweep<bf16_t, W, NS, true, true>(p);
 }
 
 // One 16-byte chunk of the packed matrix per thread.
@@ -810,8 +821,8 @@ hipError_t launch_proj_stream(bool bf16, int parts, const GemmArgs& a,
       a.Kd % 64 != 0 || a.Kd / Storage<bf16_t>::KC > kLmW * kLmNS ||
       (a.N / 16 + parts - 1) / parts > kProjMaxTiles)
     return hipErrorInvalidValue;
-  launch_k((lm_head_kernel<bf16_t, kLmW, kLmNS, true, true>), dim3(parts),
-           dim3(64 * kLmW), 0, s, a);
+  launch_k((gemm_stream_kernel<kLmW, kLmNS>), dim3(parts), dim3(64 * kLmW),
+           0, s, a);
   return hipGetLastError();
 }
 
