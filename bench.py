@@ -156,10 +156,12 @@ def kernel_cost(wl, lens, kind):
 
 # Sources that define each timed kernel class: the LM head is the persistent
 # kernel up to 16 rows and the tiled GEMM beyond; the projection GEMMs are
-# the streaming or the tiled form with their shared epilogues.
+# the streaming or the tiled form with their shared epilogues, and a split
+# GEMM's reduction (fused with the row RMSNorm that follows it where that
+# norm takes its row form: epilogue.hip).
 KERNEL_SOURCES = {
     "lmhead": ["gemm.hip", "gemm_tiled.hip", "gemm_epilogue.h"],
-    "gemm": ["gemm.hip", "gemm_tiled.hip", "gemm_epilogue.h"],
+    "gemm": ["gemm.hip", "gemm_tiled.hip", "gemm_epilogue.h", "epilogue.hip"],
     "attention": ["attention.hip"],
 }
 

@@ -314,6 +314,15 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
       b.out_f32 = sw.p;
       b.ldo = a.N;
       DF_HIP(launch_gemm_tiled(true, cfg, b, S, s));
+      if (a.norm_g != nullptr && a.ldo == a.N &&
+          rmsnorm_row_form(c->bf16, a.M, a.N)) {
+        // the reduction and the row RMSNorm that reads its rows, in one pass
+        DF_HIP(launch_splitk_norm(c->bf16, a.M, a.N, S, sw.p, a.out_f32,
+                                  a.ep == EP_RESID, a.norm_g, a.norm_eps,
+                                  a.norm_out, s));
+        a.norm_fused = 1;
+        return DFLASH_OK;
+      }
       DF_HIP(launch_splitk_reduce(a.M, a.N, S, sw.p, a.out_f32, a.ldo,
                                   a.ep == EP_RESID, s));
       return DFLASH_OK;
@@ -333,6 +342,15 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
   TimedLaunch tl(c, kind, s);
   DF_HIP(launch_gemm(c->bf16, pl, a, s));
   return DFLASH_OK;
+}
+
+// The row RMSNorm that will read a GEMM's fp32 output: run_gemm fuses it
+// with a split-K reduction where it can and then sets norm_fused.
+void set_norm(GemmArgs& a, const void* gain, float eps, void* out) {
+  a.norm_g = gain;
+  a.norm_eps = eps;
+  a.norm_out = out;
+  a.norm_fused = 0;
 }
 
 // GEMM on a packed activation operand (rows M, contraction Kd).
@@ -555,13 +573,16 @@ dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
                         anchor, block_tokens, bs, ctx->embed, ws.x,
                         draft_tokens, fuse_norm ? ctx->attn_norm[0] : nullptr,
                         c.rms_eps, ws.h, s));
-    for (int l = 0; l < c.num_layers; ++l) {
+    const int Nl = c.num_layers;
+    bool h_ready = false;  // the previous down-projection wrote ws.h
+    for (int l = 0; l < Nl; ++l) {
       char* kvl = static_cast<char*>(kv_cache) + l * layer_elems * ctx->esz;
       // q, k, v of RMSNorm(x); RoPE; q -> q buffer, block k, v -> cache
       // positions L_b + i
-      if (l > 0 || !fuse_norm)
+      if ((l > 0 || !fuse_norm) && !h_ready)
         DF_HIP(launch_rmsnorm(bf, R, D, ws.x, nullptr, ctx->attn_norm[l],
                               c.rms_eps, ws.h, s));
+      h_ready = false;
       GemmArgs a = packed_args(ws.h, ctx->pk_qkv[l], ctx->fp8, R, qd + 2 * kvd, D);
       set_pairs(a, d, d / 2);
       set_cache_geometry(a, ctx);
@@ -584,11 +605,13 @@ dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
       o.ep = EP_RESID;
       o.out_f32 = ws.x;
       o.ldo = D;
+      set_norm(o, ctx->mlp_norm[l], c.rms_eps, ws.h);
       st = run_gemm(ctx, o, s, ws.split);
       if (st != DFLASH_OK) return st;
       // act = silu(h Wg^T) * (h Wu^T), h = RMSNorm(x)
-      DF_HIP(launch_rmsnorm(bf, R, D, ws.x, nullptr, ctx->mlp_norm[l],
-                            c.rms_eps, ws.h, s));
+      if (!o.norm_fused)
+        DF_HIP(launch_rmsnorm(bf, R, D, ws.x, nullptr, ctx->mlp_norm[l],
+                              c.rms_eps, ws.h, s));
       GemmArgs gu = packed_args(ws.h, ctx->pk_gu[l], ctx->fp8, R, 2 * I, D);
       set_pairs(gu, 2 * I, I);
       gu.ep = EP_SWIGLU;
@@ -600,8 +623,11 @@ dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
       dn.ep = EP_RESID;
       dn.out_f32 = ws.x;
       dn.ldo = D;
+      // the next layer's input norm rides on this reduction when it can
+      if (l + 1 < Nl) set_norm(dn, ctx->attn_norm[l + 1], c.rms_eps, ws.h);
       st = run_gemm(ctx, dn, s, ws.split);
       if (st != DFLASH_OK) return st;
+      h_ready = dn.norm_fused != 0;
     }
     // final norm of the still-masked rows (compacted), then the LM head with
     // the fused argmax / top-2 / log-sum-exp per 16-column vocabulary tile
@@ -1083,12 +1109,14 @@ dflash_status dflash_inject_kv(dflash_ctx* ctx, void* stream,
   a.ep = EP_STORE;
   a.out_f32 = ctx->u;
   a.ldo = D;
+  set_norm(a, ctx->hidden_norm, c.rms_eps, ctx->cond);
   const SplitWs sw{ctx->splitk, ctx->splitk_floats};
   dflash_status st = run_gemm(ctx, a, s, sw);
   if (st != DFLASH_OK) return st;
   // H_cond = RMSNorm(u) * g
-  DF_HIP(launch_rmsnorm(ctx->bf16, T, D, ctx->u, nullptr, ctx->hidden_norm,
-                        c.rms_eps, ctx->cond, s));
+  if (!a.norm_fused)
+    DF_HIP(launch_rmsnorm(ctx->bf16, T, D, ctx->u, nullptr, ctx->hidden_norm,
+                          c.rms_eps, ctx->cond, s));
   // every layer's K and V projection of H_cond in one pass; RoPE on K;
   // scatter into the cache
   GemmArgs b = packed_args(ctx->cond, ctx->pk_kv, ctx->fp8, T, c.num_layers * 2 * kvd, D);

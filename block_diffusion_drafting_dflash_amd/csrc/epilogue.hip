@@ -172,6 +172,79 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(int rows, int D,
   }
 }
 
+// A split-K reduction fused with the row RMSNorm that reads its result: for
+// row r < M, x[r] = sum_s ws[s][r] (plus the old x[r] when resid), the
+// copies added in order in float exactly as splitk_reduce_kernel adds them,
+// is written back,
+// and out[r] = RMSNorm(x[r]) * g is written packed with rmsnorm_row_kernel's
+// arithmetic (the same chunks per thread, the same float64 sums and
+// rounding).  So x and out are bit for bit those of the two kernels run one
+// after the other, with one launch and one pass over x fewer.  Rows from M
+// to the next multiple of 16 are written as zeros.
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_norm_row_kernel(
+    int M, int D, int S, const float* ws, float* x, int resid, const T* g,
+    float eps, T* out) {
+  constexpr int E = Storage<T>::E;
+  __shared__ double scratch[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  char* ob = reinterpret_cast<char*>(out);
+  const int nch = D / E;
+  if (row >= M) {
+    for (int c = tid; c < nch; c += 256)
+      *reinterpret_cast<u32x4*>(ob + packed_offset<T>(row, c * E, D)) =
+          u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const int64_t plane = (int64_t)M * D;
+  float* xr = x + (int64_t)row * D;
+  const float* wr = ws + (int64_t)row * D;
+  float v[kNormChunks][E];
+  double ss = 0.0;
+#pragma unroll
+  for (int ci = 0; ci < kNormChunks; ++ci) {
+    const int c = tid + ci * 256;
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        const int col = c * E + e;
+        f32x4 q = *reinterpret_cast<const f32x4*>(wr + col);
+        for (int k = 1; k < S; ++k) {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(wr + k * plane + col);
+          q = f32x4{q[0] + w[0], q[1] + w[1], q[2] + w[2], q[3] + w[3]};
+        }
+        if (resid) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(xr + col);
+          q = f32x4{o[0] + q[0], o[1] + q[1], o[2] + q[2], o[3] + q[3]};
+        }
+        *reinterpret_cast<f32x4*>(xr + col) = q;
+        v[ci][e] = q.x;
+        v[ci][e + 1] = q.y;
+        v[ci][e + 2] = q.z;
+        v[ci][e + 3] = q.w;
+        ss += (double)q.x * q.x + (double)q.y * q.y + (double)q.z * q.z +
+              (double)q.w * q.w;
+      }
+    }
+  }
+  const double tot = block_sum<4>(ss, scratch);
+  const double inv = 1.0 / sqrt(tot / (double)D + (double)eps);
+#pragma unroll
+  for (int ci = 0; ci < kNormChunks; ++ci) {
+    const int c = tid + ci * 256;
+    if (c < nch) {
+      const u32x4 gv = load16(g + c * E);
+      const T* gt = reinterpret_cast<const T*>(&gv);
+      u32x4 o;  // the 16-byte chunk is built in registers, stored once
+      T* ot = reinterpret_cast<T*>(&o);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        store_elem(ot, e, (double)v[ci][e] * inv * (double)load_elem(gt, e));
+      *reinterpret_cast<u32x4*>(ob + packed_offset<T>(row, c * E, D)) = o;
+    }
+  }
+}
+
 // The same, one workgroup per 16-row tile of the packed output, wave r on
 // row r (faster from ~512 rows, where the row form's partial-fragment
 // stores dominate).
@@ -285,11 +358,33 @@ hipError_t launch_embed(bool bf16, int B, int K, int D, int V, int mask_id,
                                s);
 }
 
+bool rmsnorm_row_form(bool bf16, int rows, int D) {
+  return (rows + 15) / 16 < 32 && D <= 256 * kNormChunks * (bf16 ? 8 : 4);
+}
+
+hipError_t launch_splitk_norm(bool bf16, int M, int D, int S, const float* ws,
+                              float* x, bool resid, const void* gain,
+                              float eps, void* out, hipStream_t s) {
+  if (!rmsnorm_row_form(bf16, M, D) || S < 1 || M < 1 ||
+      D % (bf16 ? 8 : 4) != 0)
+    return hipErrorInvalidValue;
+  const int tiles = (M + 15) / 16;
+  if (bf16)
+    launch_k(splitk_norm_row_kernel<bf16_t>, dim3(tiles * 16), dim3(256), 0,
+             s, M, D, S, ws, x, resid ? 1 : 0,
+             static_cast<const bf16_t*>(gain), eps, static_cast<bf16_t*>(out));
+  else
+    launch_k(splitk_norm_row_kernel<float>, dim3(tiles * 16), dim3(256), 0, s,
+             M, D, S, ws, x, resid ? 1 : 0, static_cast<const float*>(gain),
+             eps, static_cast<float*>(out));
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(bool bf16, int rows, int D, const float* x,
                           const int32_t* rowmap, const void* gain, float eps,
                           void* out, hipStream_t s) {
   const int tiles = (rows + 15) / 16;
-  if (tiles < 32 && D <= 256 * 4 * (bf16 ? 8 : 4)) {
+  if (rmsnorm_row_form(bf16, rows, D)) {
     if (bf16)
       launch_k(rmsnorm_row_kernel<bf16_t>, dim3(tiles * 16), dim3(256),
                          0, s, rows, D, x, rowmap,

@@ -183,6 +183,13 @@ struct GemmArgs {
   const int32_t* rowmap;   //   LM-head row -> block row b*K + i, or -1
   int64_t logits_ld;
   int* err;
+  // host side: the row RMSNorm that reads out_f32 next (gain, epsilon,
+  // packed output), run with the split-K reduction when the GEMM is split
+  // and the norm takes its row form; run_gemm sets norm_fused when it did
+  const void* norm_g;
+  float norm_eps;
+  void* norm_out;
+  int norm_fused;
 };
 
 struct GemmPlan {
@@ -280,6 +287,15 @@ hipError_t launch_embed(bool bf16, int B, int K, int D, int V, int mask_id,
 hipError_t launch_rmsnorm(bool bf16, int rows, int D, const float* x,
                           const int32_t* rowmap, const void* gain, float eps,
                           void* out, hipStream_t s);
+// Whether launch_rmsnorm takes its one-workgroup-per-row form for this shape.
+bool rmsnorm_row_form(bool bf16, int rows, int D);
+// The split-K reduction of S float copies ws[S][M][D] into x (added to x's
+// rows when resid), fused with the row-form RMSNorm of the result into out
+// (packed): the same bits as launch_splitk_reduce then launch_rmsnorm (no row
+// map), for the shapes where rmsnorm_row_form holds (else an error).
+hipError_t launch_splitk_norm(bool bf16, int M, int D, int S, const float* ws,
+                              float* x, bool resid, const void* gain,
+                              float eps, void* out, hipStream_t s);
 
 // ---- attention (attention.hip) -----------------------------------------
 struct AttnArgs {
