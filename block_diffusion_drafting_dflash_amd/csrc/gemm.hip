@@ -586,10 +586,10 @@ __device__ __forceinline__ void persistent_sweep(const GemmArgs& p) {
   auto tile_of = [&](int i) { return wg + min(i, nt - 1) * P; };
   // this wave's units: wave, wave + W, ... (n_i of them, n_i <= NB)
   const int n_i = wave < nunits ? (nunits - 1 - wave) / W + 1 : 0;
-  const int64_t unit_off = (int64_t)wave * 1024 + lane * 16;
-  // a unit past the wave's last repeats the last (a wave with no units
-  // reads unit 0), a slot past the last tile repeats the last tile; neither
-  // is multiplied or summed
+  const int first = n_i > 0 ? wave : 0;  // a wave with no units reads unit 0
+  const int64_t unit_off = (int64_t)first * 1024 + lane * 16;
+  // a unit past the wave's last repeats the last, a slot past the last tile
+  // repeats the last tile; neither is multiplied or summed
   auto load_w = [&](u32x4(&b)[NB], int i) {  // this workgroup's i-th tile
     const char* wt = static_cast<const char*>(p.w) +
                      (int64_t)tile_of(i) * nunits * 1024 + unit_off;
@@ -602,7 +602,7 @@ __device__ __forceinline__ void persistent_sweep(const GemmArgs& p) {
     const char* at = static_cast<const char*>(p.a_ptr[0]) + lane * 16;
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
-      const int64_t unit = wave + (int64_t)min(s, max(n_i - 1, 0)) * W;
+      const int64_t unit = first + (int64_t)min(s, max(n_i - 1, 0)) * W;
       if constexpr (WF8) {
         a[2 * s] = stage_load(at + (2 * unit) * 1024);
         a[2 * s + 1] = stage_load(at + (2 * unit + 1) * 1024);

@@ -51,6 +51,13 @@ WLS = {
     "small-bf16-g8-b8": W.small_bf16(num_q_heads=16, num_kv_heads=2, batch=8,
                                      ctx_min=30, ctx_max=260,
                                      name="small-bf16-g8-b8", seed=82),
+    # a 256-wide drafter at batch 1: the persistent LM head and the chunked
+    # projection streams with fewer contraction steps than waves
+    "small-bf16-h256-b1": W.small_bf16(batch=1, hidden=256, num_q_heads=4,
+                                       num_kv_heads=2, head_dim=64,
+                                       intermediate=704, ctx_min=90,
+                                       ctx_max=90, name="small-bf16-h256-b1",
+                                       seed=99),
     # 16 sequences (256 block rows, 240 LM-head rows): the LM head in one
     # 256-row block on eight waves, and a SwiGLU output of 16512 columns (a
     # multiple of 192) in 128 x 192 blocks
