@@ -303,7 +303,7 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
     a.wfp8 = 0;
   }
   if (tiled) {
-    const int cfg = plan_tiled(a.M, a.N, a.ep, splittable(a));
+    const int cfg = plan_tiled(a.M, a.N, a.Kd, a.ep, splittable(a));
     const int S = plan_ksplit(c, a, cfg, sw);
     TimedLaunch tl(c, kind, s, S > 1 ? 2 : 1);
     if (S > 1) {
@@ -658,7 +658,7 @@ dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
     } else {
       dflash_status st = run_gemm(ctx, hd, s, ws.split, DFLASH_TIME_LMHEAD);
       if (st != DFLASH_OK) return st;
-      nrec = gemm_is_tiled(ctx, hd) ? tiled_top2_records(plan_tiled(Mh, V, EP_TOP2, false), V)
+      nrec = gemm_is_tiled(ctx, hd) ? tiled_top2_records(plan_tiled(Mh, V, D, EP_TOP2, false), V)
                                     : V / 16;
       if (nrec > kCommitMaxRecords) {
         // many records per row: merge them to kMergeChunks per row first,

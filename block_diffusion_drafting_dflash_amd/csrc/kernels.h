@@ -226,9 +226,10 @@ enum TileCfg : int {
   TILE_128x192 = 7,     // 128 x 192 on four waves of 64 x 96
   TILE_NCFG = 8,
 };
-// Block shape of an M x N tiled GEMM with epilogue `ep`; `splittable`: its
-// contraction may be split (plain-store and residual epilogues).
-int plan_tiled(int M, int N, int ep, bool splittable);
+// Block shape of an M x N tiled GEMM over a contraction of Kd with epilogue
+// `ep`; `splittable`: its contraction may be split (plain-store and
+// residual epilogues).
+int plan_tiled(int M, int N, int Kd, int ep, bool splittable);
 // Top-2 records per row that the tiled LM head writes with block shape cfg
 // (one per column block: top2[row * records + block]).
 int tiled_top2_records(int cfg, int N);
