@@ -102,13 +102,19 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
     AttnArgs p) {
   constexpr int E = Storage<T>::E, KC = Storage<T>::KC, SZ = sizeof(T);
   constexpr int DC = D / KC;
-  constexpr int KROWB = D * SZ + 16;           // padded K row, bytes
+  // Padded rows, bytes.  A K row is shifted 4 banks from the last, so the
+  // 16 rows of a score read (16 bytes per lane) cover every bank once; a
+  // bf16 V row is shifted 8 banks, so the transposed reads (eight rows of
+  // 32 bytes per half-wave) do not collide, where a 4-bank shift hits half
+  // the banks twice.
+  constexpr int KROWB = D * SZ + 16;
+  constexpr int VKROWB = D * SZ + 32;
   constexpr int VROW = kKeyTile + kVPad;       // transposed V row, elements
   constexpr int VROWB = VROW * SZ;
   constexpr int PIECES = TileRegs<T, D, G>::PIECES;
   constexpr int NP = TileRegs<T, D, G>::NP;
-  // V in LDS: bf16 key-major with K's padded rows, fp32 transposed
-  constexpr int VBYTES = SZ == 2 ? kKeyTile * KROWB : D * VROWB;
+  // V in LDS: bf16 key-major (rows of VKROWB bytes), fp32 transposed
+  constexpr int VBYTES = SZ == 2 ? kKeyTile * VKROWB : D * VROWB;
   static_assert(NP * 64 * G == kKeyTile * PIECES, "tile pieces per thread");
   // K and V tiles, double-buffered by tile parity
   __shared__ __attribute__((aligned(16))) char ks2[2][kKeyTile * KROWB];
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
       const int key = idx / PIECES, pc = idx % PIECES;
       *reinterpret_cast<u32x4*>(ks + key * KROWB + pc * E * SZ) = rg.k[j];
       if constexpr (SZ == 2) {
-        *reinterpret_cast<u32x4*>(vt + key * KROWB + pc * E * SZ) = rg.v[j];
+        *reinterpret_cast<u32x4*>(vt + key * VKROWB + pc * E * SZ) = rg.v[j];
       } else {
         const T* ve = reinterpret_cast<const T*>(&rg.v[j]);
         T* vcol = reinterpret_cast<T*>(vt) + key;
@@ -279,11 +285,11 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
         // lane (r, g) reads key 32cc + 4g + r/4 (+16), channels
         // 16dt + 4(r%4) .. +3, and receives channel 16dt + r of keys
         // 32cc + 4g + 0..3 (lo) and 32cc + 16 + 4g + 0..3 (hi)
-        const char* vsrc = vt + (32 * cc + 4 * g + (r >> 2)) * KROWB + 4 * (r & 3) * SZ;
+        const char* vsrc = vt + (32 * cc + 4 * g + (r >> 2)) * VKROWB + 4 * (r & 3) * SZ;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
           const u32x2 lo = lds_read_tr16(vsrc + 16 * dt * SZ);
-          const u32x2 hi = lds_read_tr16(vsrc + 16 * KROWB + 16 * dt * SZ);
+          const u32x2 hi = lds_read_tr16(vsrc + 16 * VKROWB + 16 * dt * SZ);
           const u32x4 afrag = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
           for (int t = 0; t < NP3; ++t) mma16(o[dt], afrag, bp[t], T());

@@ -453,15 +453,14 @@ constexpr int kSlowCap = kProjMaxTiles * 128;
 // float64 evaluation after the last tile, so the loop holds no float64
 // exponential (its constants would crowd the registers and its spill reloads
 // would wait for the loads in flight).
-// Each wave keeps its share of the activation
-// fragments in registers for the workgroup's lifetime, and the weight
-// fragments of the next two tiles are in flight in two register sets while
-// the current tile is multiplied, summed over the waves and reduced to top-2
-// records, so the weight stream does not pause at tile boundaries.  A tile
-// is summed exactly as in gemm_kernel (fp32 over a wave's steps, then
-// float64 over the waves in wave order); each row's record is merged over
-// the workgroup's tiles in tile order and written once per workgroup:
-// part[row][workgroup].
+// Each wave keeps its share of the activation fragments in registers for
+// the workgroup's lifetime, and the weight fragments of the next two tiles
+// are in flight in two register sets while the current tile is multiplied,
+// summed over the waves and reduced to top-2 records, so the weight stream
+// does not pause at tile boundaries.  An LM-head tile is summed exactly as
+// in gemm_kernel (fp32 over a wave's steps, then float64 over the waves in
+// wave order); each row's record is merged over the workgroup's tiles in
+// tile order and written once per workgroup: part[row][workgroup].
 
 // AHEAD: staging loads issued after this tile's set (the other set's, or
 // none for the last tile).  The tile is multiplied from set b; with REFILL

@@ -177,11 +177,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
                                                                 int ksplit) {
   using C = Tiled<TM, TN, WM, WN>;
   constexpr int STAGE = C::NF * 64;  // u32x4 per contraction step
-  // the ring, reused after the contraction for the LM head's logit block
+  constexpr bool kHalfStep = TM * TN >= 8 || C::NW >= 16;
+  // the ring, reused after the contraction for the block's sums
   constexpr int BM = 32 * WM * TM, BN = 32 * WN * TN;
-  // (u32x4 units) logit block, then the top-2 merge records of NT threads
+  // A block whose sums and merge records do not fit in the 160 KiB of LDS
+  // at once is parked and finished in two halves of rows (first the waves
+  // of the lower half of wm).
+  constexpr int HALVES =
+      BM * (BN + 1) * 4 + 64 * C::NW * 16 > 160 * 1024 ? 2 : 1;
+  constexpr int BMH = BM / HALVES;
+  static_assert(WM % HALVES == 0, "whole waves per half");
+  // (u32x4 units) parked sums, then the top-2 merge records of NT threads
   constexpr int RING = NBUF * STAGE;
-  constexpr int LOGITS = (BM * (BN + 1) + 3) / 4, PARTS = 64 * C::NW;
+  constexpr int LOGITS = (BMH * (BN + 1) + 3) / 4, PARTS = 64 * C::NW;
   constexpr int EPI = LOGITS + PARTS;
   __shared__ u32x4 lds[RING > EPI ? RING : EPI];
   const int lane = threadIdx.x & 63;
@@ -275,22 +283,60 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
 
 #pragma unroll
   for (int j = 0; j < NBUF; ++j) issue(j, j);
-  Ops r0, r1;
   vm_wait_n<(NBUF - 1) * C::LPW>();
   __syncthreads();
-  read(r0, 0);
-  int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
-    iter(s, r0, r1);
-    iter(s + 1, r1, r0);
+  if constexpr (!kHalfStep) {
+    Ops r0, r1;
+    read(r0, 0);
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+      iter(s, r0, r1);
+      iter(s + 1, r1, r0);
+    }
+    if (s < nsteps) mul(r0);  // odd step count: the last step
+  } else {
+    // One half-step of operands in flight instead of a whole step (for
+    // wide wave tiles or four waves per SIMD, where registers are short):
+    // the second half of step s is read while the first is multiplied,
+    // and the first half of step s + 1 while the second is.  Each
+    // accumulator still sums the half-steps in order.
+    using OpsH = u32x4[TM + TN];
+    auto read_h = [&](OpsH& r, int slot, int h) {
+      const u32x4* cur = lds + slot * STAGE;
+#pragma unroll
+      for (int m = 0; m < TM; ++m) r[m] = cur[a_off + m * 128 + 32 * h];
+#pragma unroll
+      for (int n = 0; n < TN; ++n) r[TM + n] = cur[w_off + n * 128 + 32 * h];
+    };
+    auto mul_h = [&](const OpsH& r) {
+#pragma unroll
+      for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < TN; ++n) mma32(acc[m][n], r[m], r[TM + n]);
+    };
+    OpsH ra, rb;
+    read_h(ra, 0, 0);
+    for (int s = 0; s < nsteps; ++s) {
+      read_h(rb, s % NBUF, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mul_h(ra);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < nsteps) {
+        // this wave's loads of step s + 1 have landed; after the barrier
+        // every wave's have, and every wave has read step s (the barrier
+        // waits for this wave's LDS reads), so its slot can be refilled
+        vm_wait_n<(NBUF - 2) * C::LPW>();
+        __syncthreads();
+        issue(s + NBUF, s % NBUF);
+        read_h(ra, (s + 1) % NBUF, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mul_h(rb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (s < nsteps) mul(r0);  // odd step count: the last step
   vm_wait_n<0>();  // the clamped refills past the last step
 
-  // Every wave has drained its loads and finished reading the ring: park
-  // the block's sums there, then run the epilogue over whole rows.
-  __syncthreads();
-  float* L = reinterpret_cast<float*>(lds);  // [BM][BN + 1]
   // FP8 weights: each column's sum times its row scale (one float rounding)
   float sc[TN];
 #pragma unroll
@@ -298,25 +344,38 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs p,
     const int col = nb * BN + (wn * TN + n) * 32 + (lane & 31);
     sc[n] = (p.wscale != nullptr && col < p.N) ? p.wscale[col] : 1.f;
   }
+  float* L = reinterpret_cast<float*>(lds);  // [BMH][BN + 1]
 #pragma unroll
-  for (int m = 0; m < TM; ++m)
+  for (int h = 0; h < HALVES; ++h) {
+    // Every wave has drained its loads and finished reading the ring (or
+    // the previous half): park this half's sums there, then run the
+    // epilogue over its whole rows.
+    __syncthreads();
+    if (wm / (WM / HALVES) == h) {
 #pragma unroll
-    for (int n = 0; n < TN; ++n)
+      for (int m = 0; m < TM; ++m)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = (wm * TM + m) * 32 + 4 * (lane >> 5) + 8 * (j >> 2) +
-                      (j & 3);
-        const int c = (wn * TN + n) * 32 + (lane & 31);
-        L[r * (BN + 1) + c] =
-            p.wscale != nullptr ? acc[m][n][j] * sc[n] : acc[m][n][j];
-      }
-  __syncthreads();
-  if (p.ep == EP_TOP2)
-    top2_block<BM, BN, 64 * C::NW>(p, L,
-                                   reinterpret_cast<Top2*>(lds + LOGITS),
-                                   mb * BM, nb * BN, nb, nbn);
-  else
-    block_epilogue<BM, BN, 64 * C::NW>(p, L, mb * BM, nb * C::BNT);
+        for (int n = 0; n < TN; ++n)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int r = (wm * TM + m) * 32 + 4 * (lane >> 5) +
+                          8 * (j >> 2) + (j & 3) - h * BMH;
+            const int c = (wn * TN + n) * 32 + (lane & 31);
+            L[r * (BN + 1) + c] =
+                p.wscale != nullptr ? acc[m][n][j] * sc[n] : acc[m][n][j];
+          }
+    }
+    __syncthreads();
+    // (blocks parked in halves serve the LM head only: the projection
+    // epilogues' registers on top of the live accumulators would spill)
+    if (HALVES == 2 || p.ep == EP_TOP2)
+      top2_block<BMH, BN, 64 * C::NW>(p, L,
+                                      reinterpret_cast<Top2*>(lds + LOGITS),
+                                      mb * BM + h * BMH, nb * BN, nb, nbn);
+    else if constexpr (HALVES == 1)
+      block_epilogue<BMH, BN, 64 * C::NW>(p, L, mb * BM + h * BMH,
+                                          nb * C::BNT);
+  }
 }
 
 // Row-major activation segments (the concatenated target layers) -> packed
@@ -390,6 +449,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
 #ifndef DFLASH_W8_NBUF
 #define DFLASH_W8_NBUF 4
 #endif
+#ifndef DFLASH_W16_NBUF
+#define DFLASH_W16_NBUF 4
+#endif
 hipError_t tiled_cfg(int cfg, const GemmArgs& a, int ks, hipStream_t s) {
   switch (cfg) {
     case TILE_64x64: return dma_t<1, 1, 2, 2, DFLASH_D64_NBUF>(a, ks, s);
@@ -399,8 +461,11 @@ hipError_t tiled_cfg(int cfg, const GemmArgs& a, int ks, hipStream_t s) {
     case TILE_128x256: return dma_t<2, 4, 2, 2, 4>(a, ks, s);
     case TILE_256x128_W8: return dma_t<2, 2, 4, 2, DFLASH_W8_NBUF>(a, ks, s);
     case TILE_128x192: return dma_t<2, 3, 2, 2, DFLASH_D192_NBUF>(a, ks, s);
+    case TILE_256x256:  // the LM head only
+      if (a.ep != EP_TOP2) return hipErrorInvalidValue;
+      return dma_t<2, 2, 4, 4, DFLASH_W16_NBUF>(a, ks, s);
   }
-  return hipErrorInvalidValue;  // 256 x 256: its logit block exceeds LDS
+  return hipErrorInvalidValue;
 }
 
 // output columns per block of each shape
@@ -408,7 +473,7 @@ int tiled_block_cols(int cfg) {
   switch (cfg) {
     case TILE_64x64: case TILE_256x64: return 64;
     case TILE_128x128: case TILE_256x128: case TILE_256x128_W8: return 128;
-    case TILE_128x256: return 256;
+    case TILE_128x256: case TILE_256x256: return 256;
     case TILE_128x192: return 192;
   }
   return 0;
@@ -426,6 +491,9 @@ int tiled_block_cols(int cfg) {
 #ifndef DFLASH_O_UNSPLIT
 #define DFLASH_O_UNSPLIT 1
 #endif
+#ifndef DFLASH_LM_W256_ROWS
+#define DFLASH_LM_W256_ROWS 256
+#endif
 
 // Block shape by rows, columns and epilogue (measured on MI355X at 64, 256
 // and 1024 rows over the drafter's projection and LM-head shapes).
@@ -441,6 +509,12 @@ int plan_tiled(int M, int N, int Kd, int ep, bool splittable) {
     if (ep == EP_TOP2) return TILE_256x128_W8;
     if (ep == EP_SWIGLU && N >= 16384 && N % 192 == 0) return TILE_128x192;
   }
+  // beyond that the LM head takes 256 x 256 blocks on sixteen waves of
+  // 64 x 64 (half the operand bytes per flop of 128 x 128, four waves per
+  // SIMD; the logits parked and scanned in two halves): at 960 and 448 x
+  // 151936 the batch-64 step 5.73-5.74 against 5.90-5.93 ms, where eight
+  // waves of 128 x 64 gained nothing
+  if (M > DFLASH_LM_W256_ROWS && ep == EP_TOP2) return TILE_256x256;
   // above 512 rows, outputs narrower than 16384 columns take 256 x 128
   // blocks on eight waves (with split-K filling the CUs): 16% faster than
   // 128 x 128 there at 1024 rows, slower for the wide gate/up and LM head.

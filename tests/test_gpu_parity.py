@@ -28,7 +28,9 @@ def small_s2(**kw):
 # Batch sizes pick the GEMM paths: 3 sequences (48 block rows) stream the
 # weights with wide workgroups; 8 (128 rows) and 36 (576 rows) take the
 # LDS-tiled MFMA kernel with 64x64 and 128x128 blocks (as do the LM head
-# and the injection of every prefix above 64 rows).  One sequence (15 LM-head
+# and the injection of every prefix above 64 rows); the LM head of 24 and
+# 36 sequences (360 and 540 rows) takes 256x256 blocks on sixteen waves,
+# with ragged row and column tails.  One sequence (15 LM-head
 # rows) takes the persistent LM head: its vocabulary of 8272 = 517 tiles of
 # 16 gives each of 256 workgroups two or three tiles (one each for tiny-f32);
 # its hidden size of 4096 gives the projections long contractions with few
@@ -43,6 +45,8 @@ WLS = {
                                   name="small-bf16-b8", seed=78),
     "small-bf16-b36": W.small_bf16(batch=36, ctx_min=16, ctx_max=80,
                                    name="small-bf16-b36", seed=79),
+    "small-bf16-b24": W.small_bf16(batch=24, ctx_min=16, ctx_max=120,
+                                   name="small-bf16-b24", seed=100),
     # the other two query-group sizes the attention kernel is specialised
     # for: 2 (with head_dim 128, streaming GEMMs) and 8 (tiled GEMMs)
     "small-bf16-g2-d128": W.small_bf16(num_q_heads=4, num_kv_heads=2,
