@@ -68,6 +68,11 @@ WLS = {
     "small-bf16-b16-ffn": W.small_bf16(batch=16, intermediate=8256,
                                        ctx_min=20, ctx_max=120,
                                        name="small-bf16-b16-ffn", seed=98),
+    # 36 sequences (576 block rows) with that SwiGLU output: 128 x 128
+    # blocks with a ragged last row block
+    "small-bf16-b36-ffn": W.small_bf16(batch=36, intermediate=8256,
+                                       ctx_min=16, ctx_max=80,
+                                       name="small-bf16-b36-ffn", seed=101),
 }
 
 
