@@ -3,15 +3,17 @@
 //
 // One workgroup per (context chunk, kv head, sequence); its waves are the
 // query heads sharing that kv head (GQA group), each owning its 16 block
-// queries.  K and V tiles of 64 keys are staged once in LDS for all waves;
-// the next two tiles are fetched into registers while the current one is
-// computed.  The P.V product contracts over keys, so its MFMA operand needs
-// several keys of one channel per lane: bf16 V is stored key-major like K and
-// read back transposed by the LDS transpose read, fp32 V is transposed as it
-// is written.  Each wave computes S^T = K Q^T with MFMA, keeps an online softmax
-// per query in its own lanes, and accumulates O^T = V^T P^T.  Chunks write
-// unnormalised partial outputs with their running max and sum; a merge
-// kernel combines the chunks of a sequence in chunk order.
+// queries.  K and V tiles of 64 keys are staged once in LDS for all waves:
+// bf16 tiles go straight from global memory into a ring of tile slots in
+// LDS (attn_bf16_kernel), fp32 tiles through two register sets in flight
+// (attn_f32_kernel).  The P.V product contracts over keys, so its MFMA
+// operand needs several keys of one channel per lane: bf16 V is stored
+// key-major like K and read back transposed by the LDS transpose read, fp32
+// V is transposed as it is written.  Each wave computes S^T = K Q^T with
+// MFMA, keeps an online softmax per query in its own lanes, and accumulates
+// O^T = V^T P^T.  Chunks write unnormalised partial outputs with their
+// running max and sum; a merge kernel combines the chunks of a sequence in
+// chunk order.
 #include "kernels.h"
 
 namespace dflash {
@@ -28,7 +30,7 @@ constexpr int kKeyTile = 64;
 #ifndef DFLASH_ATTN_PSPLIT
 #define DFLASH_ATTN_PSPLIT 2
 #endif
-constexpr int kVPad = 4;  // elements of padding per transposed V row (fp32)
+constexpr int kVPad = 4;  // elements of padding per transposed V row
 
 // LDS transpose read of 16-bit elements (gfx950).  Within each group of 16
 // lanes, lane i receives element i % 4 of the 8 bytes read by lanes
@@ -42,9 +44,9 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Each thread carries NP 16-byte pieces of K and of V for one 64-key tile.
-// Two such register sets are in flight: while tile t is computed from LDS,
-// tiles t + 1 and t + 2 are being loaded.
+// fp32 form.  Each thread carries NP 16-byte pieces of K and of V for one
+// 64-key tile.  Two such register sets are in flight: while tile t is
+// computed from LDS, tiles t + 1 and t + 2 are being loaded.
 template <typename T, int D, int G>
 struct TileRegs {
   static constexpr int PIECES = D / Storage<T>::E;  // 16-byte pieces per key
@@ -97,24 +99,19 @@ __device__ __forceinline__ void wait_tile(TileRegs<T, D, G>& t) {
 }
 
 // (at four waves, two workgroups per compute unit: at most 256 VGPRs)
-template <typename T, int D, int G>
-__global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
+template <int D, int G>
+__global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_f32_kernel(
     AttnArgs p) {
+  using T = float;
   constexpr int E = Storage<T>::E, KC = Storage<T>::KC, SZ = sizeof(T);
   constexpr int DC = D / KC;
-  // Padded rows, bytes.  A K row is shifted 4 banks from the last, so the
-  // 16 rows of a score read (16 bytes per lane) cover every bank once; a
-  // bf16 V row is shifted 8 banks, so the transposed reads (eight rows of
-  // 32 bytes per half-wave) do not collide, where a 4-bank shift hits half
-  // the banks twice.
+  // padded K row (bytes): the 16 rows of a score read cover every bank once
   constexpr int KROWB = D * SZ + 16;
-  constexpr int VKROWB = D * SZ + 32;
   constexpr int VROW = kKeyTile + kVPad;       // transposed V row, elements
   constexpr int VROWB = VROW * SZ;
   constexpr int PIECES = TileRegs<T, D, G>::PIECES;
   constexpr int NP = TileRegs<T, D, G>::NP;
-  // V in LDS: bf16 key-major (rows of VKROWB bytes), fp32 transposed
-  constexpr int VBYTES = SZ == 2 ? kKeyTile * VKROWB : D * VROWB;
+  constexpr int VBYTES = D * VROWB;            // V in LDS, transposed
   static_assert(NP * 64 * G == kKeyTile * PIECES, "tile pieces per thread");
   // K and V tiles, double-buffered by tile parity
   __shared__ __attribute__((aligned(16))) char ks2[2][kKeyTile * KROWB];
@@ -184,14 +181,10 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
       const int idx = tid + j * 64 * G;
       const int key = idx / PIECES, pc = idx % PIECES;
       *reinterpret_cast<u32x4*>(ks + key * KROWB + pc * E * SZ) = rg.k[j];
-      if constexpr (SZ == 2) {
-        *reinterpret_cast<u32x4*>(vt + key * VKROWB + pc * E * SZ) = rg.v[j];
-      } else {
-        const T* ve = reinterpret_cast<const T*>(&rg.v[j]);
-        T* vcol = reinterpret_cast<T*>(vt) + key;
+      const T* ve = reinterpret_cast<const T*>(&rg.v[j]);
+      T* vcol = reinterpret_cast<T*>(vt) + key;
 #pragma unroll
-        for (int e = 0; e < E; ++e) vcol[(pc * E + e) * VROW] = ve[e];
-      }
+      for (int e = 0; e < E; ++e) vcol[(pc * E + e) * VROW] = ve[e];
     }
     __syncthreads();
     load_at(rg, kt + kSets * kKeyTile);
@@ -259,53 +252,15 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
 
     // O^T += V^T P^T; contraction slots of lane group g hold the keys that
     // this lane's S^T registers hold
-    if constexpr (SZ == 2) {
-      // P = p1 + p2 (+ p3) in bf16 parts of 8 significant bits each
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        // (each pair rounded to nearest even by one packed conversion)
-        constexpr int NP3 = DFLASH_ATTN_PSPLIT;
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        float rem[8];
+    for (int cc = 0; cc < 4; ++cc) {
+      const u32x4 bfrag = {__float_as_uint(s[cc][0]), __float_as_uint(s[cc][1]),
+                           __float_as_uint(s[cc][2]), __float_as_uint(s[cc][3])};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rem[e] = s[2 * cc + e / 4][e % 4];
-        u32x4 bp[NP3];
-#pragma unroll
-        for (int t = 0; t < NP3; ++t) {
-          uint32_t w[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bf16x2_t h = {(__bf16)rem[2 * q], (__bf16)rem[2 * q + 1]};
-            w[q] = __builtin_bit_cast(uint32_t, h);
-            rem[2 * q] -= __uint_as_float(w[q] << 16);
-            rem[2 * q + 1] -= __uint_as_float(w[q] & 0xFFFF0000u);
-          }
-          bp[t] = u32x4{w[0], w[1], w[2], w[3]};
-        }
-        // lane (r, g) reads key 32cc + 4g + r/4 (+16), channels
-        // 16dt + 4(r%4) .. +3, and receives channel 16dt + r of keys
-        // 32cc + 4g + 0..3 (lo) and 32cc + 16 + 4g + 0..3 (hi)
-        const char* vsrc = vt + (32 * cc + 4 * g + (r >> 2)) * VKROWB + 4 * (r & 3) * SZ;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const u32x2 lo = lds_read_tr16(vsrc + 16 * dt * SZ);
-          const u32x2 hi = lds_read_tr16(vsrc + 16 * VKROWB + 16 * dt * SZ);
-          const u32x4 afrag = {lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-          for (int t = 0; t < NP3; ++t) mma16(o[dt], afrag, bp[t], T());
-        }
-      }
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const u32x4 bfrag = {__float_as_uint(s[cc][0]), __float_as_uint(s[cc][1]),
-                             __float_as_uint(s[cc][2]), __float_as_uint(s[cc][3])};
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const char* vrow = vt + (16 * dt + r) * VROWB;
-          const u32x4 afrag = *reinterpret_cast<const u32x4*>(vrow + (16 * cc + 4 * g) * SZ);
-          mma16(o[dt], afrag, bfrag, T());
-        }
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const char* vrow = vt + (16 * dt + r) * VROWB;
+        const u32x4 afrag = *reinterpret_cast<const u32x4*>(vrow + (16 * cc + 4 * g) * SZ);
+        mma16(o[dt], afrag, bfrag, T());
       }
     }
   };
@@ -339,24 +294,268 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_partial_kernel(
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       char* dst = ob + packed_offset<T>(row, hq * D + 16 * dt + 4 * g, Kd);
-      if constexpr (SZ == 2) {
-        u32x2 w;
-        T* wt = reinterpret_cast<T*>(&w);
+      u32x4 w;
+      T* wt = reinterpret_cast<T*>(&w);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) store_elem(wt, e, (double)o[dt][e] * inv);
-        *reinterpret_cast<u32x2*>(dst) = w;
-      } else {
-        u32x4 w;
-        T* wt = reinterpret_cast<T*>(&w);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) store_elem(wt, e, (double)o[dt][e] * inv);
-        *reinterpret_cast<u32x4*>(dst) = w;
-      }
+      for (int e = 0; e < 4; ++e) store_elem(wt, e, (double)o[dt][e] * inv);
+      *reinterpret_cast<u32x4*>(dst) = w;
     }
     return;
   }
   // partials are chunk-major within (sequence, query head, query):
   // part_o[((b*Hq + hq)*K + i)*nch + c][D], part_ml[... same index][2]
+  const int64_t base = (((int64_t)b * p.Hq + hq) * p.K + r) * p.nch + c;
+  float* po = p.part_o + base * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt];
+  if (g == 0)
+    *reinterpret_cast<float2*>(p.part_ml + base * 2) = float2{m_run, l_tot};
+}
+
+// bf16 form: K and V tiles go from global memory straight into a ring
+// of NBUF tile slots in LDS (global_load_lds_dwordx4: lane l's 16 bytes
+// land at m0 + 16 l), so no registers stage them and no LDS stores copy
+// them; NBUF - 1 tiles are in flight while one is computed.  Rows are not
+// padded: the 16-byte pieces of key k are stored permuted (piece p at
+// position p ^ swz(k)), the DMA lanes fetching the pieces that belong at
+// their positions, so that the score reads (16 keys at one piece) and the
+// transposed V reads (8 keys at two adjacent pieces) hit every bank once.
+__device__ __forceinline__ void attn_lds_load16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void attn_vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// piece permutations (SPR 16-byte pieces per key row: 16 for d = 128, 8
+// for d = 64; a 256-byte bank window holds 256 / (16 SPR) rows)
+template <int SPR>
+__device__ __forceinline__ int swz_k(int key) {
+  return (key / (16 / SPR)) & (SPR - 1);
+}
+template <int SPR>
+__device__ __forceinline__ int swz_v(int key) {
+  return 2 * ((key / (16 / SPR)) & (SPR / 2 - 1));
+}
+
+template <int D, int G, int NBUF>
+__global__ __launch_bounds__(64 * G, G == 4 && NBUF <= 2 ? 2 : 1) void
+attn_bf16_kernel(AttnArgs p) {
+  using T = bf16_t;
+  constexpr int E = Storage<T>::E, KC = Storage<T>::KC, SZ = sizeof(T);
+  constexpr int DC = D / KC;
+  constexpr int SPR = D / E;                  // pieces per key row
+  constexpr int TB = kKeyTile * D * SZ;       // bytes of one K (or V) tile
+  constexpr int NI = TB / 1024;               // 1 KiB loads per tile and operand
+  constexpr int IPW = NI / G;                 // ... per wave
+  constexpr int LPT = 2 * IPW;                // loads per wave per tile
+  static_assert(IPW * G == NI, "tile loads split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) char ring[NBUF][2][TB];
+
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  int L = __builtin_amdgcn_readfirstlane(p.ctx_len[b]);
+  L = min(max(L, 0), p.max_len);
+  const int nkeys = L + p.K;
+  const int k0 = c * p.chunk;
+  if (k0 >= nkeys) return;
+  const int k1 = min(nkeys, k0 + p.chunk);
+  const int ntile = (k1 - k0 + kKeyTile - 1) / kKeyTile;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int hq = kvh * G + wave;
+  const uint32_t lds0 =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
+
+  // this lane's part of load i (of IPW) of a tile: key row and the byte
+  // offset of its piece, for K and for V (the same keys, other pieces)
+  int key_of[IPW], koff[IPW], voff[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int slot = (wave + i * G) * 64 + lane;
+    const int key = slot / SPR, q = slot % SPR;
+    key_of[i] = key;
+    koff[i] = (q ^ swz_k<SPR>(key)) * 16;
+    voff[i] = (q ^ swz_v<SPR>(key)) * 16;
+  }
+  // tile j of the chunk into ring slot j % NBUF.  A tile never straddles a
+  // page (pages hold a multiple of 64 positions); keys past the chunk read
+  // its last key (finite values whose scores are masked, so P = 0).
+  auto issue = [&](int j) {
+    const int kt = k0 + j * kKeyTile;
+    const int first = p.pages.log2 < 0 ? 0 : (kt >> p.pages.log2) << p.pages.log2;
+    const int64_t rowb =
+        (kv_row_uniform(p.pages, p.P, p.Hkv, b, kvh, first, p.err) - first) *
+        (int64_t)D * SZ;
+    const char* kb = static_cast<const char*>(p.kc) + rowb;
+    const char* vb = static_cast<const char*>(p.vc) + rowb;
+    const uint32_t sl = lds0 + (uint32_t)((j % NBUF) * 2 * TB);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int64_t row = (int64_t)min(kt + key_of[i], k1 - 1) * D * SZ;
+      const uint32_t at = (uint32_t)((wave + i * G) * 1024);
+      attn_lds_load16(kb + row + koff[i], sl + at);
+      attn_lds_load16(vb + row + voff[i], sl + TB + at);
+    }
+  };
+
+  // Q fragments of this wave's head: staging loads, waited for once below
+  const char* qrow = static_cast<const char*>(p.q) +
+                     ((int64_t)(b * p.K + r) * p.Hq * D + hq * D + g * E) * SZ;
+  u32x4 qf[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) qf[dc] = stage_load(qrow + dc * KC * SZ);
+  if (ntile >= NBUF - 1) {
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j) issue(j);
+    stage_wait<0, DC, (NBUF - 1) * LPT>(qf);
+  } else {
+    for (int j = 0; j < ntile; ++j) issue(j);
+    stage_wait<0, DC, 0>(qf);
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int j = 0; j < ntile; ++j) {
+    // this wave's loads of tile j have landed (NBUF - 2 later tiles may
+    // still be in flight; near the end, fewer were issued: wait for all)
+    if (j + NBUF - 2 < ntile)
+      attn_vm_wait<(NBUF - 2) * LPT>();
+    else
+      attn_vm_wait<0>();
+    // every wave's part of tile j is visible, and every wave has finished
+    // tile j - 1, whose slot is refilled with tile j + NBUF - 1
+    __syncthreads();
+    if (j + NBUF - 1 < ntile) issue(j + NBUF - 1);
+    const char* ks = ring[j % NBUF][0];
+    const char* vt = ring[j % NBUF][1];
+    const int kt = k0 + j * kKeyTile;
+    const int n_valid = min(kKeyTile, k1 - kt);
+
+    // S^T tile: rows = 64 keys (4 MFMA row tiles), columns = 16 queries
+    f32x4 s[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = 16 * mt + r;
+      const char* krow = ks + key * (D * SZ);
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        mma16(s[mt], load16(krow + ((g + 4 * dc) ^ swz_k<SPR>(key)) * 16),
+              qf[dc], T());
+    }
+    // online softmax for query r (log2 domain); keys 16mt + 4g + j (only a
+    // chunk's last tile can hold keys past its end: a uniform branch)
+    float tmax = -INFINITY;
+    if (n_valid == kKeyTile) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          s[mt][jj] *= p.scale_log2;
+          tmax = fmaxf(tmax, s[mt][jj]);
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int key = 16 * mt + 4 * g + jj;
+          const float v = key < n_valid ? s[mt][jj] * p.scale_log2 : -INFINITY;
+          s[mt][jj] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float lt = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float pv = __builtin_amdgcn_exp2f(s[mt][jj] - m_new);
+        s[mt][jj] = pv;
+        lt += pv;
+      }
+    l_run = l_run * alpha + lt;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) o[dt][jj] *= alpha;
+    }
+
+    // O^T += V^T P^T with P = p1 + p2 (+ p3) in bf16 parts
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      constexpr int NP3 = DFLASH_ATTN_PSPLIT;
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      float rem[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rem[e] = s[2 * cc + e / 4][e % 4];
+      u32x4 bp[NP3];
+#pragma unroll
+      for (int t = 0; t < NP3; ++t) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x2_t h = {(__bf16)rem[2 * q], (__bf16)rem[2 * q + 1]};
+          w[q] = __builtin_bit_cast(uint32_t, h);
+          rem[2 * q] -= __uint_as_float(w[q] << 16);
+          rem[2 * q + 1] -= __uint_as_float(w[q] & 0xFFFF0000u);
+        }
+        bp[t] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+      // lane (r, g) reads 8 bytes of key 32cc + 4g + r/4 (+16): channels
+      // 16dt + 4(r%4) .. +3, piece 2dt + (r%4)/2 of the row, and receives
+      // channel 16dt + r of keys 32cc + 4g + 0..3 (lo) and +16 (hi)
+      const int klo = 32 * cc + 4 * g + (r >> 2), khi = klo + 16;
+      const char* vlo = vt + klo * (D * SZ) + (r & 1) * 8;
+      const char* vhi = vt + khi * (D * SZ) + (r & 1) * 8;
+      const int sl = swz_v<SPR>(klo), sh = swz_v<SPR>(khi);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const int pc = 2 * dt + ((r & 3) >> 1);
+        const u32x2 lo = lds_read_tr16(vlo + (pc ^ sl) * 16);
+        const u32x2 hi = lds_read_tr16(vhi + (pc ^ sh) * 16);
+        const u32x4 afrag = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int t = 0; t < NP3; ++t) mma16(o[dt], afrag, bp[t], T());
+      }
+    }
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (p.nch == 1) {
+    // one chunk holds the whole softmax: normalise here with the merge's
+    // arithmetic (float64 quotient, one rounding) and write the packed output
+    const double inv = 1.0 / (double)l_tot;
+    const int row = b * p.K + r, Kd = p.Hq * D;
+    char* ob = static_cast<char*>(p.o);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      char* dst = ob + packed_offset<T>(row, hq * D + 16 * dt + 4 * g, Kd);
+      u32x2 w;
+      T* wt = reinterpret_cast<T*>(&w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_elem(wt, e, (double)o[dt][e] * inv);
+      *reinterpret_cast<u32x2*>(dst) = w;
+    }
+    return;
+  }
   const int64_t base = (((int64_t)b * p.Hq + hq) * p.K + r) * p.nch + c;
   float* po = p.part_o + base * D;
 #pragma unroll
@@ -443,10 +642,27 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int rows) {
   for (int e = 0; e < DPL; ++e) store_elem(dst, e, acc[e] * inv);
 }
 
+// ring slots of the bf16 kernel: two workgroups per CU (about 2 x 64 KiB of
+// LDS with d = 128) or one (deep: chunks of 2048+ keys)
+#ifndef DFLASH_ATTN_RING
+#define DFLASH_ATTN_RING 2
+#endif
+#ifndef DFLASH_ATTN_RING_DEEP
+#define DFLASH_ATTN_RING_DEEP 4
+#endif
 template <typename T, int D, int G>
 hipError_t attn_t(int B, const AttnArgs& a, hipStream_t s) {
-  launch_k((attn_partial_kernel<T, D, G>), dim3(a.nch, a.Hkv, B),
-                     dim3(64 * G), 0, s, a);
+  const dim3 agrid(a.nch, a.Hkv, B);
+  if constexpr (sizeof(T) == 2) {
+    if (a.deep)
+      launch_k((attn_bf16_kernel<D, G, DFLASH_ATTN_RING_DEEP>), agrid,
+               dim3(64 * G), 0, s, a);
+    else
+      launch_k((attn_bf16_kernel<D, G, DFLASH_ATTN_RING>), agrid, dim3(64 * G),
+               0, s, a);
+  } else {
+    launch_k((attn_f32_kernel<D, G>), agrid, dim3(64 * G), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.nch == 1) return hipSuccess;  // the partial kernel normalised

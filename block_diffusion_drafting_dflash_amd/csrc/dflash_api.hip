@@ -220,7 +220,7 @@ dflash_status check_config(const dflash_config* c) {
 #ifndef DFLASH_ATTN_LONG_CHUNK
 #define DFLASH_ATTN_LONG_CHUNK 2048
 #endif
-int attn_chunk(int B, int Hkv, int max_keys, int num_cu) {
+int attn_chunk(int B, int Hkv, int max_keys, int num_cu, int* deep) {
   auto chunk_for = [&](int wg_per_cu) {
     int target = (wg_per_cu * num_cu + B * Hkv - 1) / (B * Hkv);
     if (target < 1) target = 1;
@@ -229,7 +229,14 @@ int attn_chunk(int B, int Hkv, int max_keys, int num_cu) {
     return ch < DFLASH_ATTN_MIN_CHUNK ? DFLASH_ATTN_MIN_CHUNK : ch;
   };
   const int ch = chunk_for(DFLASH_ATTN_WG_PER_CU);
-  return ch >= DFLASH_ATTN_LONG_CHUNK ? chunk_for(1) : ch;
+  if (ch < DFLASH_ATTN_LONG_CHUNK) {
+    *deep = 0;
+    return ch;
+  }
+  // long chunks: one workgroup per CU where the (sequence, kv head) pairs
+  // leave room for it, and then the deeper staging ring of the bf16 kernel
+  *deep = B * Hkv <= num_cu;
+  return chunk_for(1);
 }
 
 // Up to 16 rows (and up to 64 outside the LM head) a GEMM is a weight
@@ -439,9 +446,10 @@ void* static_scratch_ptr(int dev) {
 // Keys per attention workgroup and chunks per (sequence, kv head) for a
 // call with this batch and context bound.
 void attn_geometry(const dflash_ctx* c, int batch, int max_ctx_len,
-                   int* chunk, int* nch) {
+                   int* chunk, int* nch, int* deep) {
   const int K = c->cfg.block_size;
-  *chunk = attn_chunk(batch, c->cfg.num_kv_heads, max_ctx_len + K, c->num_cu);
+  *chunk = attn_chunk(batch, c->cfg.num_kv_heads, max_ctx_len + K, c->num_cu,
+                      deep);
   *nch = (max_ctx_len + K + *chunk - 1) / *chunk;
 }
 
@@ -455,7 +463,8 @@ size_t static_layout(const dflash_ctx* c, int batch, int max_ctx_len,
   const int R = batch * K, qd = g.num_q_heads * d;
   const size_t esz = c->esz;
   int chunk = 0, nch = 0;
-  attn_geometry(c, batch, max_ctx_len, &chunk, &nch);
+  int deep = 0;
+  attn_geometry(c, batch, max_ctx_len, &chunk, &nch, &deep);
   const size_t attn_rows = (size_t)batch * g.num_q_heads * nch * K;
   const size_t lm_rows = (size_t)batch * (K - 1);
   const size_t split_floats = (size_t)DFLASH_MAX_KSPLIT * R * D;
@@ -554,7 +563,7 @@ dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
   at.Hq = Hq;
   at.Hkv = Hkv;
   at.K = K;
-  attn_geometry(ctx, batch, max_ctx_len, &at.chunk, &at.nch);
+  attn_geometry(ctx, batch, max_ctx_len, &at.chunk, &at.nch, &at.deep);
   at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   at.part_o = ws.attn_o;
   at.part_ml = ws.attn_ml;

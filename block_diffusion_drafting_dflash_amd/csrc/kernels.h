@@ -309,6 +309,7 @@ struct AttnArgs {
   KvPages pages;        // cache addressing (contiguous or paged)
   int* err;             // device error word (page ids)
   int chunk, nch;       // keys per workgroup, chunks per (sequence, kv head)
+  int deep;             // one workgroup per CU (long chunks): deeper staging
   float scale_log2;     // log2(e) / sqrt(d)
   float* part_o;        // [B][Hq][nch][K][d]
   float* part_ml;       // [B][Hq][nch][K][2]
