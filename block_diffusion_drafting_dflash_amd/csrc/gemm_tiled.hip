@@ -461,6 +461,7 @@ hipError_t tiled_cfg(int cfg, const GemmArgs& a, int ks, hipStream_t s) {
     case TILE_128x256: return dma_t<2, 4, 2, 2, 4>(a, ks, s);
     case TILE_256x128_W8: return dma_t<2, 2, 4, 2, DFLASH_W8_NBUF>(a, ks, s);
     case TILE_128x192: return dma_t<2, 3, 2, 2, DFLASH_D192_NBUF>(a, ks, s);
+    case TILE_128x128_W8: return dma_t<2, 1, 2, 4, DFLASH_D128_NBUF>(a, ks, s);
     case TILE_256x256:  // the LM head only
       if (a.ep != EP_TOP2) return hipErrorInvalidValue;
       return dma_t<2, 2, 4, 4, DFLASH_W16_NBUF>(a, ks, s);
@@ -472,7 +473,9 @@ hipError_t tiled_cfg(int cfg, const GemmArgs& a, int ks, hipStream_t s) {
 int tiled_block_cols(int cfg) {
   switch (cfg) {
     case TILE_64x64: case TILE_256x64: return 64;
-    case TILE_128x128: case TILE_256x128: case TILE_256x128_W8: return 128;
+    case TILE_128x128: case TILE_256x128: case TILE_256x128_W8:
+    case TILE_128x128_W8:
+      return 128;
     case TILE_128x256: case TILE_256x256: return 256;
     case TILE_128x192: return 192;
   }
@@ -524,12 +527,15 @@ int plan_tiled(int M, int N, int Kd, int ep, bool splittable) {
   if (M > 512 && N < 16384 && !splittable && N % 192 == 0)
     return TILE_128x192;
   // from 1024 rows a residual / store GEMM with a contraction of at most
-  // 4096 (O) fills the grid in 128 x 128 blocks without a split: O at 1024
-  // x 4096 x 4096 took 51 us against 41 us plus a 13 us reduction
+  // 4096 (O) fills the grid in 128 x 128 blocks without a split (O at 1024
+  // x 4096 x 4096 took 51 us against 41 us plus a 13 us reduction), and
+  // above 512 rows so does a wide output (gate/up); both on eight waves of
+  // 64 x 32, four waves per SIMD at two blocks per CU (O 47.3 against 52.4
+  // us, gate/up 216.9 against 221.3 us on four waves of 64 x 64)
   if (M >= 1024 && N < 16384 && splittable && Kd <= 4096 &&
       DFLASH_O_UNSPLIT)
-    return TILE_128x128;
-  if (M > 512) return N >= 16384 ? TILE_128x128 : TILE_256x128_W8;
+    return TILE_128x128_W8;
+  if (M > 512) return N >= 16384 ? TILE_128x128_W8 : TILE_256x128_W8;
   // from 65 rows: 128 x 128 for wide outputs, and for narrow ones whose
   // contraction can be split over the grid (at 256 rows the residual and
   // store GEMMs take 30 us plus the reduction, against 44 us in 64 x 64)
@@ -546,7 +552,7 @@ int tiled_blocks(int cfg, int M, int N) {
   const int bc = tiled_block_cols(cfg);
   const int br = cfg == TILE_64x64 ? 64
                  : (cfg == TILE_128x128 || cfg == TILE_128x256 ||
-                    cfg == TILE_128x192)
+                    cfg == TILE_128x192 || cfg == TILE_128x128_W8)
                      ? 128
                      : 256;
   return bc > 0 ? ((M + br - 1) / br) * ((N + bc - 1) / bc) : 0;

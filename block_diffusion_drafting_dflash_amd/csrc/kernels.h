@@ -224,7 +224,8 @@ enum TileCfg : int {
   TILE_256x256 = 5,
   TILE_256x128_W8 = 6,  // 256 x 128 on eight waves of 64 x 64
   TILE_128x192 = 7,     // 128 x 192 on four waves of 64 x 96
-  TILE_NCFG = 8,
+  TILE_128x128_W8 = 8,  // 128 x 128 on eight waves of 64 x 32
+  TILE_NCFG = 9,
 };
 // Block shape of an M x N tiled GEMM over a contraction of Kd with epilogue
 // `ep`; `splittable`: its contraction may be split (plain-store and
