@@ -321,11 +321,15 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 2 : 1) void attn_f32_kernel(
 // position p ^ swz(k)), the DMA lanes fetching the pieces that belong at
 // their positions, so that the score reads (16 keys at one piece) and the
 // transposed V reads (8 keys at two adjacent pieces) hit every bank once.
-__device__ __forceinline__ void attn_lds_load16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds)
-               : "memory", "m0");
+// (the scalar-base form: a wave-uniform 64-bit base in SGPRs plus this
+// lane's 32-bit byte offset, so a load costs no vector address arithmetic)
+__device__ __forceinline__ void attn_lds_load16(const char* base, uint32_t off,
+                                                uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory", "m0");
 }
 template <int N>
 __device__ __forceinline__ void attn_vm_wait() {
@@ -373,8 +377,9 @@ attn_bf16_kernel(AttnArgs p) {
   const uint32_t lds0 =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
 
-  // this lane's part of load i (of IPW) of a tile: key row and the byte
-  // offset of its piece, for K and for V (the same keys, other pieces)
+  // this lane's part of load i (of IPW) of a tile: key row within the tile
+  // and the byte offset of its piece, for K and for V (the same keys,
+  // other pieces)
   int key_of[IPW], koff[IPW], voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
@@ -385,23 +390,25 @@ attn_bf16_kernel(AttnArgs p) {
     voff[i] = (q ^ swz_v<SPR>(key)) * 16;
   }
   // tile j of the chunk into ring slot j % NBUF.  A tile never straddles a
-  // page (pages hold a multiple of 64 positions); keys past the chunk read
-  // its last key (finite values whose scores are masked, so P = 0).
+  // page (pages hold a multiple of 64 positions), so its rows lie at one
+  // wave-uniform base; keys past the chunk read its last key (finite values
+  // whose scores are masked, so P = 0).
   auto issue = [&](int j) {
     const int kt = k0 + j * kKeyTile;
     const int first = p.pages.log2 < 0 ? 0 : (kt >> p.pages.log2) << p.pages.log2;
     const int64_t rowb =
-        (kv_row_uniform(p.pages, p.P, p.Hkv, b, kvh, first, p.err) - first) *
-        (int64_t)D * SZ;
+        (kv_row_uniform(p.pages, p.P, p.Hkv, b, kvh, first, p.err) - first +
+         kt) * (int64_t)D * SZ;
     const char* kb = static_cast<const char*>(p.kc) + rowb;
     const char* vb = static_cast<const char*>(p.vc) + rowb;
+    const int lim = k1 - 1 - kt;  // last key of the chunk, from the tile
     const uint32_t sl = lds0 + (uint32_t)((j % NBUF) * 2 * TB);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int64_t row = (int64_t)min(kt + key_of[i], k1 - 1) * D * SZ;
+      const uint32_t row = (uint32_t)(min(key_of[i], lim) * (D * SZ));
       const uint32_t at = (uint32_t)((wave + i * G) * 1024);
-      attn_lds_load16(kb + row + koff[i], sl + at);
-      attn_lds_load16(vb + row + voff[i], sl + TB + at);
+      attn_lds_load16(kb, row + koff[i], sl + at);
+      attn_lds_load16(vb, row + voff[i], sl + TB + at);
     }
   };
 
