@@ -412,20 +412,20 @@ attn_bf16_kernel(AttnArgs p) {
     }
   };
 
-  // Q fragments of this wave's head: staging loads, waited for once below
+  // Q fragments of this wave's head: staging loads, waited for once below.
+  // The first NBUF - 1 tiles are issued in straight-line code whatever the
+  // chunk's length (a chunk of fewer tiles loads its last tile again, into
+  // that tile's own slot), so that the wait sits at one point with one
+  // count: a branch here would let the compiler copy the Q registers, at
+  // the join, before their loads have landed.
   const char* qrow = static_cast<const char*>(p.q) +
                      ((int64_t)(b * p.K + r) * p.Hq * D + hq * D + g * E) * SZ;
   u32x4 qf[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) qf[dc] = stage_load(qrow + dc * KC * SZ);
-  if (ntile >= NBUF - 1) {
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) issue(j);
-    stage_wait<0, DC, (NBUF - 1) * LPT>(qf);
-  } else {
-    for (int j = 0; j < ntile; ++j) issue(j);
-    stage_wait<0, DC, 0>(qf);
-  }
+  for (int j = 0; j < NBUF - 1; ++j) issue(min(j, ntile - 1));
+  stage_wait<0, DC, (NBUF - 1) * LPT>(qf);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[D / 16];

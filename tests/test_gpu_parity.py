@@ -308,6 +308,42 @@ def test_draft_single_chunk_attention():
         np.testing.assert_array_equal(g[k], merged[k])
 
 
+def _deep_chunk(B, Hkv, max_keys, num_cu):
+    """The attention plan's chunk for long contexts with few (sequence, kv
+    head) pairs: one workgroup per CU, chunks a multiple of 64 keys."""
+    target = max(1, -(-num_cu // (B * Hkv)))
+    ch = -(-max_keys // target)
+    return max(128, -(-ch // 64) * 64)
+
+
+def test_draft_deep_ring_short_chunks():
+    """A length bound of over half a million positions with one sequence
+    pair per kv head puts the bf16 attention on its deeper staging ring (one
+    workgroup per CU, chunks of thousands of keys).  The contexts end one,
+    two and three 64-key tiles into a chunk, so the ring's prologue meets
+    chunks shorter than its depth, and one context fills a single chunk."""
+    wl = W.small_bf16(batch=4, num_layers=1, name="small-bf16-deep")
+    K = wl.block_size
+    max_len = 540000
+    num_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    ch = _deep_chunk(wl.batch, wl.num_kv_heads, max_len + K, num_cu)
+    assert ch >= 2048, ch
+    lens = np.array([ch + 10 - K, ch + 100 - K, ch + 192 - K, ch - 300],
+                    dtype=np.int32)
+    say(f"[draft deep ring] chunk {ch}, lens {lens.tolist()}")
+    w_cpu, w_dev, ctx = _setup(wl, random_gains=True, max_ctx=max_len)
+    model = OracleModel(wl, w_cpu)
+    kv, per_seq = _seeded_cache(wl, ctx, lens)
+    anchors = W.gen_anchors(wl)
+    g = _gpu_draft(ctx, wl, lens, kv, anchors=anchors, max_len=max_len)
+    ref = draft_batch(model, per_seq, lens, anchors=anchors, keep_logits=True)
+    fl = Float32Floor(wl, w_cpu, per_seq, lens)
+    check_single_pass(wl, wl.name, g, ref, fl, anchors)
+    ctx.close()
+    del kv
+    torch.cuda.empty_cache()
+
+
 def test_draft_is_deterministic():
     wl = WLS["small-bf16"]
     w_cpu, w_dev, ctx = _setup(wl)
