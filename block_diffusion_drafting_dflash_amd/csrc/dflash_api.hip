@@ -271,6 +271,8 @@ bool gemm_is_tiled(const dflash_ctx* c, const GemmArgs& a) {
 #ifndef DFLASH_MAX_KSPLIT
 #define DFLASH_MAX_KSPLIT 4
 #endif
+static_assert(DFLASH_MAX_KSPLIT >= 1 && DFLASH_MAX_KSPLIT <= 4,
+              "the fused split reduction and row norm takes 1 to 4 copies");
 // Where a split GEMM stores its copies: floats of room at p.
 struct SplitWs {
   float* p = nullptr;

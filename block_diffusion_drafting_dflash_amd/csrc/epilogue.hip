@@ -181,11 +181,14 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(int rows, int D,
 // rounding).  So x and out are bit for bit those of the two kernels run one
 // after the other, with one launch and one pass over x fewer.  Rows from M
 // to the next multiple of 16 are written as zeros.
-template <typename T>
+// The number of copies S is a template argument so that every load of a
+// thread (S copies and the old x of each of its chunks) is issued before the
+// first is used: one memory latency per row instead of one per copy.
+template <typename T, int S>
 __global__ __launch_bounds__(256) void splitk_norm_row_kernel(
-    int M, int D, int S, const float* ws, float* x, int resid, const T* g,
+    int M, int D, const float* ws, float* x, int resid, const T* g,
     float eps, T* out) {
-  constexpr int E = Storage<T>::E;
+  constexpr int E = Storage<T>::E, E4 = E / 4;
   __shared__ double scratch[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   char* ob = reinterpret_cast<char*>(out);
@@ -199,6 +202,22 @@ __global__ __launch_bounds__(256) void splitk_norm_row_kernel(
   const int64_t plane = (int64_t)M * D;
   float* xr = x + (int64_t)row * D;
   const float* wr = ws + (int64_t)row * D;
+  f32x4 w[kNormChunks][E4][S], o[kNormChunks][E4];
+#pragma unroll
+  for (int ci = 0; ci < kNormChunks; ++ci) {
+    const int c = tid + ci * 256;
+    if (c < nch) {
+#pragma unroll
+      for (int e4 = 0; e4 < E4; ++e4) {
+        const int col = c * E + 4 * e4;
+#pragma unroll
+        for (int k = 0; k < S; ++k)
+          w[ci][e4][k] =
+              *reinterpret_cast<const f32x4*>(wr + k * plane + col);
+        if (resid) o[ci][e4] = *reinterpret_cast<const f32x4*>(xr + col);
+      }
+    }
+  }
   float v[kNormChunks][E];
   double ss = 0.0;
 #pragma unroll
@@ -206,18 +225,19 @@ __global__ __launch_bounds__(256) void splitk_norm_row_kernel(
     const int c = tid + ci * 256;
     if (c < nch) {
 #pragma unroll
-      for (int e = 0; e < E; e += 4) {
-        const int col = c * E + e;
-        f32x4 q = *reinterpret_cast<const f32x4*>(wr + col);
-        for (int k = 1; k < S; ++k) {
-          const f32x4 w = *reinterpret_cast<const f32x4*>(wr + k * plane + col);
-          q = f32x4{q[0] + w[0], q[1] + w[1], q[2] + w[2], q[3] + w[3]};
-        }
+      for (int e4 = 0; e4 < E4; ++e4) {
+        const int col = c * E + 4 * e4;
+        f32x4 q = w[ci][e4][0];
+#pragma unroll
+        for (int k = 1; k < S; ++k)
+          q = f32x4{q[0] + w[ci][e4][k][0], q[1] + w[ci][e4][k][1],
+                    q[2] + w[ci][e4][k][2], q[3] + w[ci][e4][k][3]};
         if (resid) {
-          const f32x4 o = *reinterpret_cast<const f32x4*>(xr + col);
-          q = f32x4{o[0] + q[0], o[1] + q[1], o[2] + q[2], o[3] + q[3]};
+          const f32x4 a = o[ci][e4];
+          q = f32x4{a[0] + q[0], a[1] + q[1], a[2] + q[2], a[3] + q[3]};
         }
         *reinterpret_cast<f32x4*>(xr + col) = q;
+        const int e = 4 * e4;
         v[ci][e] = q.x;
         v[ci][e + 1] = q.y;
         v[ci][e + 2] = q.z;
@@ -235,12 +255,12 @@ __global__ __launch_bounds__(256) void splitk_norm_row_kernel(
     if (c < nch) {
       const u32x4 gv = load16(g + c * E);
       const T* gt = reinterpret_cast<const T*>(&gv);
-      u32x4 o;  // the 16-byte chunk is built in registers, stored once
-      T* ot = reinterpret_cast<T*>(&o);
+      u32x4 ov;  // the 16-byte chunk is built in registers, stored once
+      T* ot = reinterpret_cast<T*>(&ov);
 #pragma unroll
       for (int e = 0; e < E; ++e)
         store_elem(ot, e, (double)v[ci][e] * inv * (double)load_elem(gt, e));
-      *reinterpret_cast<u32x4*>(ob + packed_offset<T>(row, c * E, D)) = o;
+      *reinterpret_cast<u32x4*>(ob + packed_offset<T>(row, c * E, D)) = ov;
     }
   }
 }
@@ -362,6 +382,22 @@ bool rmsnorm_row_form(bool bf16, int rows, int D) {
   return (rows + 15) / 16 < 32 && D <= 256 * kNormChunks * (bf16 ? 8 : 4);
 }
 
+template <int S>
+hipError_t splitk_norm_t(bool bf16, int tiles, int M, int D, const float* ws,
+                         float* x, bool resid, const void* gain, float eps,
+                         void* out, hipStream_t s) {
+  if (bf16)
+    launch_k(splitk_norm_row_kernel<bf16_t, S>, dim3(tiles * 16), dim3(256),
+             0, s, M, D, ws, x, resid ? 1 : 0,
+             static_cast<const bf16_t*>(gain), eps, static_cast<bf16_t*>(out));
+  else
+    launch_k(splitk_norm_row_kernel<float, S>, dim3(tiles * 16), dim3(256), 0,
+             s, M, D, ws, x, resid ? 1 : 0, static_cast<const float*>(gain),
+             eps, static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+// S = 1 to 4 copies (the most a split GEMM makes)
 hipError_t launch_splitk_norm(bool bf16, int M, int D, int S, const float* ws,
                               float* x, bool resid, const void* gain,
                               float eps, void* out, hipStream_t s) {
@@ -369,15 +405,13 @@ hipError_t launch_splitk_norm(bool bf16, int M, int D, int S, const float* ws,
       D % (bf16 ? 8 : 4) != 0)
     return hipErrorInvalidValue;
   const int tiles = (M + 15) / 16;
-  if (bf16)
-    launch_k(splitk_norm_row_kernel<bf16_t>, dim3(tiles * 16), dim3(256), 0,
-             s, M, D, S, ws, x, resid ? 1 : 0,
-             static_cast<const bf16_t*>(gain), eps, static_cast<bf16_t*>(out));
-  else
-    launch_k(splitk_norm_row_kernel<float>, dim3(tiles * 16), dim3(256), 0, s,
-             M, D, S, ws, x, resid ? 1 : 0, static_cast<const float*>(gain),
-             eps, static_cast<float*>(out));
-  return hipGetLastError();
+  switch (S) {
+    case 1: return splitk_norm_t<1>(bf16, tiles, M, D, ws, x, resid, gain, eps, out, s);
+    case 2: return splitk_norm_t<2>(bf16, tiles, M, D, ws, x, resid, gain, eps, out, s);
+    case 3: return splitk_norm_t<3>(bf16, tiles, M, D, ws, x, resid, gain, eps, out, s);
+    case 4: return splitk_norm_t<4>(bf16, tiles, M, D, ws, x, resid, gain, eps, out, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_rmsnorm(bool bf16, int rows, int D, const float* x,

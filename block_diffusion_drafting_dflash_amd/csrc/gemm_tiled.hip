@@ -415,24 +415,27 @@ hipError_t dma_t(const GemmArgs& a, int ksplit, hipStream_t s) {
 }
 
 // out[row][col] (+)= sum over s of ws[s][row][col], s in order, fp32; one
-// float4 per thread (N % 4 == 0).
+// float4 per thread (N % 4 == 0).  S is a template argument so that the S
+// copies (and the old output) are loaded together before the sum.
+template <int S>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(
-    int M, int N, int S, const float* ws, float* out, int ldo, int resid) {
+    int M, int N, const float* ws, float* out, int ldo, int resid) {
   const int64_t n4 = (int64_t)M * N / 4, plane = (int64_t)M * N;
   for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n4;
        q += (int64_t)gridDim.x * 256) {
     const int64_t e = q * 4;
     const int row = (int)(e / N), col = (int)(e % N);
-    f32x4 v = *reinterpret_cast<const f32x4*>(ws + e);
-    for (int k = 1; k < S; ++k) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(ws + k * plane + e);
-      v = f32x4{v[0] + w[0], v[1] + w[1], v[2] + w[2], v[3] + w[3]};
-    }
     float* o = out + (int64_t)row * ldo + col;
-    if (resid) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(o);
-      v = f32x4{x[0] + v[0], x[1] + v[1], x[2] + v[2], x[3] + v[3]};
-    }
+    f32x4 w[S], x{};
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+      w[k] = *reinterpret_cast<const f32x4*>(ws + k * plane + e);
+    if (resid) x = *reinterpret_cast<const f32x4*>(o);
+    f32x4 v = w[0];
+#pragma unroll
+    for (int k = 1; k < S; ++k)
+      v = f32x4{v[0] + w[k][0], v[1] + w[k][1], v[2] + w[k][2], v[3] + w[k][3]};
+    if (resid) v = f32x4{x[0] + v[0], x[1] + v[1], x[2] + v[2], x[3] + v[3]};
     *reinterpret_cast<f32x4*>(o) = v;
   }
 }
@@ -577,8 +580,15 @@ hipError_t launch_splitk_reduce(int M, int N, int S, const float* ws,
   int64_t blocks = (n4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
-  launch_k(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, M,
-           N, S, ws, out, ldo, resid ? 1 : 0);
+  const dim3 grid((unsigned)blocks);
+  const int r = resid ? 1 : 0;
+  switch (S) {  // 1 to 4 copies (the most a split GEMM makes)
+    case 1: launch_k(splitk_reduce_kernel<1>, grid, dim3(256), 0, s, M, N, ws, out, ldo, r); break;
+    case 2: launch_k(splitk_reduce_kernel<2>, grid, dim3(256), 0, s, M, N, ws, out, ldo, r); break;
+    case 3: launch_k(splitk_reduce_kernel<3>, grid, dim3(256), 0, s, M, N, ws, out, ldo, r); break;
+    case 4: launch_k(splitk_reduce_kernel<4>, grid, dim3(256), 0, s, M, N, ws, out, ldo, r); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
