@@ -267,7 +267,9 @@ bool gemm_is_tiled(const dflash_ctx* c, const GemmArgs& a) {
 // leaves CUs idle: copies up to about one workgroup per CU (at most 4, at
 // least 8 contraction steps each, within the split workspace).  Measured:
 // at 64 rows (64 blocks, 4 copies) the split plus its reduction is 30-40%
-// faster than one pass; at 256 blocks two copies gain nothing.
+// faster than one pass; at 256 blocks two copies gain nothing.  Copies for
+// two workgroups per CU (up to 8) were slower at 64, 256 and 1024 rows
+// (batch-16 step 1.72 -> 1.79 ms, batch-64 5.64 -> 5.77 ms).
 #ifndef DFLASH_MAX_KSPLIT
 #define DFLASH_MAX_KSPLIT 4
 #endif
