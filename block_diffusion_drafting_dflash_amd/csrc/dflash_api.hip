@@ -292,6 +292,28 @@ int plan_ksplit(const dflash_ctx* c, const GemmArgs& a, int cfg,
   return std::max(S, 1);
 }
 
+// A pair-epilogue GEMM (QKV, the injected K/V) of 65 to
+// DFLASH_PAIR_SPLIT_ROWS rows whose 128 x 128 block grid fills at most half
+// the CUs: that many copies over contraction ranges (at most
+// DFLASH_MAX_KSPLIT, at least 8 steps each, within the split workspace),
+// stored in tile order and finished by the pair reduction.  Returns the
+// copies, or 1 where the GEMM keeps its unsplit plan.
+#ifndef DFLASH_PAIR_SPLIT_ROWS
+#define DFLASH_PAIR_SPLIT_ROWS 512
+#endif
+int plan_pair_split(const dflash_ctx* c, const GemmArgs& a,
+                    const SplitWs& ws) {
+  if ((a.ep != EP_QKV && a.ep != EP_KV) || a.cmap != MAP_PAIRS ||
+      a.M <= 64 || a.M > DFLASH_PAIR_SPLIT_ROWS)
+    return 1;
+  const int blocks = tiled_blocks(TILE_128x128, a.M, a.N);
+  int S = blocks > 0 ? c->num_cu / blocks : 1;
+  S = std::min(S, DFLASH_MAX_KSPLIT);
+  S = std::min(S, a.Kd / 32 / 8);
+  while (S > 1 && (size_t)S * a.M * a.N > ws.floats) --S;
+  return std::max(S, 1);
+}
+
 dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
                        const SplitWs& sw, int kind = DFLASH_TIME_GEMM) {
   a.err = c->err;
@@ -314,6 +336,18 @@ dflash_status run_gemm(dflash_ctx* c, GemmArgs& a, hipStream_t s,
     a.wfp8 = 0;
   }
   if (tiled) {
+    const int ps = plan_pair_split(c, a, sw);
+    if (ps > 1) {
+      TimedLaunch tl(c, kind, s, 2);
+      GemmArgs b = a;
+      b.ep = EP_STORE;
+      b.cmap = MAP_LINEAR;  // the copies in tile order
+      b.out_f32 = sw.p;
+      b.ldo = a.N;
+      DF_HIP(launch_gemm_tiled(true, TILE_128x128, b, ps, s));
+      DF_HIP(launch_splitk_pair(a, ps, sw.p, s));
+      return DFLASH_OK;
+    }
     const int cfg = plan_tiled(a.M, a.N, a.Kd, a.ep, splittable(a));
     const int S = plan_ksplit(c, a, cfg, sw);
     TimedLaunch tl(c, kind, s, S > 1 ? 2 : 1);

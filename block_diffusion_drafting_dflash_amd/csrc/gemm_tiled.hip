@@ -440,6 +440,48 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
   }
 }
 
+// The pair epilogue (EP_QKV, EP_KV) of a split GEMM: its S copies were stored
+// in tile order (tile t's 8 low columns, then their 8 partners, at columns
+// 16t .. 16t + 15 of ws[s][row]).  One thread per (row, tile): the copies are
+// added in order in float, then pair_epilogue8 finishes the 16 values as the
+// unsplit kernel's epilogue does.
+template <int S>
+__global__ __launch_bounds__(256) void splitk_pair_kernel(GemmArgs p,
+                                                          const float* ws) {
+  const int ntiles = p.N / 16;
+  const int64_t units = (int64_t)p.M * ntiles, plane = (int64_t)p.M * p.N;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * 256) {
+    const int row = (int)(u / ntiles), tile = (int)(u % ntiles);
+    const float* w = ws + (int64_t)row * p.N + tile * 16;
+    f32x4 c[S][4];
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        c[k][j] = *reinterpret_cast<const f32x4*>(w + k * plane + 4 * j);
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 q = c[0][j];
+#pragma unroll
+      for (int k = 1; k < S; ++k)
+        q = f32x4{q[0] + c[k][j][0], q[1] + c[k][j][1], q[2] + c[k][j][2],
+                  q[3] + c[k][j][3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * j + e] = q[e];
+    }
+    float a[8], b[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a[k] = v[k];
+      b[k] = v[k + 8];
+    }
+    pair_epilogue8(p, row, map_col(p.cmap, p.pair_group, p.pair_off, tile, 0),
+                   a, b);
+  }
+}
+
 #ifndef DFLASH_D64_NBUF
 #define DFLASH_D64_NBUF 8
 #endif
@@ -587,6 +629,25 @@ hipError_t launch_splitk_reduce(int M, int N, int S, const float* ws,
     case 2: launch_k(splitk_reduce_kernel<2>, grid, dim3(256), 0, s, M, N, ws, out, ldo, r); break;
     case 3: launch_k(splitk_reduce_kernel<3>, grid, dim3(256), 0, s, M, N, ws, out, ldo, r); break;
     case 4: launch_k(splitk_reduce_kernel<4>, grid, dim3(256), 0, s, M, N, ws, out, ldo, r); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_pair(const GemmArgs& a, int S, const float* ws,
+                              hipStream_t s) {
+  if (a.cmap != MAP_PAIRS || (a.ep != EP_QKV && a.ep != EP_KV) ||
+      a.N % 16 != 0)
+    return hipErrorInvalidValue;
+  const int64_t units = (int64_t)a.M * (a.N / 16);
+  int64_t blocks = (units + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks);
+  switch (S) {  // 2 to 4 copies (the most a split GEMM makes)
+    case 2: launch_k(splitk_pair_kernel<2>, grid, dim3(256), 0, s, a, ws); break;
+    case 3: launch_k(splitk_pair_kernel<3>, grid, dim3(256), 0, s, a, ws); break;
+    case 4: launch_k(splitk_pair_kernel<4>, grid, dim3(256), 0, s, a, ws); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

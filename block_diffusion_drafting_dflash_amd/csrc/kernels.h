@@ -245,6 +245,11 @@ hipError_t launch_gemm_tiled(bool bf16, int cfg, const GemmArgs& a,
 hipError_t launch_splitk_reduce(int M, int N, int S, const float* ws,
                                 float* out, int ldo, bool resid,
                                 hipStream_t s);
+// The pair epilogue (a.ep EP_QKV or EP_KV, MAP_PAIRS) of a GEMM whose S (2 to
+// 4) copies were stored in tile order as ws[S][a.M][a.N] (the tiled kernel
+// run with EP_STORE and MAP_LINEAR).
+hipError_t launch_splitk_pair(const GemmArgs& a, int S, const float* ws,
+                              hipStream_t s);
 // dst = packed copy of a's row-major A segments (M rows, contraction a.Kd)
 hipError_t launch_pack_act(bool bf16, const GemmArgs& a, void* dst,
                            hipStream_t s);
