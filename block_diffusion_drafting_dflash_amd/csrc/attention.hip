@@ -346,6 +346,25 @@ __device__ __forceinline__ int swz_v(int key) {
   return 2 * ((key / (16 / SPR)) & (SPR / 2 - 1));
 }
 
+// The sequence whose context is the z-th longest of the B in the batch
+// (equal lengths: lower index first), for a grid that runs sequences
+// longest first.  Every thread of the workgroup calls it (one barrier).
+__device__ int seq_by_length_rank(const AttnArgs& p, int z, int B) {
+  __shared__ int pick;
+  auto len = [&](int s) { return min(max(p.ctx_len[s], 0), p.max_len); };
+  for (int s = threadIdx.x; s < B; s += blockDim.x) {
+    const int ls = len(s);
+    int rank = 0;
+    for (int u = 0; u < B; ++u) {
+      const int lu = len(u);
+      rank += (lu > ls) || (lu == ls && u < s);
+    }
+    if (rank == z) pick = s;
+  }
+  __syncthreads();
+  return pick;
+}
+
 template <int D, int G, int NBUF>
 __global__ __launch_bounds__(64 * G, G == 4 && NBUF <= 2 ? 2 : 1) void
 attn_bf16_kernel(AttnArgs p) {
@@ -360,7 +379,12 @@ attn_bf16_kernel(AttnArgs p) {
   static_assert(IPW * G == NI, "tile loads split evenly over the waves");
   __shared__ __attribute__((aligned(16))) char ring[NBUF][2][TB];
 
-  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int c = blockIdx.x, kvh = blockIdx.y;
+  // with one chunk per sequence the grid takes the sequences longest first,
+  // so that the workgroups sharing a CU pair long contexts with short ones
+  const int b = __builtin_amdgcn_readfirstlane(
+      p.by_len ? seq_by_length_rank(p, blockIdx.z, gridDim.z)
+               : (int)blockIdx.z);
   int L = __builtin_amdgcn_readfirstlane(p.ctx_len[b]);
   L = min(max(L, 0), p.max_len);
   const int nkeys = L + p.K;

@@ -602,6 +602,10 @@ dflash_status draft_impl(dflash_ctx* ctx, const DraftWs& ws, void* stream,
   at.Hkv = Hkv;
   at.K = K;
   attn_geometry(ctx, batch, max_ctx_len, &at.chunk, &at.nch, &at.deep);
+  // one chunk per sequence: the ragged contexts run longest first (at batch
+  // 64 with 256-2048 keys 81 against 85 us per launch; with several chunks
+  // per sequence, as at batch 16, the order gained nothing)
+  at.by_len = at.nch == 1 && batch > 1;
   at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   at.part_o = ws.attn_o;
   at.part_ml = ws.attn_ml;

@@ -316,6 +316,7 @@ struct AttnArgs {
   int* err;             // device error word (page ids)
   int chunk, nch;       // keys per workgroup, chunks per (sequence, kv head)
   int deep;             // one workgroup per CU (long chunks): deeper staging
+  int by_len;           // bf16: blockIdx.z ranks the sequences, longest first
   float scale_log2;     // log2(e) / sqrt(d)
   float* part_o;        // [B][Hq][nch][K][d]
   float* part_ml;       // [B][Hq][nch][K][2]

@@ -308,6 +308,24 @@ def test_draft_single_chunk_attention():
         np.testing.assert_array_equal(g[k], merged[k])
 
 
+def test_draft_one_chunk_sequences_ordered_by_length():
+    """One attention chunk per sequence: the bf16 kernel takes the sequences
+    longest first (ranked on the device, equal lengths by index).  Ties,
+    empty contexts and several equal maxima must still give every sequence
+    its own output rows."""
+    wl = W.small_bf16(batch=7, name="small-bf16-ties")
+    lens = np.array([64, 30, 64, 0, 30, 64, 7], dtype=np.int32)
+    say(f"[draft ties] lens {lens.tolist()}")
+    w_cpu, w_dev, ctx = _setup(wl, random_gains=True)
+    model = OracleModel(wl, w_cpu)
+    kv, per_seq = _seeded_cache(wl, ctx, lens)
+    anchors = W.gen_anchors(wl)
+    g = _gpu_draft(ctx, wl, lens, kv, anchors=anchors)
+    ref = draft_batch(model, per_seq, lens, anchors=anchors, keep_logits=True)
+    fl = Float32Floor(wl, w_cpu, per_seq, lens)
+    check_single_pass(wl, wl.name, g, ref, fl, anchors)
+
+
 def _deep_chunk(B, Hkv, max_keys, num_cu):
     """The attention plan's chunk for long contexts with few (sequence, kv
     head) pairs: one workgroup per CU, chunks a multiple of 64 keys."""
